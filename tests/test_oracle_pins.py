@@ -1,0 +1,510 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU.  Each pin is chosen so that a plausible
+mistake in the oracle (a dropped term, a wrong sign or index, a transposed
+operand, a wrong chunk of the modulation) fails at least one of them; the
+mutation tests at the bottom plant such mistakes into the oracle and check
+that the pins notice.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import brute
+import oracle as O
+from diffusion_transformer_amd import synth
+
+
+# ---------------------------------------------------------------- positions
+
+def test_positions_printed_example_h16():
+    # Host contract s.4: for h = 16 the image rows run -8..7; columns alike.
+    L, h, w = 5, 16, 16
+    pos = O.positions(L, h, w)
+    img = pos[L:]
+    assert img[:, 1].min() == -8 and img[:, 1].max() == 7
+    assert img[:, 2].min() == -8 and img[:, 2].max() == 7
+    assert (img[:, 0] == L).all()                       # frame coordinate = L
+    assert sorted(set(img[:, 1].tolist())) == list(range(-8, 8))
+
+
+def test_positions_text_and_raster_order():
+    L, h, w = 3, 4, 6
+    pos = O.positions(L, h, w)
+    assert pos.shape == (L + h * w, 3)
+    for i in range(L):
+        assert tuple(pos[i]) == (i, i, i)
+    # raster order: token y*w + x; width coordinate runs fastest
+    assert tuple(pos[L + 0]) == (3, -2, -3)
+    assert tuple(pos[L + 1]) == (3, -2, -2)
+    assert tuple(pos[L + w]) == (3, -1, -3)
+    assert tuple(pos[L + h * w - 1]) == (3, 1, 2)
+
+
+def test_positions_odd_grid():
+    pos = O.positions(0, 3, 5)
+    assert sorted(set(pos[:, 1].tolist())) == [-2, -1, 0]
+    assert sorted(set(pos[:, 2].tolist())) == [-3, -2, -1, 0, 1]
+
+
+# ---------------------------------------------------------------- rope tables
+
+def _table_for(p0, p1, p2):
+    pos = np.array([[p0, p1, p2]], dtype=np.int64)
+    return O.rope_tables(pos)
+
+
+def test_rope_tables_position_zero():
+    c, s = _table_for(0, 0, 0)
+    assert c.dtype == np.float32 and c.shape == (1, 64)
+    assert (c == 1.0).all() and (s == 0.0).all()
+
+
+def test_rope_tables_known_angles():
+    # axis 0 (width 16): pair 4 has inverse frequency 10000^(-8/16) = 0.01;
+    # axes 1, 2 (width 56): pair 14 has 10000^(-28/56) = 0.01.
+    c, s = _table_for(100, 100, -100)
+    assert c[0, 4] == np.float32(0.5403023058681398)          # cos(1)
+    assert s[0, 4] == np.float32(0.8414709848078965)          # sin(1)
+    assert c[0, 8 + 14] == np.float32(0.5403023058681398)
+    assert c[0, 36 + 14] == np.float32(0.5403023058681398)
+    assert s[0, 36 + 14] == np.float32(-0.8414709848078965)   # odd in position
+    # pair 0 of every axis has inverse frequency 1: angle = position
+    c, s = _table_for(3, -2, 7)
+    assert c[0, 0] == np.float32(-0.9899924966004454)         # cos(3)
+    assert s[0, 8] == np.float32(-0.9092974268256817)         # sin(-2)
+    assert c[0, 36] == np.float32(0.7539022543433046)         # cos(7)
+    # the last pair of axis 0: 10000^(-14/16) = 10^(-3.5)
+    c, s = _table_for(1000, 0, 0)
+    assert abs(float(s[0, 7]) - math.sin(1000 * 10 ** -3.5)) < 1e-7
+
+
+def test_rope_tables_axes_1_2_identical_and_unit():
+    pos = O.positions(7, 9, 11)
+    pos2 = pos.copy()
+    pos2[:, 2] = pos2[:, 1]
+    c, s = O.rope_tables(pos2)
+    assert (c[:, 8:36] == c[:, 36:64]).all() and (s[:, 8:36] == s[:, 36:64]).all()
+    c, s = O.rope_tables(pos)
+    r = c.astype(np.float64) ** 2 + s.astype(np.float64) ** 2
+    assert np.abs(r - 1).max() < 2e-7
+
+
+def test_rope_tables_angle_addition():
+    # angle linear in position: cos(a+b) = cos a cos b - sin a sin b
+    pa = np.array([[5, 37, -12]]); pb = np.array([[9, -20, 30]])
+    ca, sa = O.rope_tables(pa); cb, sb = O.rope_tables(pb); cab, sab = O.rope_tables(pa + pb)
+    ca, sa, cb, sb = (v.astype(np.float64) for v in (ca, sa, cb, sb))
+    assert np.abs(cab - (ca * cb - sa * sb)).max() < 3e-7
+    assert np.abs(sab - (sa * cb + ca * sb)).max() < 3e-7
+
+
+# ---------------------------------------------------------------- rope apply
+
+def test_rope_apply_identity_and_quarter_turn():
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal((2, 5, 8))
+    ones, zeros = np.ones((5, 4)), np.zeros((5, 4))
+    assert (O.rope_apply(v, ones, zeros) == v).all()
+    r = O.rope_apply(v, zeros, ones)                  # +90 degrees per pair
+    assert (r[..., 0::2] == -v[..., 1::2]).all()
+    assert (r[..., 1::2] == v[..., 0::2]).all()
+
+
+def test_rope_apply_one_pair_only():
+    v = np.arange(1.0, 9.0)[None, :]                  # one row, 4 pairs
+    c = np.ones((1, 4)); s = np.zeros((1, 4))
+    c[0, 2], s[0, 2] = 0.0, -1.0                       # -90 degrees on pair 2
+    r = O.rope_apply(v, c, s)
+    assert r.tolist() == [[1, 2, 3, 4, 6, -5, 7, 8]]
+
+
+def test_rope_relative_position():
+    # <R(p) q, R(p') k> = <q, R(p' - p) k> per axis
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal(128); k = rng.standard_normal(128)
+    p, pp = np.array([[4, -7, 19]]), np.array([[11, 3, -2]])
+    cp, sp = O.rope_tables(p); cq, sq = O.rope_tables(pp); cd, sd = O.rope_tables(pp - p)
+    lhs = O.rope_apply(q[None], cp, sp)[0] @ O.rope_apply(k[None], cq, sq)[0]
+    rhs = q @ O.rope_apply(k[None], cd, sd)[0]
+    assert abs(lhs - rhs) < 1e-4 * (1 + abs(lhs))
+    pair_norm = lambda v: v[0::2] ** 2 + v[1::2] ** 2
+    assert np.allclose(pair_norm(O.rope_apply(q[None], cp, sp)[0]), pair_norm(q), rtol=1e-6)
+
+
+# ---------------------------------------------------------------- time embedding
+
+def test_sinusoids_closed_values():
+    e = O.timestep_embedding(0.0)
+    assert e.shape == (256,)
+    assert (e[:128] == 1).all() and (e[128:] == 0).all()
+    e = O.timestep_embedding(0.1)                     # 1000 t = 100
+    assert abs(e[64] - 0.5403023058681398) < 1e-12    # freq 10000^(-64/128) = 0.01
+    assert abs(e[128 + 64] - 0.8414709848078965) < 1e-12
+    assert abs(e[0] - math.cos(100.0)) < 1e-12
+    assert abs(e[128] - math.sin(100.0)) < 1e-12
+
+
+def test_silu_values():
+    assert O.silu(0.0) == 0.0
+    assert abs(O.silu(1.0) - 0.7310585786300049) < 1e-15
+    assert abs(O.silu(-1.0) + 0.2689414213699951) < 1e-15
+    assert abs(O.silu(40.0) - 40.0) < 1e-12
+
+
+# ---------------------------------------------------------------- norms
+
+def test_layer_norm_moments_and_invariance():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((7, 96)) * 3 + 1
+    n = O.layer_norm(x, 0.0)
+    assert np.abs(n.mean(1)).max() < 1e-12
+    assert np.abs((n ** 2).mean(1) - 1).max() < 1e-12        # biased variance
+    assert np.allclose(O.layer_norm(2.5 * x - 4, 0.0), n, atol=1e-12)
+
+
+def test_rms_norm_and_weight_index():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 64))
+    r = O.rms_norm(x, None, 0.0)
+    assert np.abs(np.sqrt((r ** 2).mean(1)) - 1).max() < 1e-12
+    w = np.arange(64.0)
+    assert np.allclose(O.rms_norm(x, w, 0.0), r * w[None, :], atol=1e-12)
+
+
+def test_modulated_norm_scale_minus_one_gives_shift():
+    arch = O.Arch(256, 2, 128, 1024)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 256))
+    shift = rng.standard_normal(256)
+    y = O.modulated_norm(x, shift, -np.ones(256), arch)
+    assert (y == shift[None, :]).all()
+
+
+# ---------------------------------------------------------------- linear, attention
+
+def test_linear_brute_force():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((3, 5)); w = rng.standard_normal((4, 5))
+    y = O.linear(x, w)
+    for r in range(3):
+        assert np.allclose(y[r], brute.matvec(brute.mat(w), brute.vec(x[r])), atol=1e-12)
+
+
+def _attn_brute(q, k, v):
+    H, S, d = q.shape
+    out = np.zeros((H, S, v.shape[-1]))
+    for h in range(H):
+        for i in range(S):
+            sc = [sum(q[h, i, e] * k[h, j, e] for e in range(d)) / math.sqrt(d) for j in range(S)]
+            mx = max(sc)
+            ex = [math.exp(s - mx) for s in sc]
+            for e in range(v.shape[-1]):
+                out[h, i, e] = sum(ex[j] * v[h, j, e] for j in range(S)) / sum(ex)
+    return out
+
+
+def test_attention_brute_force_and_properties():
+    rng = np.random.default_rng(7)
+    q, k, v = (rng.standard_normal((2, 6, 4)) * 2 for _ in range(3))
+    o = O.attention(q, k, v)
+    assert np.abs(o - _attn_brute(q, k, v)).max() < 1e-12
+    # rows of P sum to 1
+    p = O.softmax_rows(q[0] @ k[0].T / 2.0)
+    assert np.abs(p.sum(1) - 1).max() < 1e-14
+    # all keys equal -> o = mean of v
+    kk = np.repeat(k[:, :1], 6, axis=1)
+    assert np.allclose(O.attention(q, kk, v), v.mean(1, keepdims=True).repeat(6, 1), atol=1e-12)
+    # one row -> o = v
+    assert np.allclose(O.attention(q[:, :1], k[:, :1], v[:, :1]), v[:, :1], atol=1e-15)
+    # a joint permutation of keys and values changes nothing
+    perm = rng.permutation(6)
+    assert np.allclose(O.attention(q, k[:, perm], v[:, perm]), o, atol=1e-12)
+
+
+def test_swiglu_interleave():
+    u = np.array([[1.0, 2.0, 0.0, 5.0, -1.0, 3.0]])
+    a = O.swiglu_interleaved(u)
+    assert a.shape == (1, 3)
+    assert abs(a[0, 0] - 0.7310585786300049 * 2) < 1e-15
+    assert a[0, 1] == 0.0                              # silu(0) * up = 0
+    assert abs(a[0, 2] + 0.2689414213699951 * 3) < 1e-15
+
+
+# ---------------------------------------------------------------- int8 block-32
+
+def test_dequant_exact_and_block_index():
+    rng = np.random.default_rng(8)
+    q, s = synth.int8_weight(rng, 16, 128)
+    w = O.dequant_int8_b32(q, s)
+    exact = q.astype(np.float64) * np.repeat(s.astype(np.float64), 32, axis=1)
+    assert w.dtype == np.float32 and (w.astype(np.float64) == exact).all()
+    s1 = np.zeros((16, 4), np.float32); s1[3, 2] = 1.0
+    w1 = O.dequant_int8_b32(np.ones((16, 128), np.int8), s1)
+    nz = np.argwhere(w1 != 0)
+    assert set(nz[:, 0]) == {3} and nz[:, 1].min() == 64 and nz[:, 1].max() == 95
+    # extremes: 127 and -127 times the largest bf16 scale drawn
+    assert O.dequant_int8_b32(np.full((1, 32), -127, np.int8), np.full((1, 1), 0.0390625, np.float32))[0, 0] == np.float32(-4.9609375)
+
+
+# ---------------------------------------------------------------- Euler
+
+def test_sigma_grid_and_euler_telescopes():
+    sig = O.sigma_grid(4)
+    assert sig.dtype == np.float32 and sig.tolist() == [1.0, 0.75, 0.5, 0.25, 0.0]
+    rng = np.random.default_rng(9)
+    x0 = rng.integers(-50, 50, 1000).astype(np.float32)
+    v = (rng.integers(-50, 50, 1000) * 4).astype(np.float32)
+    x = x0
+    for i in range(4):
+        x = O.euler_step(x, v, sig[i], sig[i + 1])
+    assert (x == x0 - v).all()                         # sum of the steps' dt = -1
+
+
+def test_euler_fp32_roundings():
+    x = np.array([1.0], np.float32); v = np.array([1e-8], np.float32)
+    assert O.euler_step(x, v, 1.0, 0.75)[0] == np.float32(1.0)   # fp32 sum absorbs
+    assert O.euler_step(np.float32([0.0]), np.float32([3.0]), 0.5, 0.25)[0] == np.float32(-0.75)
+
+
+# ---------------------------------------------------------------- whole block
+
+TINY = O.Arch(hidden=16, heads=2, head_dim=8, ffn=12, axes=(2, 2, 4))
+
+
+def _tiny_case(seed=10, S_L=2, h=2, w=2, rms=False, std=0.3):
+    rng = np.random.default_rng(seed)
+    D, F, hd = TINY.hidden, TINY.ffn, TINY.head_dim
+    W = dict(w_qkv=rng.standard_normal((3 * D, D)) * std, w_out=rng.standard_normal((D, D)) * std,
+             w_up=rng.standard_normal((2 * F, D)) * std, w_down=rng.standard_normal((D, F)) * std,
+             w_mod=rng.standard_normal((6 * D, D)) * std,
+             q_norm=1 + 0.2 * rng.standard_normal(hd), k_norm=1 + 0.2 * rng.standard_normal(hd))
+    if rms:
+        W["norm1"] = 1 + 0.2 * rng.standard_normal(D)
+        W["norm2"] = 1 + 0.2 * rng.standard_normal(D)
+    pos = O.positions(S_L, h, w)
+    x = rng.standard_normal((len(pos), D))
+    vecc = rng.standard_normal(D)
+    return W, pos, x, vecc
+
+
+def _oracle_block(W, pos, x, vecc, arch):
+    c, s = O.rope_tables(pos, arch.axes)
+    bw = O.BlockWeights(**W)
+    return O.block_forward(x, bw, vecc, c, s, arch)
+
+
+def _brute_block(W, pos, x, vecc, arch, rms=False):
+    # the brute force takes its angles in float64 straight from the positions
+    # (the oracle's tables are fp32, so the two differ by fp32 rounding only)
+    ang = [brute.angles(list(map(float, p)), arch.axes) for p in pos]
+    Wl = {k: (brute.mat(v) if np.ndim(v) == 2 else brute.vec(v)) for k, v in W.items()}
+    return np.array(brute.block(brute.mat(x), Wl, brute.vec(vecc), ang,
+                                arch.hidden, arch.heads, arch.head_dim, arch.ffn, rms=rms))
+
+
+@pytest.mark.parametrize("rms", [False, True])
+def test_block_brute_force(rms):
+    arch = O.Arch(16, 2, 8, 12, axes=(2, 2, 4), norm="rms" if rms else "layer")
+    W, pos, x, vecc = _tiny_case(rms=rms)
+    y = _oracle_block(W, pos, x, vecc, arch)
+    yb = _brute_block(W, pos, x, vecc, arch, rms=rms)
+    # differences come from the fp32 rounding of the oracle's rotary tables
+    assert np.abs(y - yb).max() < 2e-6, np.abs(y - yb).max()
+    assert np.abs((y - x) - (yb - x)).max() / np.abs(yb - x).max() < 2e-6
+
+
+def test_block_zero_modulation_is_identity():
+    W, pos, x, vecc = _tiny_case()
+    W["w_mod"] = np.zeros_like(W["w_mod"])
+    assert (_oracle_block(W, pos, x, vecc, TINY) == x).all()
+
+
+def test_block_gate_isolation():
+    W, pos, x, vecc = _tiny_case()
+    D = TINY.hidden
+    # gate_a rows (third chunk) zero: the output cannot depend on the QKV/OUT weights
+    W["w_mod"][2 * D:3 * D] = 0
+    y1 = _oracle_block(W, pos, x, vecc, TINY)
+    W2 = dict(W); W2["w_qkv"] = W["w_qkv"] * -3.0 + 1; W2["w_out"] = W["w_out"].T.copy()
+    assert (y1 == _oracle_block(W2, pos, x, vecc, TINY)).all()
+    # gate_m rows (sixth chunk) zero: the output cannot depend on UP/DOWN
+    W3, pos, x, vecc = _tiny_case(seed=11)
+    W3["w_mod"][5 * D:6 * D] = 0
+    y3 = _oracle_block(W3, pos, x, vecc, TINY)
+    W4 = dict(W3); W4["w_up"] = W3["w_up"][::-1].copy()
+    assert (y3 == _oracle_block(W4, pos, x, vecc, TINY)).all()
+    assert not np.allclose(y3, x)
+
+
+def test_block_row_permutation_equivariance():
+    W, pos, x, vecc = _tiny_case(S_L=3, h=2, w=3)
+    y = _oracle_block(W, pos, x, vecc, TINY)
+    perm = np.random.default_rng(12).permutation(len(pos))
+    yp = _oracle_block(W, pos[perm], x[perm], vecc, TINY)
+    assert np.allclose(yp, y[perm], atol=1e-12)
+
+
+def test_block_rows_matches_full():
+    W, pos, x, vecc = _tiny_case(S_L=3, h=3, w=3)
+    c, s = O.rope_tables(pos, TINY.axes)
+    bw = O.BlockWeights(**W)
+    y, inter = O.block_forward(x, bw, vecc, c, s, TINY, keep=True)
+    rows = np.array([0, 4, 11])
+    yr, o, x1, a = O.block_forward_rows(x, bw, vecc, c, s, TINY, rows)
+    assert np.allclose(yr, y[rows], atol=1e-12)
+    assert np.allclose(o, inter["o"][rows], atol=1e-12)
+    assert np.allclose(a, inter["a"][rows], atol=1e-12)
+
+
+def test_block_precision_consistency():
+    # the oracle is a float64 definition: re-running it on float32-cast
+    # inputs moves the result by float32 rounding only
+    W, pos, x, vecc = _tiny_case()
+    y = _oracle_block(W, pos, x, vecc, TINY)
+    W32 = {k: np.float32(v).astype(np.float64) for k, v in W.items()}
+    y32 = _oracle_block(W32, pos, np.float32(x).astype(np.float64), np.float32(vecc).astype(np.float64), TINY)
+    assert np.abs(y - y32).max() < 1e-5
+
+
+# ---------------------------------------------------------------- time vector, modulation
+
+def test_time_vector_brute_force():
+    rng = np.random.default_rng(13)
+    w1 = rng.standard_normal((16, 8)) * 0.3; w2 = rng.standard_normal((16, 16)) * 0.3
+    v = O.time_vector(0.37, w1, w2, dim=8)
+    e = brute.time_embed(0.37, 8)
+    h = [brute.silu(z) for z in brute.matvec(brute.mat(w1), e)]
+    vb = brute.matvec(brute.mat(w2), h)
+    assert np.abs(v - np.array(vb)).max() < 1e-12
+    m = O.modulation(v, rng.standard_normal((6 * 16, 16)), 6)
+    assert m.shape == (6, 16)
+
+
+# ---------------------------------------------------------------- whole DiT
+
+def _tiny_model(seed=14, blocks=2, L=2, h=2, w=2, text_dim=6, latent=4):
+    rng = np.random.default_rng(seed)
+    D = TINY.hidden
+    blks = []
+    for b in range(blocks):
+        W, _, _, _ = _tiny_case(seed=seed + 100 + b, S_L=L, h=h, w=w)
+        blks.append(O.BlockWeights(**W))
+    mw = O.ModelWeights(w_t1=rng.standard_normal((D, 8)) * 0.3, w_t2=rng.standard_normal((D, D)) * 0.3,
+                        w_in=rng.standard_normal((D, latent)) * 0.3,
+                        w_txt=rng.standard_normal((D, text_dim)) * 0.3,
+                        w_fmod=rng.standard_normal((2 * D, D)) * 0.3,
+                        w_final=rng.standard_normal((latent, D)) * 0.3, blocks=blks)
+    x_lat = rng.standard_normal((h * w, latent))
+    ctx = rng.standard_normal((L, text_dim))
+    return mw, x_lat, ctx, O.positions(L, h, w)
+
+
+def test_velocity_brute_force():
+    arch = O.Arch(16, 2, 8, 12, axes=(2, 2, 4), time_dim=8, latent=4)
+    mw, x_lat, ctx, pos = _tiny_model()
+    c, s = O.rope_tables(pos, arch.axes)
+    t = 0.6
+    v = O.velocity(x_lat, O.text_rows(ctx, mw), mw, c, s, t, arch)
+    # brute force: text rows, image rows, blocks, final modulated norm, out linear
+    ang = [brute.angles(list(map(float, p)), arch.axes) for p in pos]
+    seq = [brute.matvec(brute.mat(mw.w_txt), brute.vec(r)) for r in ctx]
+    seq += [brute.matvec(brute.mat(mw.w_in), brute.vec(r)) for r in x_lat]
+    vecc = brute.matvec(brute.mat(mw.w_t2), [brute.silu(z) for z in
+                        brute.matvec(brute.mat(mw.w_t1), brute.time_embed(t, 8))])
+    for bw in mw.blocks:
+        Wl = {k: (brute.mat(getattr(bw, k)) if np.ndim(getattr(bw, k)) == 2 else brute.vec(getattr(bw, k)))
+              for k in ("w_qkv", "w_out", "w_up", "w_down", "w_mod", "q_norm", "k_norm")}
+        seq = brute.block(seq, Wl, vecc, ang, 16, 2, 8, 12)
+    fm = brute.matvec(brute.mat(mw.w_fmod), [brute.silu(z) for z in vecc])
+    vb = []
+    for r in seq[2:]:
+        n = brute.layernorm(r, 1e-6)
+        hrow = [n[i] * (1 + fm[16 + i]) + fm[i] for i in range(16)]
+        vb.append(brute.matvec(brute.mat(mw.w_final), hrow))
+    assert np.abs(v - np.array(vb)).max() < 2e-6
+
+
+def test_denoise_zero_final_keeps_latent():
+    arch = O.Arch(16, 2, 8, 12, axes=(2, 2, 4), time_dim=8, latent=4)
+    mw, x_lat, ctx, pos = _tiny_model()
+    mw.w_final = np.zeros_like(mw.w_final)
+    c, s = O.rope_tables(pos, arch.axes)
+    x = O.denoise(np.float32(x_lat), ctx, mw, c, s, O.sigma_grid(4), arch)
+    assert (x == np.float32(x_lat)).all()
+
+
+def test_denoise_composes_velocity_and_euler():
+    arch = O.Arch(16, 2, 8, 12, axes=(2, 2, 4), time_dim=8, latent=4)
+    mw, x_lat, ctx, pos = _tiny_model()
+    c, s = O.rope_tables(pos, arch.axes)
+    sig = O.sigma_grid(2)
+    x, vels = O.denoise(np.float32(x_lat), ctx, mw, c, s, sig, arch, keep_velocities=True)
+    x0 = np.float32(x_lat)
+    v0 = np.float32(O.velocity(x0, O.text_rows(ctx, mw), mw, c, s, 1.0, arch))
+    assert (vels[0] == v0).all()
+    x1 = O.euler_step(x0, v0, 1.0, 0.5)
+    v1 = np.float32(O.velocity(x1, O.text_rows(ctx, mw), mw, c, s, 0.5, arch))
+    assert (x == O.euler_step(x1, v1, 0.5, 0.0)).all()
+
+
+def test_block_flops_config_north_star():
+    arch = O.Arch(3072, 24, 128, 12288)
+    f = O.block_flops(4608, arch)
+    assert abs(f / 1e9 - 1652.6) < 0.1
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _brute_fails(monkeypatch, name, bad):
+    monkeypatch.setattr(O.dit_oracle, name, bad)
+    W, pos, x, vecc = _tiny_case()
+    y = O.dit_oracle.block_forward(x, O.BlockWeights(**W), vecc, *O.rope_tables(pos, TINY.axes), TINY)
+    yb = _brute_block(W, pos, x, vecc, TINY)
+    return np.abs(y - yb).max() > 1e-4
+
+
+def test_pins_catch_rope_sign(monkeypatch):
+    good = O.dit_oracle.rope_apply
+    assert _brute_fails(monkeypatch, "rope_apply", lambda v, c, s: good(v, c, -s))
+
+
+def test_pins_catch_softmax_axis(monkeypatch):
+    def bad(q, k, v, scale=None):
+        out = np.empty(q.shape)
+        for h in range(q.shape[0]):
+            sc = q[h] @ k[h].T / math.sqrt(q.shape[-1])
+            p = np.exp(sc - sc.max(0, keepdims=True)); p /= p.sum(0, keepdims=True)
+            out[h] = p @ v[h]
+        return out
+    assert _brute_fails(monkeypatch, "attention", bad)
+
+
+def test_pins_catch_glu_order(monkeypatch):
+    assert _brute_fails(monkeypatch, "swiglu_interleaved",
+                        lambda u: O.silu(u[..., 1::2]) * u[..., 0::2])
+
+
+def test_pins_catch_modulation_order(monkeypatch):
+    good = O.dit_oracle.modulation
+    assert _brute_fails(monkeypatch, "modulation", lambda v, w, c=6: good(v, w, c)[[1, 0, 2, 3, 4, 5]])
+
+
+def test_pins_catch_head_norm_weight(monkeypatch):
+    good = O.dit_oracle.head_prep
+    assert _brute_fails(monkeypatch, "head_prep", lambda qk, w, e, c, s: good(qk, w[::-1], e, c, s))
+
+
+def test_pins_catch_transposed_out_projection(monkeypatch):
+    good = O.dit_oracle.linear
+    calls = {"n": 0}
+
+    def bad(x, w):
+        calls["n"] += 1
+        w = np.asarray(w)
+        if calls["n"] == 3 and w.shape[0] == w.shape[1]:   # the output projection
+            return good(x, w.T)
+        return good(x, w)
+    assert _brute_fails(monkeypatch, "linear", bad)
