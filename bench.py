@@ -1,0 +1,283 @@
+"""Benchmark of the DiT hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--images I] [--no-cpu]
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value      block-forward TFLOP/s at the 1024-px block (L=512 text + N=4096
+             image rows, hidden 3072, 24 heads x 128, SwiGLU ffn 12288, bf16
+             weights), algorithmic FLOPs (2*M*N*K per product, 4*H*S^2*d for
+             attention, the modulation GEMV) over the measured time of K
+             consecutive dit_block_forward calls (inputs resident in HBM);
+  images_per_s  the whole path for one image: positions and rotary tables,
+             the text-row prologue and 4 Euler steps of a 32-block DiT
+             (random-init bf16 weights), timed over I images;
+  roofline   the dominant kernel's algorithmic TFLOP/s from HIP events around
+             its launches, against the bf16 dense MFMA peak;
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--images", type=int, default=2)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-denoise", action="store_true", help="skip the 32-block image timing")
+    p.add_argument("--no-int8", action="store_true", help="skip the int8-weight block timing")
+    return p.parse_args()
+
+
+def stage_flops(S, D, H, F):
+    """Algorithmic FLOPs of each block stage at S rows."""
+    return {
+        "mod": 2 * 6 * D * D,
+        "qkv": 2 * S * D * 3 * D,
+        "attn": 4 * H * S * S * 128,
+        "out": 2 * S * D * D,
+        "up": 2 * S * D * 2 * F,
+        "down": 2 * S * F * D,
+    }
+
+
+def time_blocks(L, torch, ctx, bw, x, seq, sh, steps, warmup):
+    for _ in range(warmup):
+        ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is "
+              "described in DESIGN.md and not run here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from diffusion_transformer_amd import lib as L
+    from diffusion_transformer_amd import synth
+
+    torch.cuda.set_device(0)
+    out = {}
+
+    # ---------------------------------------------------------------- block forward (bf16)
+    sh = synth.SHAPES["s4608"]
+    S, D, H, F = sh.S, sh.hidden, sh.heads, sh.ffn
+    arch = L.make_arch(hidden=D, heads=H, ffn=F)
+    ctx = L.Context(arch, max_rows=S)
+    log("generating the 1024-px block inputs")
+    case = synth.block_case("s4608")
+    bw = L.BlockWeights.from_host(case["block"])
+
+    class Seq:
+        pass
+
+    seq = Seq()
+    seq.pos = torch.empty((S, 3), dtype=torch.int32, device="cuda")
+    seq.cos = torch.empty((S, 64), dtype=torch.float32, device="cuda")
+    seq.sin = torch.empty_like(seq.cos)
+    seq.vec = torch.empty(D, dtype=torch.float32, device="cuda")
+    ctx.positions(sh.L, sh.h, sh.w, seq.pos)
+    ctx.rope_tables(seq.pos, S, seq.cos, seq.sin)
+    ctx.time_vector(L.dev_bf16(case["w_t1"]), L.dev_bf16(case["w_t2"]), float(case["t"]), seq.vec)
+    x = L.dev_f32(case["x"])
+    fl = stage_flops(S, D, H, F)
+    total_flops = sum(fl.values())
+    log(f"block forward: {args.warmup} warmup + {args.steps} timed steps")
+    ms = time_blocks(L, torch, ctx, bw, x, seq, sh, args.steps, args.warmup)
+    tflops = total_flops / (ms * 1e-3) / 1e12
+    log(f"block: {ms:.3f} ms  {tflops:.1f} TFLOP/s  ({100 * tflops / PEAK_BF16_TFLOPS:.1f} % of bf16 peak)")
+
+    # per-stage breakdown with HIP events on the library's stream
+    ctx.timing(True)
+    for _ in range(args.steps):
+        ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    tm = ctx.timing_read()
+    ctx.timing(False)
+    stages = {k: v[0] / v[1] for k, v in tm.items() if v[1]}
+    log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+    dom = max((k for k in stages if k in fl), key=lambda k: stages[k])
+    dom_tf = fl[dom] / (stages[dom] * 1e-3) / 1e12
+    roofline = {"kernel": f"{dom} product" if dom not in ("attn", "mod") else dom, "bound": "mfma",
+                "achieved": round(dom_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": fl[dom], "avg_ms": round(stages[dom], 4)}
+    del bw, x, case
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- int8 block
+    int8_tf = None
+    if not args.no_int8:
+        log("int8-weight block")
+        c8 = synth.block_case("s4608_int8")
+        bw8 = L.BlockWeights.from_host(c8["block"])
+        x8 = L.dev_f32(c8["x"])
+        ms8 = time_blocks(L, torch, ctx, bw8, x8, seq, sh, max(3, args.steps // 2), 2)
+        int8_tf = total_flops / (ms8 * 1e-3) / 1e12
+        log(f"int8 block: {ms8:.3f} ms  {int8_tf:.1f} TFLOP/s")
+        del bw8, x8, c8
+        torch.cuda.empty_cache()
+    ctx.close()
+
+    # ---------------------------------------------------------------- whole image
+    img = None
+    if not args.no_denoise:
+        img = bench_images(torch, L, synth, args.images)
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None if args.no_cpu else cpu_baseline()
+
+    out = {
+        "metric": "DiT block fwd TFLOP/s (% bf16 MFMA peak) at N=4096; images/s, 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dit_block_forward, 1024-px block: L=512 text + N=4096 image rows, "
+                               "hidden 3072, 24 heads x 128, SwiGLU ffn 12288, bf16 weights",
+                   "L": sh.L, "N": sh.N, "hidden": D, "heads": H, "head_dim": 128, "ffn": F,
+                   "flops_per_step": total_flops},
+        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": roofline,
+        "int8_block_tflops": None if int8_tf is None else round(int8_tf, 2),
+    }
+    if img:
+        out.update(img)
+    out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+def bench_images(torch, L, synth, images):
+    """Whole path per image at the 1024-px DiT: 32 blocks, 4 Euler steps."""
+    sh = synth.SHAPES["dit32"]
+    S, D, H, F, lat = sh.S, sh.hidden, sh.heads, sh.ffn, sh.latent
+    arch = L.make_arch(hidden=D, heads=H, ffn=F, latent=lat, text_dim=sh.text_dim)
+    ctx = L.Context(arch, max_rows=S)
+    log("generating 32 blocks of random bf16 weights on the GPU")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(sh.seed)
+
+    def w(o, i):
+        t = torch.randn((o, i), generator=g, device="cuda", dtype=torch.float32).mul_(0.02)
+        return t.to(torch.bfloat16)
+
+    blocks = []
+    for _ in range(sh.blocks):
+        t = {"w_qkv": w(3 * D, D), "w_out": w(D, D), "w_up": w(2 * F, D), "w_down": w(D, F),
+             "w_mod": w(6 * D, D),
+             "q_norm": torch.ones(128, device="cuda"), "k_norm": torch.ones(128, device="cuda")}
+        blocks.append(L.BlockWeights(t))
+    top = {"w_t1": w(D, sh.time_dim), "w_t2": w(D, D), "w_in": w(D, lat), "w_txt": w(D, sh.text_dim),
+           "w_fmod": w(2 * D, D), "w_final": w(lat, D)}
+    model = L.ModelWeights(top, blocks)
+    x0 = torch.randn((sh.N, lat), generator=g, device="cuda")
+    ctx_feats = torch.randn((sh.L, sh.text_dim), generator=g, device="cuda")
+    pos = torch.empty((S, 3), dtype=torch.int32, device="cuda")
+    cs = torch.empty((S, 64), dtype=torch.float32, device="cuda")
+    sn = torch.empty_like(cs)
+    txt = torch.empty((sh.L, D), dtype=torch.float32, device="cuda")
+    sig = np.linspace(1.0, 0.0, 5).astype(np.float32)
+
+    def one_image(x):
+        ctx.positions(sh.L, sh.h, sh.w, pos)
+        ctx.rope_tables(pos, S, cs, sn)
+        ctx.prologue(model, ctx_feats, sh.L, txt)
+        for i in range(4):
+            ctx.denoise_step(model, x, txt, cs, sn, sh.L, sh.N, float(sig[i]), float(sig[i + 1]))
+
+    x = x0.clone()
+    one_image(x)                       # warm-up image
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(images):
+        x.copy_(x0)
+        one_image(x)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / images
+    finite = bool(torch.isfinite(x).all().item())
+    blk = sum(stage_flops(S, D, H, F).values())
+    img_flops = 4 * (sh.blocks * blk + 2 * sh.N * lat * D + 2 * sh.N * D * lat + 2 * D * 256
+                     + 2 * D * D + 2 * 2 * D * D) + 2 * sh.L * sh.text_dim * D
+    log(f"image: {ms:.1f} ms  {1000 / ms:.3f} img/s  {img_flops / ms / 1e9:.1f} TFLOP/s  finite={finite}")
+    ctx.close()
+    del model, blocks, top
+    torch.cuda.empty_cache()
+    return {"images_per_s": round(1000.0 / ms, 4), "ms_per_image": round(ms, 2),
+            "image_tflops": round(img_flops / ms / 1e9, 2), "image_flops": img_flops,
+            "image_workload": "32-block DiT, 4 Euler steps (sigmas 1, .75, .5, .25, 0), L=512 + N=4096, "
+                              "latent 64, text features 4096-d, batch 1, random-init bf16 weights",
+            "image_finite": finite}
+
+
+def cpu_baseline():
+    """The CPU oracle (float64 NumPy) on one whole 512-px block forward
+    (L=64 + N=1024 rows, hidden 3072, ffn 12288): ~343 GFLOP of the same
+    per-row arithmetic as the 1024-px block, reported in the metric's unit."""
+    import oracle as O
+    from diffusion_transformer_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    case = synth.block_case("s1088")
+    sh = case["shape"]
+    oa = O.Arch(sh.hidden, sh.heads, 128, sh.ffn)
+    pos = O.positions(sh.L, sh.h, sh.w)
+    cs, sn = O.rope_tables(pos)
+    b = case["block"]
+    bw = O.BlockWeights(w_qkv=b["w_qkv"], w_out=b["w_out"], w_up=b["w_up"], w_down=b["w_down"],
+                        w_mod=b["w_mod"], q_norm=b["q_norm"], k_norm=b["k_norm"])
+    t0 = time.perf_counter()
+    vec = O.time_vector(float(case["t"]), case["w_t1"], case["w_t2"])
+    O.block_forward(case["x"], bw, vec, cs, sn, oa)
+    dt = time.perf_counter() - t0
+    flops = O.block_flops(sh.S, oa)
+    log(f"cpu oracle: {dt:.1f} s for {flops / 1e9:.1f} GFLOP ({threads} threads)")
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": "one whole block forward of the float64 NumPy oracle at the 512-px block "
+                      "(L=64 + N=1024 rows, hidden 3072, 24x128 heads, ffn 12288), 343.2 GFLOP"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,584 @@
+// libdit C ABI: argument validation, the context and its workspace, and the
+// launch sequences of a block forward and a denoise step.
+//
+// Sources: "gizai:dit" reference (Block.forward, Work, CHUNK, Modulation);
+// "Host contract -- RGBA-Image-2.1-Turbo" s.1 (DiT graph boundary and axes),
+// s.4 (positions, rotary tables), s.6 (Euler sampler); "944 -> 346 ms:
+// optimizing FLUX.2 klein-4B on one TPU v6e chip" s.4.1 (resident weights)
+// and Appendix B D2 (text rows and rotary tables hoisted out of the loop).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/dit.h"
+#include "kernels.h"
+
+using namespace dit;
+
+struct dit_ctx {
+    int device = -1;
+    hipStream_t stream = nullptr;
+    dit_arch arch{};
+    int max_rows = 0;
+    int max_rows_pad = 0;
+    void *pool = nullptr;
+    size_t pool_bytes = 0;
+    // workspace ([GZ] Work), carved from one allocation
+    float *mod = nullptr, *vec = nullptr, *temb = nullptr, *t1 = nullptr, *fmod = nullptr;
+    uint16_t *h = nullptr, *h2 = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr,
+             *a = nullptr, *latb = nullptr, *ctxb = nullptr;
+    float *seq = nullptr, *vel = nullptr;
+    size_t bytes[8] = {};
+    std::string err;
+    // stage timing
+    bool timing = false;
+    struct Rec {
+        int stage;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> spare;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+dit_status fail(dit_ctx *c, dit_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (c)
+        c->err = buf;
+    else
+        g_err = buf;
+    return s;
+}
+
+dit_status check_launch(dit_ctx *c, hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(c, DIT_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return DIT_OK;
+}
+
+#define DIT_TRY(expr)                      \
+    do {                                   \
+        dit_status _s = (expr);            \
+        if (_s != DIT_OK) return _s;       \
+    } while (0)
+
+#define DIT_LAUNCH(c, expr, what) DIT_TRY(check_launch((c), (expr), (what)))
+
+int round_up(int a, int b) { return (a + b - 1) / b * b; }
+
+hipEvent_t take_event(dit_ctx *c) {
+    if (!c->spare.empty()) {
+        hipEvent_t e = c->spare.back();
+        c->spare.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets one launch stage with HIP events when timing is enabled.
+struct Stage {
+    dit_ctx *c;
+    int stage;
+    hipEvent_t a = nullptr;
+    Stage(dit_ctx *ctx, int s) : c(ctx), stage(s) {
+        if (!c->timing) return;
+        a = take_event(c);
+        if (a) hipEventRecord(a, c->stream);
+    }
+    ~Stage() {
+        if (!a) return;
+        hipEvent_t b = take_event(c);
+        if (!b) {
+            c->spare.push_back(a);
+            return;
+        }
+        hipEventRecord(b, c->stream);
+        c->recs.push_back({stage, a, b});
+    }
+};
+
+void drop_records(dit_ctx *c) {
+    for (auto &r : c->recs) {
+        c->spare.push_back(r.a);
+        c->spare.push_back(r.b);
+    }
+    c->recs.clear();
+}
+
+dit_status validate_arch(const dit_arch *a) {
+    if (!a) return fail(nullptr, DIT_EINVAL, "arch is NULL");
+    if (a->head_dim != 128) return fail(nullptr, DIT_EUNSUPPORTED, "head_dim %d: only 128 is supported", a->head_dim);
+    if (a->heads < 1 || a->hidden != a->heads * a->head_dim)
+        return fail(nullptr, DIT_EINVAL, "hidden %d != heads %d * head_dim %d", a->hidden, a->heads, a->head_dim);
+    if (a->hidden % 256 || a->hidden > 4096)
+        return fail(nullptr, DIT_EUNSUPPORTED, "hidden %d: must be a multiple of 256, at most 4096", a->hidden);
+    if (a->ffn < 256 || a->ffn % 256 || a->ffn > 65536)
+        return fail(nullptr, DIT_EUNSUPPORTED, "ffn %d: must be a multiple of 256 in 256..65536", a->ffn);
+    if (a->axes[0] < 0 || a->axes[1] < 0 || a->axes[2] < 0 || a->axes[0] % 2 || a->axes[1] % 2 ||
+        a->axes[2] % 2 || a->axes[0] + a->axes[1] + a->axes[2] != a->head_dim)
+        return fail(nullptr, DIT_EINVAL, "rotary axes %d+%d+%d must be even and sum to head_dim", a->axes[0],
+                    a->axes[1], a->axes[2]);
+    if (!(a->eps > 0) || !(a->qk_eps > 0) || !(a->final_eps > 0) || !(a->rope_theta > 0))
+        return fail(nullptr, DIT_EINVAL, "eps and rope_theta must be positive");
+    if (a->norm != DIT_NORM_LAYER && a->norm != DIT_NORM_RMS) return fail(nullptr, DIT_EINVAL, "unknown norm %d", a->norm);
+    if (a->time_dim < 2 || a->time_dim % 8 || a->time_dim > 4096)
+        return fail(nullptr, DIT_EINVAL, "time_dim %d: must be a multiple of 8 in 8..4096", a->time_dim);
+    if (a->latent < 64 || a->latent % 64 || a->latent > 4096)
+        return fail(nullptr, DIT_EINVAL, "latent %d: must be a multiple of 64", a->latent);
+    if (a->text_dim < 64 || a->text_dim % 64 || a->text_dim > 65536)
+        return fail(nullptr, DIT_EINVAL, "text_dim %d: must be a multiple of 64", a->text_dim);
+    return DIT_OK;
+}
+
+dit_status check_ctx(dit_ctx *c) {
+    if (!c) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (c->device < 0 || !c->pool) return fail(c, DIT_EDEVICE, "context has no device");
+    if (hipSetDevice(c->device) != hipSuccess) return fail(c, DIT_EDEVICE, "hipSetDevice(%d) failed", c->device);
+    return DIT_OK;
+}
+
+dit_status check_block(dit_ctx *c, const dit_block *b) {
+    if (!b) return fail(c, DIT_EINVAL, "block is NULL");
+    if (b->wtype != DIT_W_BF16 && b->wtype != DIT_W_INT8_B32) return fail(c, DIT_EINVAL, "unknown wtype %d", b->wtype);
+    for (int i = 0; i < 4; ++i) {
+        if (!b->w[i]) return fail(c, DIT_EINVAL, "block weight w[%d] is NULL", i);
+        if (b->wtype == DIT_W_INT8_B32 && !b->scale[i]) return fail(c, DIT_EINVAL, "int8 weight %d has no scales", i);
+        if (b->wtype == DIT_W_BF16 && b->scale[i]) return fail(c, DIT_EINVAL, "bf16 weight %d given scales", i);
+    }
+    if (!b->w_mod) return fail(c, DIT_EINVAL, "block w_mod is NULL");
+    if (!b->norm_w[2] || !b->norm_w[3]) return fail(c, DIT_EINVAL, "head-norm weights are NULL");
+    if (c->arch.norm == DIT_NORM_RMS && (!b->norm_w[0] || !b->norm_w[1]))
+        return fail(c, DIT_EINVAL, "RMSNorm needs norm weights NORM1 and NORM2");
+    return DIT_OK;
+}
+
+dit_status check_rows(dit_ctx *c, int L, int N) {
+    if (L < 0 || L > 512) return fail(c, DIT_ERANGE, "L = %d outside 0..512", L);
+    if (N < 1 || N > 4096) return fail(c, DIT_ERANGE, "N = %d outside 1..4096", N);
+    if (L + N > c->max_rows) return fail(c, DIT_ERANGE, "L + N = %d exceeds max_rows %d", L + N, c->max_rows);
+    return DIT_OK;
+}
+
+// The block forward's launch sequence (validated arguments).
+dit_status block_forward(dit_ctx *c, const dit_block *b, float *x, const float *vec, const float *cs,
+                         const float *sn, int S) {
+    const dit_arch &A = c->arch;
+    const int D = A.hidden, F = A.ffn, H = A.heads;
+    const int Sp = round_up(S, 64);
+    const bool w8 = b->wtype == DIT_W_INT8_B32;
+    const bool rms = A.norm == DIT_NORM_RMS;
+    hipStream_t st = c->stream;
+    float *mod = c->mod;
+
+    {
+        Stage t(c, DIT_ST_MOD);
+        DIT_LAUNCH(c, launch_gemv(b->w_mod, vec, 6 * D, D, true, mod, st), "modulation");
+    }
+    {
+        Stage t(c, DIT_ST_NORM1);
+        DIT_LAUNCH(c, launch_modnorm(x, S, D, mod, mod + D, b->norm_w[0], rms, A.eps, c->h, st), "norm1");
+    }
+
+    GemmEpi e{};
+    e.kind = EPI_QKV;
+    e.q = c->q;
+    e.k = c->k;
+    e.vt = c->vt;
+    e.heads = H;
+    e.ldv = Sp;
+    e.qn = b->norm_w[2];
+    e.kn = b->norm_w[3];
+    e.cos = cs;
+    e.sin = sn;
+    e.qk_eps = A.qk_eps;
+    {
+        Stage t(c, DIT_ST_QKV);
+        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], b->scale[0], w8, S, 3 * D, D, e, st), "qkv");
+    }
+    {
+        Stage t(c, DIT_ST_ATTN);
+        DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
+    }
+
+    GemmEpi g{};
+    g.kind = EPI_GATE_RES;
+    g.out = x;
+    g.ldo = D;
+    g.gate = mod + 2 * D;
+    {
+        Stage t(c, DIT_ST_OUT);
+        DIT_LAUNCH(c, launch_gemm(c->o, b->w[1], b->scale[1], w8, S, D, D, g, st), "out");
+    }
+    {
+        Stage t(c, DIT_ST_NORM2);
+        DIT_LAUNCH(c, launch_modnorm(x, S, D, mod + 3 * D, mod + 4 * D, b->norm_w[1], rms, A.eps, c->h2, st),
+                   "norm2");
+    }
+
+    GemmEpi u{};
+    u.kind = EPI_SWIGLU;
+    u.act = c->a;
+    {
+        Stage t(c, DIT_ST_UP);
+        DIT_LAUNCH(c, launch_gemm(c->h2, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st), "up");
+    }
+    g.gate = mod + 5 * D;
+    {
+        Stage t(c, DIT_ST_DOWN);
+        DIT_LAUNCH(c, launch_gemm(c->a, b->w[3], b->scale[3], w8, S, D, F, g, st), "down");
+    }
+    return DIT_OK;
+}
+
+dit_status time_vector(dit_ctx *c, const uint16_t *w1, const uint16_t *w2, float t, float *vec) {
+    const dit_arch &A = c->arch;
+    hipStream_t st = c->stream;
+    Stage tm(c, DIT_ST_TIME);
+    DIT_LAUNCH(c, launch_time_embedding(t, A.time_dim, c->temb, st), "time embedding");
+    DIT_LAUNCH(c, launch_gemv(w1, c->temb, A.hidden, A.time_dim, false, c->t1, st), "time mlp 1");
+    DIT_LAUNCH(c, launch_gemv(w2, c->t1, A.hidden, A.hidden, true, vec, st), "time mlp 2");
+    return DIT_OK;
+}
+
+dit_status check_model(dit_ctx *c, const dit_model *m) {
+    if (!m) return fail(c, DIT_EINVAL, "model is NULL");
+    if (m->n_blocks < 0 || m->n_blocks > 1024) return fail(c, DIT_ERANGE, "n_blocks %d outside 0..1024", m->n_blocks);
+    if (m->n_blocks > 0 && !m->blocks) return fail(c, DIT_EINVAL, "model blocks array is NULL");
+    if (!m->w_t1 || !m->w_t2 || !m->w_in || !m->w_txt || !m->w_fmod || !m->w_final)
+        return fail(c, DIT_EINVAL, "a model weight pointer is NULL");
+    for (int i = 0; i < m->n_blocks; ++i) DIT_TRY(check_block(c, &m->blocks[i]));
+    return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dit_version(void) { return "libdit 0.1 (gfx950)"; }
+
+const char *dit_last_error(const dit_ctx *ctx) {
+    if (ctx) return ctx->err.c_str();
+    return g_err.c_str();
+}
+
+dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arch *arch, int max_rows) {
+    if (!out) return fail(nullptr, DIT_EINVAL, "out is NULL");
+    *out = nullptr;
+    DIT_TRY(validate_arch(arch));
+    if (max_rows < 1 || max_rows > 65536) return fail(nullptr, DIT_ERANGE, "max_rows %d outside 1..65536", max_rows);
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0)
+        return fail(nullptr, DIT_EDEVICE, "no HIP device available");
+    if (device < 0 || device >= count) return fail(nullptr, DIT_EDEVICE, "device %d outside 0..%d", device, count - 1);
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+        return fail(nullptr, DIT_EDEVICE, "cannot query device %d", device);
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(nullptr, DIT_EDEVICE, "device %d is %s; this library is built for gfx950", device, prop.gcnArchName);
+    if (hipSetDevice(device) != hipSuccess) return fail(nullptr, DIT_EDEVICE, "hipSetDevice(%d) failed", device);
+
+    dit_ctx *c = new (std::nothrow) dit_ctx();
+    if (!c) return fail(nullptr, DIT_ENOMEM, "out of host memory");
+    c->device = device;
+    c->stream = static_cast<hipStream_t>(stream);
+    c->arch = *arch;
+    c->max_rows = max_rows;
+    c->max_rows_pad = round_up(max_rows, 256);
+
+    const size_t S = c->max_rows_pad, D = arch->hidden, F = arch->ffn, H = arch->heads;
+    const size_t sizes[] = {
+        6 * D * 4, D * 4, size_t(arch->time_dim) * 4, D * 4, 2 * D * 4,  // mod vec temb t1 fmod
+        S * D * 2, S * D * 2,                                          // h h2
+        H * S * 128 * 2, H * S * 128 * 2, H * 128 * S * 2,             // q k vt
+        S * D * 2, S * F * 2,                                          // o a
+        S * size_t(arch->latent) * 2, S * size_t(arch->text_dim) * 2,  // latb ctxb
+        S * D * 4, S * size_t(arch->latent) * 4,                       // seq vel
+    };
+    size_t off[sizeof sizes / sizeof sizes[0]];
+    size_t total = 0;
+    for (size_t i = 0; i < sizeof sizes / sizeof sizes[0]; ++i) {
+        off[i] = total;
+        total += (sizes[i] + 255) / 256 * 256;
+    }
+    if (hipMalloc(&c->pool, total) != hipSuccess) {
+        delete c;
+        return fail(nullptr, DIT_ENOMEM, "workspace allocation of %zu bytes failed", total);
+    }
+    c->pool_bytes = total;
+    char *p = static_cast<char *>(c->pool);
+    c->mod = reinterpret_cast<float *>(p + off[0]);
+    c->vec = reinterpret_cast<float *>(p + off[1]);
+    c->temb = reinterpret_cast<float *>(p + off[2]);
+    c->t1 = reinterpret_cast<float *>(p + off[3]);
+    c->fmod = reinterpret_cast<float *>(p + off[4]);
+    c->h = reinterpret_cast<uint16_t *>(p + off[5]);
+    c->h2 = reinterpret_cast<uint16_t *>(p + off[6]);
+    c->q = reinterpret_cast<uint16_t *>(p + off[7]);
+    c->k = reinterpret_cast<uint16_t *>(p + off[8]);
+    c->vt = reinterpret_cast<uint16_t *>(p + off[9]);
+    c->o = reinterpret_cast<uint16_t *>(p + off[10]);
+    c->a = reinterpret_cast<uint16_t *>(p + off[11]);
+    c->latb = reinterpret_cast<uint16_t *>(p + off[12]);
+    c->ctxb = reinterpret_cast<uint16_t *>(p + off[13]);
+    c->seq = reinterpret_cast<float *>(p + off[14]);
+    c->vel = reinterpret_cast<float *>(p + off[15]);
+    const size_t dbg[8] = {sizes[0], sizes[5], sizes[7], sizes[8], sizes[9], sizes[10], sizes[6], sizes[11]};
+    for (int i = 0; i < 8; ++i) c->bytes[i] = dbg[i];
+    *out = c;
+    return DIT_OK;
+}
+
+void dit_ctx_destroy(dit_ctx *ctx) {
+    if (!ctx) return;
+    if (ctx->pool) {
+        hipSetDevice(ctx->device);
+        drop_records(ctx);
+        for (hipEvent_t e : ctx->spare) hipEventDestroy(e);
+        hipFree(ctx->pool);
+    }
+    delete ctx;
+}
+
+dit_status dit_timing_enable(dit_ctx *ctx, int on) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    DIT_TRY(check_ctx(ctx));
+    drop_records(ctx);
+    ctx->timing = on != 0;
+    return DIT_OK;
+}
+
+dit_status dit_timing_read(dit_ctx *ctx, double *ms, int64_t *count) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!ms || !count) return fail(ctx, DIT_EINVAL, "ms or count is NULL");
+    DIT_TRY(check_ctx(ctx));
+    for (int i = 0; i < DIT_NSTAGES; ++i) {
+        ms[i] = 0.0;
+        count[i] = 0;
+    }
+    dit_status st = DIT_OK;
+    for (auto &r : ctx->recs) {
+        float e = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&e, r.a, r.b) != hipSuccess) {
+            st = fail(ctx, DIT_EDEVICE, "reading a timing event failed");
+            break;
+        }
+        ms[r.stage] += e;
+        count[r.stage] += 1;
+    }
+    drop_records(ctx);
+    return st;
+}
+
+dit_status dit_ctx_set_stream(dit_ctx *ctx, void *stream) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    ctx->stream = static_cast<hipStream_t>(stream);
+    return DIT_OK;
+}
+
+dit_status dit_positions(dit_ctx *ctx, int L, int h, int w, int32_t *pos) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!pos) return fail(ctx, DIT_EINVAL, "pos is NULL");
+    if (L < 0 || h < 1 || w < 1) return fail(ctx, DIT_ERANGE, "L %d, h %d, w %d: need L >= 0, h, w >= 1", L, h, w);
+    if (static_cast<int64_t>(h) * w + L > ctx->max_rows)
+        return fail(ctx, DIT_ERANGE, "L + h*w exceeds max_rows %d", ctx->max_rows);
+    DIT_TRY(check_ctx(ctx));
+    DIT_LAUNCH(ctx, launch_positions(L, h, w, pos, ctx->stream), "positions");
+    return DIT_OK;
+}
+
+dit_status dit_rope_tables(dit_ctx *ctx, const int32_t *pos, int S, float *cos_t, float *sin_t) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!pos || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "pos, cos or sin is NULL");
+    if (S < 1 || S > ctx->max_rows) return fail(ctx, DIT_ERANGE, "S = %d outside 1..%d", S, ctx->max_rows);
+    DIT_TRY(check_ctx(ctx));
+    const dit_arch &A = ctx->arch;
+    DIT_LAUNCH(ctx, launch_rope_tables(pos, S, A.axes[0], A.axes[1], A.axes[2], A.rope_theta, cos_t, sin_t, ctx->stream),
+               "rope tables");
+    return DIT_OK;
+}
+
+dit_status dit_time_vector(dit_ctx *ctx, const uint16_t *w_t1, const uint16_t *w_t2, float t, float *vec) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!w_t1 || !w_t2 || !vec) return fail(ctx, DIT_EINVAL, "w_t1, w_t2 or vec is NULL");
+    DIT_TRY(check_ctx(ctx));
+    return time_vector(ctx, w_t1, w_t2, t, vec);
+}
+
+dit_status dit_modulation(dit_ctx *ctx, const uint16_t *w_mod, int chunks, const float *vec, float *mod) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!w_mod || !vec || !mod) return fail(ctx, DIT_EINVAL, "w_mod, vec or mod is NULL");
+    if (chunks < 1 || chunks > 6) return fail(ctx, DIT_ERANGE, "chunks %d outside 1..6", chunks);
+    DIT_TRY(check_ctx(ctx));
+    const int D = ctx->arch.hidden;
+    DIT_LAUNCH(ctx, launch_gemv(w_mod, vec, chunks * D, D, true, mod, ctx->stream), "modulation");
+    return DIT_OK;
+}
+
+dit_status dit_modulated_norm(dit_ctx *ctx, const float *x, int rows, const float *shift, const float *scale,
+                              const float *norm_w, float eps, uint16_t *out) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !shift || !scale || !out) return fail(ctx, DIT_EINVAL, "x, shift, scale or out is NULL");
+    const bool rms = ctx->arch.norm == DIT_NORM_RMS;
+    if (rms && !norm_w) return fail(ctx, DIT_EINVAL, "RMSNorm needs norm_w");
+    if (rows < 1 || rows > ctx->max_rows) return fail(ctx, DIT_ERANGE, "rows %d outside 1..%d", rows, ctx->max_rows);
+    if (!(eps > 0)) return fail(ctx, DIT_EINVAL, "eps must be positive");
+    DIT_TRY(check_ctx(ctx));
+    DIT_LAUNCH(ctx, launch_modnorm(x, rows, ctx->arch.hidden, shift, scale, norm_w, rms, eps, out, ctx->stream),
+               "modulated norm");
+    return DIT_OK;
+}
+
+dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint16_t *scale, int wtype, int M, int N,
+                      int K, float *out) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!a || !w || !out) return fail(ctx, DIT_EINVAL, "a, w or out is NULL");
+    if (wtype != DIT_W_BF16 && wtype != DIT_W_INT8_B32) return fail(ctx, DIT_EINVAL, "unknown wtype %d", wtype);
+    if (wtype == DIT_W_INT8_B32 && !scale) return fail(ctx, DIT_EINVAL, "int8 weight has no scales");
+    if (wtype == DIT_W_BF16 && scale) return fail(ctx, DIT_EINVAL, "bf16 weight given scales");
+    if (M < 1 || M > ctx->max_rows) return fail(ctx, DIT_ERANGE, "M %d outside 1..%d", M, ctx->max_rows);
+    if (N < 64 || N % 64 || N > 65536) return fail(ctx, DIT_EINVAL, "N %d: must be a multiple of 64 in 64..65536", N);
+    if (K < 64 || K % 64 || K > 65536) return fail(ctx, DIT_EINVAL, "K %d: must be a multiple of 64 in 64..65536", K);
+    DIT_TRY(check_ctx(ctx));
+    GemmEpi e{};
+    e.kind = EPI_F32;
+    e.out = out;
+    e.ldo = N;
+    DIT_LAUNCH(ctx, launch_gemm(a, w, scale, wtype == DIT_W_INT8_B32, M, N, K, e, ctx->stream), "linear");
+    return DIT_OK;
+}
+
+dit_status dit_attention(dit_ctx *ctx, const uint16_t *q, const uint16_t *k, const uint16_t *vt, int heads, int S,
+                         uint16_t *o) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!q || !k || !vt || !o) return fail(ctx, DIT_EINVAL, "q, k, vt or o is NULL");
+    if (heads < 1 || heads > ctx->arch.heads) return fail(ctx, DIT_ERANGE, "heads %d outside 1..%d", heads, ctx->arch.heads);
+    if (S < 1 || S > ctx->max_rows) return fail(ctx, DIT_ERANGE, "S %d outside 1..%d", S, ctx->max_rows);
+    DIT_TRY(check_ctx(ctx));
+    DIT_LAUNCH(ctx, launch_attention(q, k, vt, heads, S, round_up(S, 64), o, heads * 128, ctx->stream), "attention");
+    return DIT_OK;
+}
+
+dit_status dit_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const float *vec, const float *cos_t,
+                             const float *sin_t, int L, int N) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
+    DIT_TRY(check_block(ctx, b));
+    DIT_TRY(check_rows(ctx, L, N));
+    DIT_TRY(check_ctx(ctx));
+    return block_forward(ctx, b, x, vec, cos_t, sin_t, L + N);
+}
+
+dit_status dit_prologue(dit_ctx *ctx, const dit_model *m, const float *ctx_feats, int L, float *txt) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!ctx_feats || !txt) return fail(ctx, DIT_EINVAL, "ctx_feats or txt is NULL");
+    DIT_TRY(check_model(ctx, m));
+    if (L < 1 || L > 512 || L > ctx->max_rows) return fail(ctx, DIT_ERANGE, "L = %d outside 1..512", L);
+    DIT_TRY(check_ctx(ctx));
+    const dit_arch &A = ctx->arch;
+    Stage tm(ctx, DIT_ST_TXT_IN);
+    DIT_LAUNCH(ctx, launch_to_bf16(ctx_feats, static_cast<int64_t>(L) * A.text_dim, ctx->ctxb, ctx->stream), "to bf16");
+    GemmEpi e{};
+    e.kind = EPI_F32;
+    e.out = txt;
+    e.ldo = A.hidden;
+    DIT_LAUNCH(ctx, launch_gemm(ctx->ctxb, m->w_txt, nullptr, false, L, A.hidden, A.text_dim, e, ctx->stream), "txt_in");
+    return DIT_OK;
+}
+
+dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, const float *txt, const float *cos_t,
+                            const float *sin_t, int L, int N, float sigma, float sigma_next, float *vel_out) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x_lat || !cos_t || !sin_t || (L > 0 && !txt)) return fail(ctx, DIT_EINVAL, "x_lat, txt, cos or sin is NULL");
+    DIT_TRY(check_model(ctx, m));
+    DIT_TRY(check_rows(ctx, L, N));
+    DIT_TRY(check_ctx(ctx));
+    const dit_arch &A = ctx->arch;
+    const int D = A.hidden, S = L + N, lat = A.latent;
+    hipStream_t st = ctx->stream;
+
+    DIT_TRY(time_vector(ctx, m->w_t1, m->w_t2, sigma, ctx->vec));
+    {
+        Stage tm(ctx, DIT_ST_IMG_IN);
+        if (L > 0 &&
+            hipMemcpyAsync(ctx->seq, txt, static_cast<size_t>(L) * D * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+            return fail(ctx, DIT_EDEVICE, "copy of text rows failed");
+        DIT_LAUNCH(ctx, launch_to_bf16(x_lat, static_cast<int64_t>(N) * lat, ctx->latb, st), "latent to bf16");
+        GemmEpi e{};
+        e.kind = EPI_F32;
+        e.out = ctx->seq + static_cast<size_t>(L) * D;
+        e.ldo = D;
+        DIT_LAUNCH(ctx, launch_gemm(ctx->latb, m->w_in, nullptr, false, N, D, lat, e, st), "img_in");
+    }
+    for (int i = 0; i < m->n_blocks; ++i) DIT_TRY(block_forward(ctx, &m->blocks[i], ctx->seq, ctx->vec, cos_t, sin_t, S));
+    {
+        Stage tm(ctx, DIT_ST_FINAL);
+        DIT_LAUNCH(ctx, launch_gemv(m->w_fmod, ctx->vec, 2 * D, D, true, ctx->fmod, st), "final modulation");
+        DIT_LAUNCH(ctx, launch_modnorm(ctx->seq + static_cast<size_t>(L) * D, N, D, ctx->fmod, ctx->fmod + D, nullptr,
+                                       false, A.final_eps, ctx->h, st),
+                   "final norm");
+        GemmEpi f{};
+        f.kind = EPI_F32;
+        f.out = ctx->vel;
+        f.ldo = lat;
+        DIT_LAUNCH(ctx, launch_gemm(ctx->h, m->w_final, nullptr, false, N, lat, D, f, st), "final linear");
+    }
+    {
+        Stage tm(ctx, DIT_ST_EULER);
+        const float dt = sigma_next - sigma;
+        DIT_LAUNCH(ctx, launch_euler(x_lat, ctx->vel, static_cast<int64_t>(N) * lat, dt, st), "euler");
+        if (vel_out && hipMemcpyAsync(vel_out, ctx->vel, static_cast<size_t>(N) * lat * 4, hipMemcpyDeviceToDevice,
+                                      st) != hipSuccess)
+            return fail(ctx, DIT_EDEVICE, "copy of the velocity failed");
+    }
+    return DIT_OK;
+}
+
+dit_status dit_euler_step(dit_ctx *ctx, float *x, const float *v, int64_t n, float sigma, float sigma_next) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (n < 0) return fail(ctx, DIT_ERANGE, "n = %lld is negative", static_cast<long long>(n));
+    if (n > 0 && (!x || !v)) return fail(ctx, DIT_EINVAL, "x or v is NULL");
+    DIT_TRY(check_ctx(ctx));
+    const float dt = sigma_next - sigma;
+    DIT_LAUNCH(ctx, launch_euler(x, v, n, dt, ctx->stream), "euler");
+    return DIT_OK;
+}
+
+dit_status dit_dequant_int8_b32(dit_ctx *ctx, const int8_t *q, const uint16_t *s, int out, int in, float *w_out) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!q || !s || !w_out) return fail(ctx, DIT_EINVAL, "q, s or w_out is NULL");
+    if (out < 1 || in < 32) return fail(ctx, DIT_ERANGE, "out %d, in %d: need out >= 1, in >= 32", out, in);
+    if (in % 32) return fail(ctx, DIT_EINVAL, "in = %d is not a multiple of 32", in);
+    DIT_TRY(check_ctx(ctx));
+    DIT_LAUNCH(ctx, launch_dequant(q, s, out, in, w_out, ctx->stream), "dequant");
+    return DIT_OK;
+}
+
+dit_status dit_debug_copy(dit_ctx *ctx, int which, void *dst, int64_t bytes) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (which < 0 || which > 7) return fail(ctx, DIT_ERANGE, "buffer %d outside 0..7", which);
+    if (bytes <= 0) return DIT_OK;
+    if (!dst) return fail(ctx, DIT_EINVAL, "dst is NULL");
+    if (static_cast<size_t>(bytes) > ctx->bytes[which])
+        return fail(ctx, DIT_ERANGE, "%lld bytes exceed buffer %d (%zu bytes)", static_cast<long long>(bytes), which,
+                    ctx->bytes[which]);
+    DIT_TRY(check_ctx(ctx));
+    const void *p[8] = {ctx->mod, ctx->h, ctx->q, ctx->k, ctx->vt, ctx->o, ctx->h2, ctx->a};
+    if (hipMemcpyAsync(dst, p[which], static_cast<size_t>(bytes), hipMemcpyDeviceToDevice, ctx->stream) != hipSuccess)
+        return fail(ctx, DIT_EDEVICE, "debug copy failed");
+    return DIT_OK;
+}
+
+}  // extern "C"

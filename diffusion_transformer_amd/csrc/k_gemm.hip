@@ -1,0 +1,376 @@
+// bf16 MFMA products of the DiT block with fused epilogues, for gfx950.
+//
+//   C[M, N] = A[M, K] * W[N, K]^T      A bf16 row-major; W bf16 or int8+scales
+//
+// Epilogues ("gizai:dit" reference: linearInto, gatedInto, prepOf, gluRows;
+// "944 -> 346 ms: optimizing FLUX.2 klein-4B on one TPU v6e chip" s.4.4 for
+// the fused head norm + rotary):
+//   EPI_F32       out[r][c] = C                              (plain fp32 store)
+//   EPI_GATE_RES  x[r][c] += gate[c] * C                     (gated residual, in place)
+//   EPI_SWIGLU    act[r][j] = bf16(silu(C[r][2j]) * C[r][2j+1])   (UP rows interleaved)
+//   EPI_QKV       per 128-wide head of Q and K: RMSNorm times the head-norm
+//                 weight, then the adjacent-pair rotation with cos/sin[r];
+//                 bf16 to q, k [H, M, 128]; V heads to vt [H, 128, ldv]
+//
+// Design (CDNA4): block tile BM x BN x 64, wave tile 64 x 128 (4 x 8 MFMA
+// 16x16x32 bf16 sub-tiles), fp32 accumulators in registers, LDS double
+// buffer with register staging of the next k-tile.  LDS rows are 128 bytes
+// (64 bf16 of K) in 16-byte chunks placed at chunk ^ ((slot >> 1) & 7), which
+// keeps both the 16-byte writes and the MFMA operand reads free of bank
+// conflicts on the 64-bank LDS.  W rows are de-interleaved into LDS (even
+// rows first, then odd rows), so each lane ends up holding output columns
+// 2p and 2p+1 in two accumulators: the rotary pairs and the SwiGLU
+// (gate, up) pairs meet in one lane without shuffles.  int8 weights are
+// dequantised (code * scale, rounded to bf16) on the way into LDS, once per
+// block.  Blocks are remapped so that each XCD works on a compact group of
+// tiles (its own L2), in groups of 8 row-tiles.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace {
+
+constexpr int BK = 64;
+constexpr int WM = 64, WN = 128;
+constexpr int TM = WM / 16, TN = WN / 16;
+
+template <int BM, int BN>
+struct Cfg {
+    static constexpr int WAVES_M = BM / WM;
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int NT = NW * 64;
+    static constexpr int A_PER_T = BM * 8 / NT;   // 16-byte chunks per thread per k-tile
+    static constexpr int B_PER_T = BN * 8 / NT;
+    static constexpr int B8_PER_T = BN * 4 / NT;  // int8: 16 codes per chunk
+    static constexpr int STAGE = (BM + BN) * 8;   // u32x4 per LDS buffer
+    static_assert(A_PER_T >= 1 && B_PER_T >= 1 && B8_PER_T >= 1, "tile too small");
+};
+
+__device__ __forceinline__ int swz(int slot) { return (slot >> 1) & 7; }
+__device__ __forceinline__ int lidx(int slot, int chunk) { return slot * 8 + (chunk ^ swz(slot)); }
+
+// W row n of the tile -> LDS slot: even rows in the first half, odd rows in
+// the second half.
+template <int BN>
+__device__ __forceinline__ int bslot(int n) { return (n & 1) * (BN / 2) + (n >> 1); }
+
+// 16 int8 codes times one scale -> 16 bf16 (two 16-byte chunks).
+__device__ __forceinline__ void dequant16(u32x4 q, float s, u32x4 &lo, u32x4 &hi) {
+    float f[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t w = q[j];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            f[4 * j + b] = static_cast<float>(static_cast<int8_t>((w >> (8 * b)) & 0xff)) * s;
+    }
+    lo = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+               pack_bf16x2(f[6], f[7])};
+    hi = u32x4{pack_bf16x2(f[8], f[9]), pack_bf16x2(f[10], f[11]), pack_bf16x2(f[12], f[13]),
+               pack_bf16x2(f[14], f[15])};
+}
+
+}  // namespace
+
+template <int BM, int BN, bool W8, int EPI>
+__global__ void __launch_bounds__((BM / 64) * (BN / 128) * 64)
+k_gemm(const uint16_t *__restrict__ A, const void *__restrict__ Wv,
+       const uint16_t *__restrict__ Ws, int M, int N, int K, GemmEpi ep) {
+    using C = Cfg<BM, BN>;
+    __shared__ u32x4 lds[2 * C::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+
+    // ---- tile mapping: XCD-compact, then grouped row-major
+    const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+    const int total = ntm * ntn;
+    int bid = blockIdx.x;
+    {
+        const int per = total / 8, rem = total % 8, xcd = bid % 8, loc = bid / 8;
+        bid = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+    }
+    constexpr int GM = 8;
+    const int group = bid / (GM * ntn), first = group * GM;
+    const int gsz = min(ntm - first, GM);
+    const int tile_m = first + (bid % (GM * ntn)) % gsz;
+    const int tile_n = (bid % (GM * ntn)) / gsz;
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+    // ---- global load assignment
+    const int a_c = tid & 7;
+    const uint16_t *a_src[C::A_PER_T];
+    int a_dst[C::A_PER_T];
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i) {
+        int r = (tid >> 3) + i * (C::NT / 8);
+        int gr = min(m0 + r, M - 1);
+        a_src[i] = A + static_cast<int64_t>(gr) * K + a_c * 8;
+        a_dst[i] = lidx(r, a_c);
+    }
+    const uint8_t *b_src[W8 ? C::B8_PER_T : C::B_PER_T];
+    const uint16_t *s_src[W8 ? C::B8_PER_T : 1];
+    int b_dst[W8 ? C::B8_PER_T : C::B_PER_T];
+    int b_dst2[W8 ? C::B8_PER_T : 1];
+    if constexpr (!W8) {
+        const uint16_t *W = static_cast<const uint16_t *>(Wv);
+#pragma unroll
+        for (int i = 0; i < C::B_PER_T; ++i) {
+            int q = (tid >> 3) + i * (C::NT / 8);
+            // rows 4a+{0,2,1,3}: the two rows a 16-lane group writes land in
+            // different halves of the 64 banks
+            int r = (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1);
+            int gr = min(n0 + r, N - 1);
+            b_src[i] = reinterpret_cast<const uint8_t *>(W + static_cast<int64_t>(gr) * K + a_c * 8);
+            b_dst[i] = BM * 8 + lidx(bslot<BN>(r), a_c);
+        }
+    } else {
+        const int8_t *W = static_cast<const int8_t *>(Wv);
+        const int c4 = tid & 3;
+#pragma unroll
+        for (int i = 0; i < C::B8_PER_T; ++i) {
+            int r = (tid >> 2) + i * (C::NT / 4);
+            int gr = min(n0 + r, N - 1);
+            b_src[i] = reinterpret_cast<const uint8_t *>(W + static_cast<int64_t>(gr) * K + c4 * 16);
+            s_src[i] = Ws + static_cast<int64_t>(gr) * (K / 32) + (c4 >> 1);
+            b_dst[i] = BM * 8 + lidx(bslot<BN>(r), 2 * c4);
+            b_dst2[i] = BM * 8 + lidx(bslot<BN>(r), 2 * c4 + 1);
+        }
+    }
+
+    u32x4 ra[C::A_PER_T];
+    u32x4 rb[W8 ? C::B8_PER_T : C::B_PER_T];
+    uint16_t rs[W8 ? C::B8_PER_T : 1];
+
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < C::A_PER_T; ++i)
+            ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + kt * BK);
+        if constexpr (!W8) {
+#pragma unroll
+            for (int i = 0; i < C::B_PER_T; ++i)
+                rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + kt * BK * 2);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::B8_PER_T; ++i) {
+                rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + kt * BK);
+                rs[i] = s_src[i][kt * 2];
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        u32x4 *L = lds + buf * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::A_PER_T; ++i) L[a_dst[i]] = ra[i];
+        if constexpr (!W8) {
+#pragma unroll
+            for (int i = 0; i < C::B_PER_T; ++i) L[b_dst[i]] = rb[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::B8_PER_T; ++i) {
+                u32x4 lo, hi;
+                dequant16(rb[i], bf16_to_f32(rs[i]), lo, hi);
+                L[b_dst[i]] = lo;
+                L[b_dst2[i]] = hi;
+            }
+        }
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // operand slots of this lane
+    int a_slot[TM], b_slot[TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) a_slot[tm] = wm * WM + tm * 16 + (lane & 15);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+        b_slot[tn] = (tn < TN / 2 ? 0 : BN / 2) + wn * (WN / 2) + (tn % (TN / 2)) * 16 + (lane & 15);
+
+    const int KT = K / BK;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) load_tile(kt + 1);
+        const u32x4 *L = lds + cur * C::STAGE;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            const int ch = ks * 4 + (lane >> 4);
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+                af[tm] = __builtin_bit_cast(bf16x8, L[lidx(a_slot[tm], ch)]);
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+                bfr[tn] = __builtin_bit_cast(bf16x8, L[BM * 8 + lidx(b_slot[tn], ch)]);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
+        }
+        if (kt + 1 < KT) store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue.  Lane holds rows m0 + wm*64 + tm*16 + 4*(lane>>4) + r and
+    // output pairs P = (n0 + wn*128)/2 + tp*16 + (lane & 15): column 2P in
+    // acc[tm][tp][r], column 2P+1 in acc[tm][tp+4][r].
+    const int col0 = n0 + wn * WN;
+    if (col0 >= N) return;
+    const int rbase = m0 + wm * WM + 4 * (lane >> 4);
+    const int pl = lane & 15;
+
+    if constexpr (EPI == EPI_F32 || EPI == EPI_GATE_RES) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rbase + tm * 16 + r;
+                if (row >= M) continue;
+#pragma unroll
+                for (int tp = 0; tp < TN / 2; ++tp) {
+                    const int c = col0 + 2 * (tp * 16 + pl);
+                    if (c >= N) continue;
+                    float2 *dst = reinterpret_cast<float2 *>(ep.out + static_cast<int64_t>(row) * ep.ldo + c);
+                    float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
+                    if constexpr (EPI == EPI_F32) {
+                        *dst = make_float2(e, o);
+                    } else {
+                        float2 g = *reinterpret_cast<const float2 *>(ep.gate + c);
+                        float2 x = *dst;
+                        x.x += g.x * e;
+                        x.y += g.y * o;
+                        *dst = x;
+                    }
+                }
+            }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        const int half = N / 2;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rbase + tm * 16 + r;
+                if (row >= M) continue;
+#pragma unroll
+                for (int tp = 0; tp < TN / 2; ++tp) {
+                    const int p = col0 / 2 + tp * 16 + pl;
+                    if (2 * p >= N) continue;
+                    float g = acc[tm][tp][r], u = acc[tm][tp + TN / 2][r];
+                    ep.act[static_cast<int64_t>(row) * half + p] = f32_to_bf16(silu_f(g) * u);
+                }
+            }
+    } else if constexpr (EPI == EPI_QKV) {
+        const int H = ep.heads;
+        const int hb = col0 / 128;
+        const int region = hb / H, head = hb % H;
+        if (region < 2) {
+            const float *nw = region == 0 ? ep.qn : ep.kn;
+            uint16_t *dst = region == 0 ? ep.q : ep.k;
+            float we[TN / 2], wo[TN / 2];
+#pragma unroll
+            for (int tp = 0; tp < TN / 2; ++tp) {
+                const int p = tp * 16 + pl;
+                we[tp] = nw[2 * p];
+                wo[tp] = nw[2 * p + 1];
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int tp = 0; tp < TN / 2; ++tp) {
+                        float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
+                        ss += e * e + o * o;
+                    }
+                    // sum over the 16 lanes that share this row (lane bits 0..3)
+                    ss += __shfl_xor(ss, 1, 64);
+                    ss += __shfl_xor(ss, 2, 64);
+                    ss += __shfl_xor(ss, 4, 64);
+                    ss += __shfl_xor(ss, 8, 64);
+                    const float rstd = rsqrtf(ss * (1.0f / 128.0f) + ep.qk_eps);
+                    const int row = rbase + tm * 16 + r;
+                    const int rr = min(row, M - 1);
+#pragma unroll
+                    for (int tp = 0; tp < TN / 2; ++tp) {
+                        const int p = tp * 16 + pl;
+                        const float c = ep.cos[static_cast<int64_t>(rr) * 64 + p];
+                        const float s = ep.sin[static_cast<int64_t>(rr) * 64 + p];
+                        const float a = acc[tm][tp][r] * rstd * we[tp];
+                        const float b = acc[tm][tp + TN / 2][r] * rstd * wo[tp];
+                        if (row < M)
+                            *reinterpret_cast<uint32_t *>(
+                                dst + (static_cast<int64_t>(head) * M + row) * 128 + 2 * p) =
+                                pack_bf16x2(a * c - b * s, a * s + b * c);
+                    }
+                }
+        } else {
+            // V: rows rbase + tm*16 + 0..3 are consecutive -> 4 bf16 along vt's row
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const int row0 = rbase + tm * 16;
+                if (row0 >= ep.ldv) continue;
+#pragma unroll
+                for (int tp = 0; tp < TN / 2; ++tp) {
+                    const int p = tp * 16 + pl;
+                    uint16_t *d0 = ep.vt + (static_cast<int64_t>(head) * 128 + 2 * p) * ep.ldv + row0;
+                    uint16_t *d1 = d0 + ep.ldv;
+                    const f32x4 e = acc[tm][tp], o = acc[tm][tp + TN / 2];
+                    *reinterpret_cast<u32x2 *>(d0) = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
+                    *reinterpret_cast<u32x2 *>(d1) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, bool W8>
+static hipError_t launch_cfg(const uint16_t *A, const void *W, const uint16_t *Ws, int M, int N, int K,
+                             const GemmEpi &ep, hipStream_t st) {
+    using C = Cfg<BM, BN>;
+    const int grid = static_cast<int>(cdiv(M, BM) * cdiv(N, BN));
+    switch (ep.kind) {
+        case EPI_F32:
+            k_gemm<BM, BN, W8, EPI_F32><<<grid, C::NT, 0, st>>>(A, W, Ws, M, N, K, ep);
+            break;
+        case EPI_GATE_RES:
+            k_gemm<BM, BN, W8, EPI_GATE_RES><<<grid, C::NT, 0, st>>>(A, W, Ws, M, N, K, ep);
+            break;
+        case EPI_SWIGLU:
+            k_gemm<BM, BN, W8, EPI_SWIGLU><<<grid, C::NT, 0, st>>>(A, W, Ws, M, N, K, ep);
+            break;
+        case EPI_QKV:
+            k_gemm<BM, BN, W8, EPI_QKV><<<grid, C::NT, 0, st>>>(A, W, Ws, M, N, K, ep);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Ws, bool w8, int M, int N,
+                       int K, const GemmEpi &ep, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    // Large problems: 256x256 tiles (8 waves).  Small ones: 128x128 (2 waves)
+    // so the grid still spreads over the chip.
+    const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
+    if (big_tiles >= 128) {
+        return w8 ? launch_cfg<256, 256, true>(A, W, Ws, M, N, K, ep, st)
+                  : launch_cfg<256, 256, false>(A, W, Ws, M, N, K, ep, st);
+    }
+    return w8 ? launch_cfg<128, 128, true>(A, W, Ws, M, N, K, ep, st)
+              : launch_cfg<128, 128, false>(A, W, Ws, M, N, K, ep, st);
+}
+
+}  // namespace dit

@@ -1,0 +1,256 @@
+// Small HBM- or launch-bound kernels of the DiT path: positions and rotary
+// tables, the timestep sinusoid, the modulation / time-MLP GEMV, the
+// modulated norm, the Euler update, int8 dequantisation and fp32->bf16.
+//
+// Sources: "Host contract -- RGBA-Image-2.1-Turbo" s.4 (positions, rotary
+// tables), s.6 (Euler update, fp32); "gizai:dit" reference: sinusoids,
+// Modulation, normedInto; s.1 of the host contract for the int8 format.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+// ------------------------------------------------------------------ positions
+// Text token i -> (i, i, i); image token y*w + x -> (L, y - (h - h/2),
+// x - (w - w/2)) (host contract s.4; the grid is centred on zero).
+__global__ void k_positions(int L, int h, int w, int32_t *pos) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    int S = L + h * w;
+    if (i >= S) return;
+    int a, b, c;
+    if (i < L) {
+        a = b = c = i;
+    } else {
+        int t = i - L, y = t / w, x = t - y * w;
+        a = L;
+        b = y - (h - h / 2);
+        c = x - (w - w / 2);
+    }
+    pos[3 * i + 0] = a;
+    pos[3 * i + 1] = b;
+    pos[3 * i + 2] = c;
+}
+
+hipError_t launch_positions(int L, int h, int w, int32_t *pos, hipStream_t st) {
+    int S = L + h * w;
+    k_positions<<<(S + 255) / 256, 256, 0, st>>>(L, h, w, pos);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- rotary tables
+// One thread per (token, pair).  Pair p belongs to axis 0 for p < a0/2, to
+// axis 1 for the next a1/2, then axis 2.  The angle pos * theta^(-2j/d) and
+// its cos/sin are computed in fp64 and rounded once to fp32.
+__global__ void k_rope_tables(const int32_t *pos, int S, int a0, int a1, int a2, double theta,
+                              float *cs, float *sn) {
+    int P = (a0 + a1 + a2) / 2;
+    int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= S * P) return;
+    int r = idx / P, p = idx - r * P;
+    int axis, j, d;
+    if (p < a0 / 2) {
+        axis = 0; j = p; d = a0;
+    } else if (p < (a0 + a1) / 2) {
+        axis = 1; j = p - a0 / 2; d = a1;
+    } else {
+        axis = 2; j = p - (a0 + a1) / 2; d = a2;
+    }
+    double inv = 1.0 / pow(theta, static_cast<double>(2 * j) / static_cast<double>(d));
+    double ang = static_cast<double>(pos[3 * r + axis]) * inv;
+    cs[idx] = static_cast<float>(cos(ang));
+    sn[idx] = static_cast<float>(sin(ang));
+}
+
+hipError_t launch_rope_tables(const int32_t *pos, int S, int a0, int a1, int a2, float theta,
+                              float *cos_t, float *sin_t, hipStream_t st) {
+    int P = (a0 + a1 + a2) / 2;
+    int64_t n = static_cast<int64_t>(S) * P;
+    k_rope_tables<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(pos, S, a0, a1, a2,
+                                                                          theta, cos_t, sin_t);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ time embedding
+// [cos | sin] of (1000 t) * 10000^(-i/(dim/2)) ("gizai:dit" sinusoids), taken
+// in fp64 and stored fp32.
+__global__ void k_time_embedding(float t, int dim, float *temb) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    int half = dim / 2;
+    if (i >= dim) return;
+    int f = i < half ? i : i - half;
+    double freq = pow(10000.0, -static_cast<double>(f) / static_cast<double>(half));
+    double ang = 1000.0 * static_cast<double>(t) * freq;
+    temb[i] = static_cast<float>(i < half ? cos(ang) : sin(ang));
+}
+
+hipError_t launch_time_embedding(float t, int dim, float *temb, hipStream_t st) {
+    k_time_embedding<<<(dim + 255) / 256, 256, 0, st>>>(t, dim, temb);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------- Euler
+// x + dt * v in fp32 with the product and the sum each rounded (no fused
+// multiply-add): the host contract writes the update as plain fp32 ops.
+__global__ void k_euler(float *__restrict__ x, const float *__restrict__ v, int64_t n, float dt) {
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) x[i] = __fadd_rn(x[i], __fmul_rn(dt, v[i]));
+}
+
+hipError_t launch_euler(float *x, const float *v, int64_t n, float dt, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    k_euler<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(x, v, n, dt);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- dequant
+// w[o][k] = q[o][k] * s[o][k/32]; exact in fp32 (|q| <= 127, bf16 scale).
+__global__ void k_dequant(const int8_t *q, const uint16_t *s, int out, int in, float *w) {
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    int64_t n = static_cast<int64_t>(out) * in;
+    if (i >= n) return;
+    int64_t o = i / in, k = i - o * in;
+    w[i] = static_cast<float>(q[i]) * bf16_to_f32(s[o * (in / 32) + k / 32]);
+}
+
+hipError_t launch_dequant(const int8_t *q, const uint16_t *s, int out, int in, float *w,
+                          hipStream_t st) {
+    int64_t n = static_cast<int64_t>(out) * in;
+    if (n == 0) return hipSuccess;
+    k_dequant<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(q, s, out, in, w);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- to bf16
+__global__ void k_to_bf16(const float *x, int64_t n, uint16_t *y) {
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = f32_to_bf16(x[i]);
+}
+
+hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *y, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    k_to_bf16<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(x, n, y);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------- GEMV
+// One wave per output row, 16-byte loads of W (8 bf16 per lane per step),
+// the input vector staged once per block in LDS (with silu applied).  The
+// weight is read exactly once: the kernel is HBM-bound.
+constexpr int kGemvThreads = 256;
+constexpr int kGemvMaxI = 4096;
+
+__global__ void __launch_bounds__(kGemvThreads)
+k_gemv(const uint16_t *__restrict__ W, const float *__restrict__ x, int O, int I, int silu_in,
+       float *__restrict__ y) {
+    __shared__ float xs[kGemvMaxI];
+    for (int i = threadIdx.x; i < I; i += kGemvThreads) {
+        float v = x[i];
+        xs[i] = silu_in ? silu_f(v) : v;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int nchunk = I / 8;
+    for (int o = blockIdx.x * 4 + wv; o < O; o += gridDim.x * 4) {
+        const u32x4 *row = reinterpret_cast<const u32x4 *>(W + static_cast<int64_t>(o) * I);
+        float acc = 0.f;
+        for (int c = lane; c < nchunk; c += 64) {
+            u32x4 w = __builtin_nontemporal_load(row + c);
+            const float *xp = xs + c * 8;
+            acc += bf16lo_to_f32(w.x) * xp[0] + bf16hi_to_f32(w.x) * xp[1];
+            acc += bf16lo_to_f32(w.y) * xp[2] + bf16hi_to_f32(w.y) * xp[3];
+            acc += bf16lo_to_f32(w.z) * xp[4] + bf16hi_to_f32(w.z) * xp[5];
+            acc += bf16lo_to_f32(w.w) * xp[6] + bf16hi_to_f32(w.w) * xp[7];
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) y[o] = acc;
+    }
+}
+
+hipError_t launch_gemv(const uint16_t *W, const float *x, int O, int I, bool silu_in, float *y,
+                       hipStream_t st) {
+    int blocks = (O + 3) / 4;
+    if (blocks > 2048) blocks = 2048;
+    k_gemv<<<blocks, kGemvThreads, 0, st>>>(W, x, O, I, silu_in ? 1 : 0, y);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ modulated norm
+// One row per block of 256 threads; each thread keeps up to 4 float4 of the
+// row in registers (D <= 4096).  Statistics in fp32 with a two-pass
+// variance over the register-resident row; output bf16.
+constexpr int kNormThreads = 256;
+
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wv] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormThreads / 64; ++i) t += red[i];
+    return t;
+}
+
+__global__ void __launch_bounds__(kNormThreads)
+k_modnorm(const float *__restrict__ x, int D, const float *__restrict__ shift,
+          const float *__restrict__ scale, const float *__restrict__ nw, int rms, float eps,
+          uint16_t *__restrict__ out) {
+    __shared__ float red[kNormThreads / 64];
+    const int64_t r = blockIdx.x;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + r * D);
+    const int n4 = D / 4;
+    float4 v[4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        v[i] = c < n4 ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float invD = 1.0f / static_cast<float>(D);
+    float mu = 0.f, rstd;
+    if (!rms) {
+        mu = block_sum(s, red) * invD;
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int c = threadIdx.x + i * kNormThreads;
+            if (c < n4) {
+                float a = v[i].x - mu, b = v[i].y - mu, cc = v[i].z - mu, d = v[i].w - mu;
+                q += (a * a + b * b) + (cc * cc + d * d);
+            }
+        }
+        rstd = rsqrtf(block_sum(q, red) * invD + eps);
+    } else {
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
+        rstd = rsqrtf(block_sum(q, red) * invD + eps);
+    }
+    u32x2 *orow = reinterpret_cast<u32x2 *>(out + r * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        if (c >= n4) continue;
+        float4 sh = reinterpret_cast<const float4 *>(shift)[c];
+        float4 sc = reinterpret_cast<const float4 *>(scale)[c];
+        float4 w = rms ? reinterpret_cast<const float4 *>(nw)[c] : make_float4(1.f, 1.f, 1.f, 1.f);
+        float a = (v[i].x - mu) * rstd * w.x * (1.f + sc.x) + sh.x;
+        float b = (v[i].y - mu) * rstd * w.y * (1.f + sc.y) + sh.y;
+        float cc = (v[i].z - mu) * rstd * w.z * (1.f + sc.z) + sh.z;
+        float d = (v[i].w - mu) * rstd * w.w * (1.f + sc.w) + sh.w;
+        u32x2 o2 = {pack_bf16x2(a, b), pack_bf16x2(cc, d)};
+        orow[c] = o2;
+    }
+}
+
+hipError_t launch_modnorm(const float *x, int rows, int D, const float *shift, const float *scale,
+                          const float *norm_w, bool rms, float eps, uint16_t *out, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    k_modnorm<<<rows, kNormThreads, 0, st>>>(x, D, shift, scale, norm_w, rms ? 1 : 0, eps, out);
+    return hipGetLastError();
+}
+
+}  // namespace dit

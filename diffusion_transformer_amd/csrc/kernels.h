@@ -1,0 +1,57 @@
+// Internal launch interface between the C ABI layer (dit_api.cpp) and the
+// HIP kernels.  Every launcher only enqueues on `st` and returns the launch
+// status; shapes have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+// ---- small kernels (k_misc.hip) ------------------------------------------
+hipError_t launch_positions(int L, int h, int w, int32_t *pos, hipStream_t st);
+hipError_t launch_rope_tables(const int32_t *pos, int S, int a0, int a1, int a2, float theta,
+                              float *cos, float *sin, hipStream_t st);
+hipError_t launch_time_embedding(float t, int dim, float *temb, hipStream_t st);
+hipError_t launch_euler(float *x, const float *v, int64_t n, float dt, hipStream_t st);
+hipError_t launch_dequant(const int8_t *q, const uint16_t *s, int out, int in, float *w,
+                          hipStream_t st);
+hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *y, hipStream_t st);
+
+// y[o] = sum_i W[o, i] * f(x[i]); f = silu when silu_in, else identity.
+// W bf16 [O, I]; x, y fp32.  I a multiple of 8.
+hipError_t launch_gemv(const uint16_t *W, const float *x, int O, int I, bool silu_in, float *y,
+                       hipStream_t st);
+
+// out[r] = bf16(norm(x[r]) * (1 + scale) + shift), r < rows; D <= 4096,
+// D a multiple of 4.  rms: RMSNorm times norm_w; else LayerNorm.
+hipError_t launch_modnorm(const float *x, int rows, int D, const float *shift, const float *scale,
+                          const float *norm_w, bool rms, float eps, uint16_t *out, hipStream_t st);
+
+// ---- products (k_gemm.hip) -------------------------------------------------
+enum EpiKind { EPI_F32 = 0, EPI_GATE_RES = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+
+struct GemmEpi {
+    int kind;
+    float *out;            // EPI_F32: out [M, ldo] fp32; EPI_GATE_RES: x [M, ldo] += gate * acc
+    int ldo;
+    const float *gate;     // EPI_GATE_RES: [N]
+    uint16_t *act;         // EPI_SWIGLU: bf16 [M, N/2]
+    // EPI_QKV
+    uint16_t *q, *k, *vt;  // q, k [H, M, 128]; vt [H, 128, ldv]
+    int heads, ldv;
+    const float *qn, *kn;  // [128] head-norm weights
+    const float *cos, *sin;// [M, 64]
+    float qk_eps;
+};
+
+// C = A[M,K] * W[N,K]^T, A bf16; W bf16 (w8 = false) or int8 with bf16
+// scales [N, K/32] (w8 = true); then the epilogue.  K % 64 == 0, N % 64 == 0.
+hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Wscale, bool w8, int M,
+                       int N, int K, const GemmEpi &epi, hipStream_t st);
+
+// ---- attention (k_attn.hip) ------------------------------------------------
+hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int heads,
+                            int S, int ldv, uint16_t *o, int ldo, hipStream_t st);
+
+}  // namespace dit

@@ -20,27 +20,37 @@ Weights ~ N(0, 0.02); activations and text features ~ N(0, 1); norm weights
 
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 
 import numpy as np
 
 
+def _round_inplace(u: np.ndarray) -> np.ndarray:
+    """u: uint32 view of float32 values; rounds them in place to bf16
+    (round to nearest, ties to even; finite inputs) and returns u."""
+    t = u >> 16
+    t &= 1
+    t += np.uint32(0x7FFF)
+    u += t
+    u &= np.uint32(0xFFFF0000)
+    return u
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """float32 array of the bf16-rounded values of a (a copy)."""
+    u = np.array(a, dtype=np.float32, copy=True).view(np.uint32)
+    return _round_inplace(u).view(np.float32)
+
+
 def bf16_bits(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (round to nearest, ties to even) and
-    return the 16-bit patterns (uint16).  Inputs are finite draws."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
-    lsb = (u >> 16) & 1
-    return ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+    """The 16-bit patterns (uint16) of the bf16-rounded values of a."""
+    return (bf16_round(a).view(np.uint32) >> 16).astype(np.uint16)
 
 
 def bf16_values(bits: np.ndarray) -> np.ndarray:
     """float32 values of bf16 bit patterns."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
-
-
-def bf16_round(a: np.ndarray) -> np.ndarray:
-    """float32 array of the bf16-rounded values of a."""
-    return bf16_values(bf16_bits(a))
 
 
 @dataclass(frozen=True)
@@ -79,8 +89,41 @@ SHAPES = {
 }
 
 
+_CHUNK = 1 << 22
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1)))
+    return _POOL
+
+
 def _normal(rng, shape, std):
-    return bf16_round(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+    """bf16-rounded N(0, std^2) draws.  Large arrays are filled in chunks of
+    4 Mi values, chunk i from its own generator seeded with (s, i) where s is
+    drawn from `rng`, so the result is the same whatever the thread count."""
+    a = np.empty(shape, dtype=np.float32)
+    flat = a.reshape(-1)
+    s = int(rng.integers(0, 2 ** 62))
+    n = flat.size
+
+    def fill(i):
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        g = np.random.default_rng([s, i])
+        part = flat[lo:hi]
+        g.standard_normal(hi - lo, dtype=np.float32, out=part)
+        part *= np.float32(std)
+        _round_inplace(part.view(np.uint32))
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        fill(0) if n else None
+    else:
+        list(_pool().map(fill, range(nchunks)))
+    return a
 
 
 def int8_weight(rng, out: int, inn: int):
@@ -162,6 +205,12 @@ def model_case(name: str = "dit32", blocks=None, seed=None, hidden=None, heads=N
     )
     blocks = [block_weights(rng, sh, int8=False) for _ in range(sh.blocks)]
     return dict(shape=sh, x_lat=x_lat, ctx=ctx, top=top, blocks=blocks)
+
+
+def normal(shape, seed: int, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
+    """float32 draws N(mean, std^2) from a generator seeded with `seed`."""
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(std) + np.float32(mean)).astype(np.float32)
 
 
 def rows_sample(S: int, count: int, L: int = 0, seed: int = 123) -> np.ndarray:

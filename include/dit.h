@@ -1,0 +1,277 @@
+/*
+ * dit.h -- C ABI of libdit, the gfx950 (MI355X) hot path of an AdaLN
+ * diffusion-transformer (DiT) block and its few-step Euler denoise loop.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [HC] "Host contract -- RGBA-Image-2.1-Turbo (Core AI port of
+ *        Qwen-Image-2.1-Turbo)": s.1 The graphs, s.4 Sequence layout and
+ *        RoPE, s.6 Sampler.
+ *   [K4] "944 -> 346 ms: optimizing FLUX.2 klein-4B on one TPU v6e chip":
+ *        s.2 cast points, s.4.1 device-resident weights, s.4.3 flash
+ *        attention, s.4.4 fused qk-prep.
+ *   [GZ] "gizai:dit" module reference: Arch, Block, Modulation, Sequence,
+ *        Work, gluRows, gatedInto, normedInto, prepOf, sinusoids,
+ *        Block.forward, HEAD, CHUNK.
+ *
+ * Conventions (all entry points):
+ *  - Every tensor argument is a DEVICE pointer to caller-owned memory on the
+ *    context's device, row-major and densely packed, unless stated otherwise.
+ *    The library never frees caller memory and keeps no pointer after a call
+ *    returns ([K4] s.4.1: weights stay resident; nothing is copied from the
+ *    host inside a call).
+ *  - bf16 tensors are passed as `const uint16_t *` holding bf16 bit patterns.
+ *  - Every call only enqueues work on the context's HIP stream and returns;
+ *    there is no host synchronisation inside a call.  Results are visible
+ *    after the caller synchronises that stream.  Device faults surface at the
+ *    caller's next synchronisation.
+ *  - Arguments are validated on the host BEFORE any device work; a non-OK
+ *    status means nothing was enqueued, and dit_last_error() describes it.
+ *  - One context per stream; a context is not safe to use from two threads
+ *    at once.  Calls on one context share its workspace, so they must be
+ *    ordered on its stream (they are, when issued from one thread).
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dit_ctx dit_ctx;
+
+typedef enum {
+    DIT_OK = 0,
+    DIT_EINVAL = -1,        /* null pointer, inconsistent shape, bad enum */
+    DIT_ERANGE = -2,        /* a size outside its supported range */
+    DIT_ENOMEM = -3,        /* workspace allocation failed */
+    DIT_EDEVICE = -4,       /* no usable gfx950 device, or a launch failed */
+    DIT_EUNSUPPORTED = -5   /* valid but not implemented (e.g. head_dim != 128) */
+} dit_status;
+
+/* Weight storage of the four block linears ([HC] s.1: bf16, or int8 with
+ * one bf16 scale per block of 32 along the input axis). */
+typedef enum { DIT_W_BF16 = 0, DIT_W_INT8_B32 = 1 } dit_wtype;
+
+/* Norm before attention and MLP: LayerNorm without affine, or RMSNorm times
+ * a per-feature weight ([GZ] normedInto; Block.parallel's modulated LayerNorm). */
+typedef enum { DIT_NORM_LAYER = 0, DIT_NORM_RMS = 1 } dit_norm;
+
+/* Architecture ([GZ] Arch).  Supported: head_dim == 128 ([GZ] HEAD),
+ * hidden == heads * head_dim, hidden and ffn multiples of 256,
+ * axes[0] + axes[1] + axes[2] == head_dim with every axis even
+ * ([HC] s.4: 16, 56, 56), time_dim even, latent and text_dim multiples of 64. */
+typedef struct {
+    int32_t hidden;         /* D, e.g. 3072 */
+    int32_t heads;          /* H, e.g. 24 */
+    int32_t head_dim;       /* 128 */
+    int32_t ffn;            /* F, SwiGLU width, e.g. 12288 */
+    int32_t axes[3];        /* rotary axis widths (frame, height, width) */
+    float eps;              /* modulated-norm epsilon */
+    float qk_eps;           /* head RMSNorm epsilon */
+    float final_eps;        /* final-layer norm epsilon */
+    float rope_theta;       /* 10000 */
+    int32_t norm;           /* dit_norm */
+    int32_t time_dim;       /* sinusoid width, 256 */
+    int32_t latent;         /* latent channels per image token, 64 */
+    int32_t text_dim;       /* text feature width, 4096 */
+} dit_arch;
+
+/* One block's weights ([GZ] Block; linears stored [out, in]).
+ *   w[0] QKV  [3*H*hd, D]  rows: all queries, all keys, all values; head j
+ *                          of each is rows j*hd .. (j+1)*hd-1
+ *   w[1] OUT  [D, H*hd]
+ *   w[2] UP   [2F, D]      gate j at row 2j, up j at row 2j+1 ([GZ] gluRows)
+ *   w[3] DOWN [D, F]
+ * wtype DIT_W_BF16: w[i] are bf16; scale[i] must be NULL.
+ * wtype DIT_W_INT8_B32: w[i] are int8 [out, in]; scale[i] are bf16
+ *   [out, in/32]; weight = code * scale[o][k/32].
+ * norm_w: fp32.  [0] NORM1, [1] NORM2 ([D], required for DIT_NORM_RMS,
+ *   ignored for DIT_NORM_LAYER), [2] Q_NORM, [3] K_NORM ([hd], required).
+ * w_mod: bf16 [6D, D]; its output rows are shift, scale, gate of the
+ *   attention, then of the MLP ([GZ] Modulation). */
+typedef struct {
+    int32_t wtype;
+    const void *w[4];
+    const uint16_t *scale[4];
+    const float *norm_w[4];
+    const uint16_t *w_mod;
+} dit_block;
+
+/* The whole DiT ([HC] s.1 DiT graph).  All bf16 [out, in]:
+ *   w_t1 [D, time_dim], w_t2 [D, D]   time MLP (silu between)
+ *   w_in [D, latent]                  image tokens in
+ *   w_txt [D, text_dim]               text features in
+ *   w_fmod [2D, D]                    final (shift, scale)
+ *   w_final [latent, D]               final linear
+ * blocks: HOST array of n_blocks descriptors (device weight pointers). */
+typedef struct {
+    int32_t n_blocks;
+    const dit_block *blocks;
+    const uint16_t *w_t1, *w_t2, *w_in, *w_txt, *w_fmod, *w_final;
+} dit_model;
+
+/* Create a context on `device` whose calls enqueue on `stream` (a
+ * hipStream_t; NULL = the device's null stream).  The workspace ([GZ] Work)
+ * is allocated here once, sized for sequences of up to `max_rows` rows
+ * (L + N), and reused by every call.  Errors: DIT_EINVAL (null out, bad
+ * arch), DIT_EUNSUPPORTED (head_dim != 128 and the like), DIT_ERANGE
+ * (max_rows outside 1..65536), DIT_EDEVICE (no such device, or it is not
+ * gfx950), DIT_ENOMEM.  On error *out is NULL and the message is available
+ * from dit_last_error(NULL). */
+dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arch *arch,
+                          int max_rows);
+
+/* Free the workspace and the context.  NULL is a no-op.  The caller must
+ * synchronise the stream first if calls are still in flight. */
+void dit_ctx_destroy(dit_ctx *ctx);
+
+/* Change the stream later calls enqueue on. */
+dit_status dit_ctx_set_stream(dit_ctx *ctx, void *stream);
+
+/* Text of the last non-OK status on this context (or of the last failed
+ * dit_ctx_create / null-context call when ctx is NULL).  Never NULL. */
+const char *dit_last_error(const dit_ctx *ctx);
+
+/* Library version string. */
+const char *dit_version(void);
+
+/* [HC] s.4 positions: pos [L + h*w, 3] int32 device.  Text token i ->
+ * (i, i, i); image token y*w + x -> (L, y - (h - h/2), x - (w - w/2)).
+ * Requires 0 <= L, 1 <= h, 1 <= w, L + h*w <= max_rows. */
+dit_status dit_positions(dit_ctx *ctx, int L, int h, int w, int32_t *pos);
+
+/* [HC] s.4 rotary tables from positions pos [S, 3] int32: for each axis a
+ * of width d_a, angles pos[:, a] * theta^(-2j/d_a), j < d_a/2; a token's
+ * row is the three axes' rows concatenated (head_dim/2 values).
+ * cos, sin: fp32 [S, head_dim/2] outputs (angle and cos/sin taken in fp64,
+ * rounded once to fp32).  Requires 1 <= S <= max_rows. */
+dit_status dit_rope_tables(dit_ctx *ctx, const int32_t *pos, int S, float *cos, float *sin);
+
+/* Conditioning vector ([GZ] sinusoids + the time MLP): vec = w_t2 *
+ * silu(w_t1 * [cos | sin](1000 t * 10000^(-i/(time_dim/2)))).
+ * w_t1 bf16 [D, time_dim], w_t2 bf16 [D, D]; vec fp32 [D] output. */
+dit_status dit_time_vector(dit_ctx *ctx, const uint16_t *w_t1, const uint16_t *w_t2, float t,
+                           float *vec);
+
+/* Modulation GEMV ([GZ] Modulation): mod = w_mod * silu(vec), w_mod bf16
+ * [chunks*D, D], vec fp32 [D], mod fp32 [chunks*D].  chunks in 1..6. */
+dit_status dit_modulation(dit_ctx *ctx, const uint16_t *w_mod, int chunks, const float *vec,
+                          float *mod);
+
+/* Modulated norm ([GZ] normedInto): out[r] = bf16(norm(x[r]) * (1 + scale)
+ * + shift) for r < rows; norm is the arch's (norm_w fp32 [D] for RMS, may
+ * be NULL for LayerNorm); x fp32 [rows, D]; shift, scale fp32 [D];
+ * out bf16 [rows, D]; eps as given. */
+dit_status dit_modulated_norm(dit_ctx *ctx, const float *x, int rows, const float *shift,
+                              const float *scale, const float *norm_w, float eps,
+                              uint16_t *out);
+
+/* Plain product out = a * W^T ([GZ] linearInto): a bf16 [M, K]; W bf16
+ * [N, K] (wtype DIT_W_BF16, scale NULL) or int8 [N, K] with bf16 scales
+ * [N, K/32] (DIT_W_INT8_B32); out fp32 [M, N].  K a multiple of 64,
+ * N a multiple of 64, 1 <= M <= max_rows. */
+dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint16_t *scale,
+                      int wtype, int M, int N, int K, float *out);
+
+/* Joint attention ([K4] s.4.3): for each head h, o[:, h*128:(h+1)*128] =
+ * bf16(softmax(q_h k_h^T / sqrt(128)) v_h), no mask.  q, k bf16
+ * [heads, S, 128]; vt bf16 [heads, 128, Sp] with Sp = S rounded up to a
+ * multiple of 64 (values transposed, feature-major; columns S..Sp-1 are
+ * never used and may hold anything); o bf16 [S, heads*128].
+ * 1 <= S <= max_rows, 1 <= heads <= arch heads. */
+dit_status dit_attention(dit_ctx *ctx, const uint16_t *q, const uint16_t *k, const uint16_t *vt,
+                         int heads, int S, uint16_t *o);
+
+/* One AdaLN block, in place ([GZ] Block.forward): with (shift_a, scale_a,
+ * gate_a, shift_m, scale_m, gate_m) = w_mod * silu(vec),
+ *   x += gate_a * OUT(attention(prep(QKV(norm1(x)*(1+scale_a)+shift_a))))
+ *   x += gate_m * DOWN(swiglu(UP(norm2(x)*(1+scale_m)+shift_m)))
+ * where prep is the per-head RMSNorm times Q_NORM/K_NORM followed by the
+ * adjacent-pair rotation with cos/sin ([GZ] prepOf).  x fp32 [L+N, D]
+ * (text rows first), vec fp32 [D], cos/sin fp32 [L+N, 64] (from
+ * dit_rope_tables).  Requires 0 <= L <= 512, 1 <= N <= 4096 (the DiT graph
+ * axes of [HC] s.1, extended down to 0 and 1 for small tests),
+ * L + N <= max_rows.  Operands of the products are bf16, accumulation and
+ * the residual stream fp32 ([K4] s.2 cast points). */
+dit_status dit_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const float *vec,
+                             const float *cos, const float *sin, int L, int N);
+
+/* Text rows of the sequence, step-invariant ([K4] Appendix B, D2 hoists
+ * them out of the Euler loop): txt fp32 [L, D] = ctx_feats * w_txt^T with
+ * ctx_feats fp32 [L, text_dim] (taken to bf16 for the product). */
+dit_status dit_prologue(dit_ctx *ctx, const dit_model *m, const float *ctx_feats, int L,
+                        float *txt);
+
+/* One denoise step ([HC] s.6): t = sigma; vel = DiT(x_lat, txt, t) (image
+ * rows x_lat*w_in^T after the text rows txt, every block, the final
+ * modulated LayerNorm of the image rows with (shift, scale) = w_fmod *
+ * silu(vec), then w_final); x_lat += (sigma_next - sigma) * vel in fp32.
+ * x_lat fp32 [N, latent] in place; txt fp32 [L, D] from dit_prologue;
+ * cos/sin fp32 [L+N, 64]; vel_out fp32 [N, latent] or NULL. */
+dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, const float *txt,
+                            const float *cos, const float *sin, int L, int N, float sigma,
+                            float sigma_next, float *vel_out);
+
+/* [HC] s.6 Euler update, fp32, unfused: x[i] = x[i] + (float)(sigma_next -
+ * sigma) * v[i] (difference, product and sum each rounded to fp32).
+ * x, v fp32 [n]; n >= 0 (0 is a no-op). */
+dit_status dit_euler_step(dit_ctx *ctx, float *x, const float *v, int64_t n, float sigma,
+                          float sigma_next);
+
+/* [HC] s.1 int8lin dequantisation, exposed for tests: w_out fp32 [out, in]
+ * = q[o][k] * s[o][k/32] (exact in fp32).  q int8 [out, in], s bf16
+ * [out, in/32]; in a multiple of 32. */
+dit_status dit_dequant_int8_b32(dit_ctx *ctx, const int8_t *q, const uint16_t *s, int out,
+                                int in, float *w_out);
+
+/* Launch stages of the block forward, denoise step and prologue, for
+ * per-kernel timing (dit_timing_read). */
+typedef enum {
+    DIT_ST_MOD = 0,     /* modulation GEMV */
+    DIT_ST_NORM1 = 1,   /* modulated norm before attention */
+    DIT_ST_QKV = 2,     /* QKV product + head norm + rotary epilogue */
+    DIT_ST_ATTN = 3,    /* joint attention */
+    DIT_ST_OUT = 4,     /* output product + gated residual */
+    DIT_ST_NORM2 = 5,   /* modulated norm before the MLP */
+    DIT_ST_UP = 6,      /* UP product + SwiGLU epilogue */
+    DIT_ST_DOWN = 7,    /* DOWN product + gated residual */
+    DIT_ST_TIME = 8,    /* sinusoid + time MLP */
+    DIT_ST_IMG_IN = 9,  /* latent -> bf16, image-in product, text-row copy */
+    DIT_ST_FINAL = 10,  /* final modulation, norm and product */
+    DIT_ST_EULER = 11,  /* Euler update (+ velocity copy) */
+    DIT_ST_TXT_IN = 12, /* prologue: text features -> bf16, text-in product */
+    DIT_NSTAGES = 13
+} dit_stage;
+
+/* Per-stage timing, a measurement aid ([K4] s.3: every op of the busy time
+ * is accounted to a bucket).  While enabled (on != 0), each stage above that
+ * a call enqueues is bracketed by a pair of HIP events on the context's
+ * stream.  Enabling or disabling discards pending records. */
+dit_status dit_timing_enable(dit_ctx *ctx, int on);
+
+/* Wait for the recorded events and return, per stage, the summed elapsed
+ * milliseconds ms[DIT_NSTAGES] and the number of timed launches
+ * count[DIT_NSTAGES] since the last read; then reset.  Synchronises with the
+ * recorded events (host blocks until they complete). */
+dit_status dit_timing_read(dit_ctx *ctx, double *ms, int64_t *count);
+
+/* Copy an intermediate buffer of the last dit_block_forward on this
+ * context into dst (device memory, at least `bytes` long), enqueued on the
+ * context's stream; for per-step checks.  Valid until the next call that
+ * uses the workspace.  Buffers, packed for that call's S = L + N with
+ * Sp = S rounded up to 64:
+ *   0 mod  fp32 [6, D]        1 h   bf16 [S, D] (norm1 output)
+ *   2 q    bf16 [H, S, 128]   3 k   bf16 [H, S, 128] (after head norm + rotary)
+ *   4 vt   bf16 [H, 128, Sp]  5 o   bf16 [S, D] (attention output)
+ *   6 h2   bf16 [S, D]        7 a   bf16 [S, F] (SwiGLU output)
+ * Errors: DIT_ERANGE if `which` is outside 0..7 or `bytes` exceeds the
+ * workspace buffer (bytes <= 0 is a no-op). */
+dit_status dit_debug_copy(dit_ctx *ctx, int which, void *dst, int64_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */
