@@ -8,17 +8,22 @@
 //
 // Design (CDNA4, 64-wide waves, MFMA 16x16x32 bf16):
 //  - block = 4 waves = 128 queries of one head; each wave owns 32 queries.
+//    Two blocks share a CU (<= 256 registers per lane, 64 KB LDS each), so
+//    each SIMD interleaves one wave's exponentials with the other's MFMAs.
 //  - the wave computes the TRANSPOSED scores S^T = K Q^T for a 64-key tile:
 //    K (from LDS) is the A operand, the wave's queries (registers, loaded
 //    once) the B operand.  A lane then holds one query column and 16 of its
-//    keys, so the softmax statistics are per lane (plus two cross-lane
-//    steps) and P^T is already in the B-operand layout of O^T += V^T P^T.
-//  - values arrive feature-major (vt [H, 128, Sp], written that way by the
-//    QKV product's epilogue), so V^T fragments are two 8-byte LDS reads.
-//  - K and V^T tiles are double-buffered in LDS (64 KB per block, two blocks
-//    per CU); XOR-swizzled chunk placement avoids bank conflicts.
-//  - exp2 with log2(e) folded into the fp32 score scale; the row sum is kept
-//    per lane and reduced once at the end.
+//    keys, so P^T is already in the B-operand layout of O^T += V^T P^T.
+//  - values arrive feature-major (vt [H, 128, Sp], as the QKV product's
+//    epilogue writes them), so V^T fragments are two 8-byte LDS reads.
+//  - K and V^T tiles go global -> LDS directly (global_load_lds_dwordx4,
+//    no register staging), double-buffered; each lane fetches the global
+//    chunk that belongs at its LDS position under the XOR swizzle.
+//  - the row sum is one more MFMA per 32 keys with an all-ones A operand
+//    (it sums the same bf16-rounded P the values are weighted with);
+//    the running maximum is rescaled lazily: only when a tile's maximum
+//    exceeds it by more than 2^8 (exponents stay <= 2^8, exact either way).
+//  - blocks are remapped so that each XCD (own L2) serves whole heads.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,22 +35,39 @@ constexpr int QW = 32;    // queries per wave
 constexpr int KT = 64;    // keys per tile
 constexpr int HD = 128;   // head dim
 constexpr int NT = 256;
-constexpr int K_U4 = KT * 16;     // K tile: 64 rows x 16 chunks
+constexpr int K_U4 = KT * 16;     // K tile: 64 rows x 16 chunks of 16 B
 constexpr int V_U4 = HD * 8;      // V^T tile: 128 rows x 8 chunks
 constexpr int STAGE = K_U4 + V_U4;
+constexpr float kLazy = 8.0f;     // rescale when the maximum grows by > 2^8
 
 __device__ __forceinline__ int kidx(int row, int c) { return row * 16 + (c ^ (row & 15)); }
 __device__ __forceinline__ int vidx(int d, int c) { return K_U4 + d * 8 + (c ^ ((d >> 1) & 7)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void g2l16(const void *g, u32x4 *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(l), 16, 0, 0);
+}
 }  // namespace
 
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT, 2)
 k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
-            const uint16_t *__restrict__ Vt, int S, int ldv, uint16_t *__restrict__ O, int ldo) {
+            const uint16_t *__restrict__ Vt, int S, int ldv, int heads, uint16_t *__restrict__ O,
+            int ldo) {
     __shared__ u32x4 lds[2 * STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = blockIdx.y;
-    const int q0 = blockIdx.x * QB + wave * QW;
     const int g = lane >> 4, l16 = lane & 15;
+
+    // XCD-compact order: consecutive work ids on one XCD share a head
+    const int nqb = (S + QB - 1) / QB;
+    const int total = nqb * heads;
+    int bid = blockIdx.x;
+    {
+        const int per = total / 8, rem = total % 8, xcd = bid % 8, loc = bid / 8;
+        bid = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+    }
+    const int h = bid / nqb;
+    const int q0 = (bid % nqb) * QB + wave * QW;
 
     const uint16_t *Qh = Q + static_cast<int64_t>(h) * S * HD;
     const uint16_t *Kh = Kg + static_cast<int64_t>(h) * S * HD;
@@ -62,64 +84,65 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
                 bf16x8, *reinterpret_cast<const u32x4 *>(Qh + static_cast<int64_t>(qr) * HD + ks * 32 + g * 8));
     }
 
-    // global -> LDS assignment
-    const int kc = tid & 15, kr0 = tid >> 4;   // K: 4 rows (kr0 + 16 i), chunk kc
-    const int vc = tid & 7, vr0 = tid >> 3;    // V^T: 4 rows (vr0 + 32 i), chunk vc
-    u32x4 rk[4], rv[4];
     const int ntiles = (S + KT - 1) / KT;
-
-    auto load_tile = [&](int t) {
+    // direct global -> LDS: wave instruction i writes 1 KB = 4 K rows or 8 V^T rows
+    auto issue_tile = [&](int t, int buf) {
         const int kv0 = t * KT;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = min(kv0 + kr0 + 16 * i, S - 1);
-            rk[i] = *reinterpret_cast<const u32x4 *>(Kh + static_cast<int64_t>(key) * HD + kc * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = vr0 + 32 * i;
-            u32x4 v = *reinterpret_cast<const u32x4 *>(Vh + static_cast<int64_t>(d) * ldv + kv0 + vc * 8);
-            const int k8 = kv0 + vc * 8;
-            if (k8 + 8 > S) {   // zero the values of keys >= S (their weights are 0)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t w = v[j];
-                    if (k8 + 2 * j >= S) w &= 0xffff0000u;
-                    if (k8 + 2 * j + 1 >= S) w &= 0x0000ffffu;
-                    v[j] = w;
-                }
-            }
-            rv[i] = v;
-        }
-    };
-    auto store_tile = [&](int buf) {
         u32x4 *L = lds + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L[kidx(kr0 + 16 * i, kc)] = rk[i];
+        for (int i = 0; i < 4; ++i) {
+            const int blk = wave * 4 + i;                 // 0..15
+            const int r = blk * 4 + (lane >> 4);          // K row 0..63
+            const int c = (lane & 15) ^ (r & 15);         // global chunk for LDS position lane&15
+            const int key = min(kv0 + r, S - 1);
+            g2l16(Kh + static_cast<int64_t>(key) * HD + c * 8, L + blk * 64);
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L[vidx(vr0 + 32 * i, vc)] = rv[i];
+        for (int i = 0; i < 4; ++i) {
+            const int blk = wave * 4 + i;                 // 0..15
+            const int d = blk * 8 + (lane >> 3);          // V^T row 0..127
+            const int c = (lane & 7) ^ ((d >> 1) & 7);
+            g2l16(Vh + static_cast<int64_t>(d) * ldv + kv0 + c * 8, L + K_U4 + blk * 64);
+        }
     };
 
-    f32x4 oacc[8][2];
+    f32x4 oacc[8][2], rsum[2];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    rsum[0] = rsum[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     float mrun[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.f, 0.f};
     const float sc = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
+    const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_u);
 
-    load_tile(0);
-    store_tile(0);
+    issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const int cur = t & 1;
-        if (t + 1 < ntiles) load_tile(t + 1);
-        const u32x4 *L = lds + cur * STAGE;
         const int kv0 = t * KT;
+        const bool tail = kv0 + KT > S;
+        if (tail) {
+            // keys >= S: zero their values so that 0-weight * garbage stays 0
+            u32x4 *L = lds + cur * STAGE;
+            uint16_t *V16 = reinterpret_cast<uint16_t *>(L + K_U4);
+            const int valid = S - kv0;
+            for (int e = tid; e < HD * KT; e += NT) {
+                const int d = e / KT, key = e % KT;
+                if (key >= valid) {
+                    const int c = key >> 3;
+                    V16[(d * 8 + (c ^ ((d >> 1) & 7))) * 8 + (key & 7)] = 0;
+                }
+            }
+            __syncthreads();
+        }
+        if (t + 1 < ntiles) issue_tile(t + 1, cur ^ 1);
+        const u32x4 *L = lds + cur * STAGE;
 
-        // ---- S^T = K Q^T for 64 keys x 32 queries
+        // ---- S^T = K Q^T for 64 keys x 32 queries (raw scores)
         f32x4 s[4][2];
 #pragma unroll
         for (int tk = 0; tk < 4; ++tk)
@@ -136,54 +159,62 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
             }
         }
 
-        // ---- online softmax per query column (lane); keys of this lane:
+        // ---- online softmax per query column (lane); keys of this lane are
         // kv0 + tk*16 + 4g + r
-        const bool tail = kv0 + KT > S;
-        float alpha[2];
+        if (tail) {
+#pragma unroll
+            for (int tk = 0; tk < 4; ++tk)
+#pragma unroll
+                for (int tq = 0; tq < 2; ++tq)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (kv0 + tk * 16 + 4 * g + r >= S) s[tk][tq][r] = -INFINITY;
+        }
+        float mt[2];
 #pragma unroll
         for (int tq = 0; tq < 2; ++tq) {
-            float mx = -INFINITY;
+            float mx = s[0][tq][0];
 #pragma unroll
             for (int tk = 0; tk < 4; ++tk)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = s[tk][tq][r] * sc;
-                    if (tail && kv0 + tk * 16 + 4 * g + r >= S) v = -INFINITY;
-                    s[tk][tq][r] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tk][tq][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mnew = fmaxf(mrun[tq], mx);
-            alpha[tq] = exp2f(mrun[tq] - mnew);
-            mrun[tq] = mnew;
-            float ps = 0.f;
-#pragma unroll
-            for (int tk = 0; tk < 4; ++tk)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float p = exp2f(s[tk][tq][r] - mnew);
-                    s[tk][tq][r] = p;
-                    ps += p;
-                }
-            lsum[tq] = lsum[tq] * alpha[tq] + ps;
+            mt[tq] = mx * sc;
         }
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd)
-#pragma unroll
-            for (int tq = 0; tq < 2; ++tq) oacc[dd][tq] *= alpha[tq];
-
-        // ---- O^T += V^T P^T, two 32-key steps
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            bf16x8 pf[2];
+        const bool grow = (mt[0] > mrun[0] + kLazy) || (mt[1] > mrun[1] + kLazy);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
             for (int tq = 0; tq < 2; ++tq) {
-                const f32x4 a = s[2 * j][tq], b = s[2 * j + 1][tq];
-                u32x4 u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                           pack_bf16x2(b[2], b[3])};
-                pf[tq] = __builtin_bit_cast(bf16x8, u);
+                const float mnew = fmaxf(mrun[tq], mt[tq]);
+                const float alpha = exp2f(mrun[tq] - mnew);
+                mrun[tq] = mnew;
+#pragma unroll
+                for (int dd = 0; dd < 8; ++dd) oacc[dd][tq] *= alpha;
+                rsum[tq] *= alpha;
             }
+        }
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+            const float nm = -mrun[tq];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const f32x4 a = s[2 * j][tq], b = s[2 * j + 1][tq];
+                u32x4 u = {pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(a[0], sc, nm)), __builtin_amdgcn_exp2f(fmaf(a[1], sc, nm))),
+                           pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(a[2], sc, nm)), __builtin_amdgcn_exp2f(fmaf(a[3], sc, nm))),
+                           pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(b[0], sc, nm)), __builtin_amdgcn_exp2f(fmaf(b[1], sc, nm))),
+                           pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(b[2], sc, nm)), __builtin_amdgcn_exp2f(fmaf(b[3], sc, nm)))};
+                pf[j][tq] = __builtin_bit_cast(bf16x8, u);
+            }
+        }
+
+        // ---- O^T += V^T P^T and the row sums, two 32-key steps
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int tq = 0; tq < 2; ++tq)
+                rsum[tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[j][tq], rsum[tq], 0, 0, 0);
 #pragma unroll
             for (int dd = 0; dd < 8; ++dd) {
                 const int d = dd * 16 + l16;
@@ -194,21 +225,18 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
                 for (int tq = 0; tq < 2; ++tq)
-                    oacc[dd][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[tq], oacc[dd][tq], 0, 0, 0);
+                    oacc[dd][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[j][tq], oacc[dd][tq], 0, 0, 0);
             }
         }
 
-        if (t + 1 < ntiles) store_tile(cur ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile t+1 have landed
+        __syncthreads();                 // everyone's have, and nobody still reads tile t
     }
 
     // ---- normalise and store o[q][h*128 + d], d = dd*16 + 4g + r
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
-        float l = lsum[tq];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
-        const float inv = 1.0f / l;
+        const float inv = 1.0f / rsum[tq][0];
         const int q = q0 + tq * 16 + l16;
         if (q >= S) continue;
         uint16_t *orow = O + static_cast<int64_t>(q) * ldo + h * HD;
@@ -224,8 +252,8 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int heads,
                             int S, int ldv, uint16_t *o, int ldo, hipStream_t st) {
     if (S <= 0 || heads <= 0) return hipSuccess;
-    dim3 grid(static_cast<unsigned>((S + QB - 1) / QB), static_cast<unsigned>(heads));
-    k_attention<<<grid, NT, 0, st>>>(q, k, vt, S, ldv, o, ldo);
+    const int grid = ((S + QB - 1) / QB) * heads;
+    k_attention<<<grid, NT, 0, st>>>(q, k, vt, S, ldv, heads, o, ldo);
     return hipGetLastError();
 }
 
