@@ -33,7 +33,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// silu(x) = x * sigmoid(x); hardware reciprocal (1 ulp) of 1 + e^-x.
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Butterfly sum over all 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -206,7 +206,7 @@ dit_status block_forward(dit_ctx *c, const dit_block *b, float *x, const float *
     e.qk_eps = A.qk_eps;
     {
         Stage t(c, DIT_ST_QKV);
-        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], b->scale[0], w8, S, 3 * D, D, e, st), "qkv");
+        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], b->scale[0], w8, S, 3 * D, D, e, st, true), "qkv");
     }
     {
         Stage t(c, DIT_ST_ATTN);
@@ -220,7 +220,7 @@ dit_status block_forward(dit_ctx *c, const dit_block *b, float *x, const float *
     g.gate = mod + 2 * D;
     {
         Stage t(c, DIT_ST_OUT);
-        DIT_LAUNCH(c, launch_gemm(c->o, b->w[1], b->scale[1], w8, S, D, D, g, st), "out");
+        DIT_LAUNCH(c, launch_gemm(c->o, b->w[1], b->scale[1], w8, S, D, D, g, st, true), "out");
     }
     {
         Stage t(c, DIT_ST_NORM2);
@@ -233,12 +233,12 @@ dit_status block_forward(dit_ctx *c, const dit_block *b, float *x, const float *
     u.act = c->a;
     {
         Stage t(c, DIT_ST_UP);
-        DIT_LAUNCH(c, launch_gemm(c->h2, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st), "up");
+        DIT_LAUNCH(c, launch_gemm(c->h2, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st, true), "up");
     }
     g.gate = mod + 5 * D;
     {
         Stage t(c, DIT_ST_DOWN);
-        DIT_LAUNCH(c, launch_gemm(c->a, b->w[3], b->scale[3], w8, S, D, F, g, st), "down");
+        DIT_LAUNCH(c, launch_gemm(c->a, b->w[3], b->scale[3], w8, S, D, F, g, st, true), "down");
     }
     return DIT_OK;
 }
@@ -456,7 +456,7 @@ dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint
     e.kind = EPI_F32;
     e.out = out;
     e.ldo = N;
-    DIT_LAUNCH(ctx, launch_gemm(a, w, scale, wtype == DIT_W_INT8_B32, M, N, K, e, ctx->stream), "linear");
+    DIT_LAUNCH(ctx, launch_gemm(a, w, scale, wtype == DIT_W_INT8_B32, M, N, K, e, ctx->stream, false), "linear");
     return DIT_OK;
 }
 
@@ -494,7 +494,7 @@ dit_status dit_prologue(dit_ctx *ctx, const dit_model *m, const float *ctx_feats
     e.kind = EPI_F32;
     e.out = txt;
     e.ldo = A.hidden;
-    DIT_LAUNCH(ctx, launch_gemm(ctx->ctxb, m->w_txt, nullptr, false, L, A.hidden, A.text_dim, e, ctx->stream), "txt_in");
+    DIT_LAUNCH(ctx, launch_gemm(ctx->ctxb, m->w_txt, nullptr, false, L, A.hidden, A.text_dim, e, ctx->stream, true), "txt_in");
     return DIT_OK;
 }
 
@@ -520,7 +520,7 @@ dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, cons
         e.kind = EPI_F32;
         e.out = ctx->seq + static_cast<size_t>(L) * D;
         e.ldo = D;
-        DIT_LAUNCH(ctx, launch_gemm(ctx->latb, m->w_in, nullptr, false, N, D, lat, e, st), "img_in");
+        DIT_LAUNCH(ctx, launch_gemm(ctx->latb, m->w_in, nullptr, false, N, D, lat, e, st, true), "img_in");
     }
     for (int i = 0; i < m->n_blocks; ++i) DIT_TRY(block_forward(ctx, &m->blocks[i], ctx->seq, ctx->vec, cos_t, sin_t, S));
     {
@@ -533,7 +533,7 @@ dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, cons
         f.kind = EPI_F32;
         f.out = ctx->vel;
         f.ldo = lat;
-        DIT_LAUNCH(ctx, launch_gemm(ctx->h, m->w_final, nullptr, false, N, lat, D, f, st), "final linear");
+        DIT_LAUNCH(ctx, launch_gemm(ctx->h, m->w_final, nullptr, false, N, lat, D, f, st, true), "final linear");
     }
     {
         Stage tm(ctx, DIT_ST_EULER);

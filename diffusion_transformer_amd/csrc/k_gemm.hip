@@ -74,6 +74,127 @@ __device__ __forceinline__ void dequant16(u32x4 q, float s, u32x4 &lo, u32x4 &hi
 
 }  // namespace
 
+// Epilogue shared by the products (wave tile TMW*16 rows x 128 columns).
+// Lane holds rows m0 + wm*TMW*16 + tm*16 + 4*(lane>>4) + r and output pairs
+// P = (n0 + wn*128)/2 + tp*16 + (lane & 15): column 2P in acc[tm][tp][r],
+// column 2P+1 in acc[tm][tp+4][r].
+template <int EPI, int TMW>
+__device__ __forceinline__ void gemm_epilogue(f32x4 (&acc)[TMW][TN], int m0, int n0, int wm, int wn, int lane,
+                                              int M, int N, const GemmEpi &ep) {
+    const int col0 = n0 + wn * WN;
+    if (col0 >= N) return;
+    const int rbase = m0 + wm * TMW * 16 + 4 * (lane >> 4);
+    const int pl = lane & 15;
+
+    if constexpr (EPI == EPI_F32 || EPI == EPI_GATE_RES) {
+#pragma unroll
+        for (int tm = 0; tm < TMW; ++tm) {
+            __builtin_amdgcn_sched_barrier(0);   // bound the loads kept in flight
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rbase + tm * 16 + r;
+                if (row >= M) continue;
+#pragma unroll
+                for (int tp = 0; tp < TN / 2; ++tp) {
+                    const int c = col0 + 2 * (tp * 16 + pl);
+                    if (c >= N) continue;
+                    float2 *dst = reinterpret_cast<float2 *>(ep.out + static_cast<int64_t>(row) * ep.ldo + c);
+                    float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
+                    if constexpr (EPI == EPI_F32) {
+                        *dst = make_float2(e, o);
+                    } else {
+                        float2 g = *reinterpret_cast<const float2 *>(ep.gate + c);
+                        float2 x = *dst;
+                        x.x += g.x * e;
+                        x.y += g.y * o;
+                        *dst = x;
+                    }
+                }
+            }
+        }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        const int half = N / 2;
+#pragma unroll
+        for (int tm = 0; tm < TMW; ++tm) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rbase + tm * 16 + r;
+                if (row >= M) continue;
+#pragma unroll
+                for (int tp = 0; tp < TN / 2; ++tp) {
+                    const int p = col0 / 2 + tp * 16 + pl;
+                    if (2 * p >= N) continue;
+                    float g = acc[tm][tp][r], u = acc[tm][tp + TN / 2][r];
+                    ep.act[static_cast<int64_t>(row) * half + p] = f32_to_bf16(silu_f(g) * u);
+                }
+            }
+        }
+    } else if constexpr (EPI == EPI_QKV) {
+        const int H = ep.heads;
+        const int hb = col0 / 128;
+        const int region = hb / H, head = hb % H;
+        if (region < 2) {
+            const float *nw = region == 0 ? ep.qn : ep.kn;
+            uint16_t *dst = region == 0 ? ep.q : ep.k;
+            float we[TN / 2], wo[TN / 2];
+#pragma unroll
+            for (int tp = 0; tp < TN / 2; ++tp) {
+                const int p = tp * 16 + pl;
+                we[tp] = nw[2 * p];
+                wo[tp] = nw[2 * p + 1];
+            }
+#pragma unroll
+            for (int tm = 0; tm < TMW; ++tm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int tp = 0; tp < TN / 2; ++tp) {
+                        float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
+                        ss += e * e + o * o;
+                    }
+                    // sum over the 16 lanes that share this row (lane bits 0..3)
+                    ss += __shfl_xor(ss, 1, 64);
+                    ss += __shfl_xor(ss, 2, 64);
+                    ss += __shfl_xor(ss, 4, 64);
+                    ss += __shfl_xor(ss, 8, 64);
+                    const float rstd = rsqrtf(ss * (1.0f / 128.0f) + ep.qk_eps);
+                    const int row = rbase + tm * 16 + r;
+                    const int rr = min(row, M - 1);
+#pragma unroll
+                    for (int tp = 0; tp < TN / 2; ++tp) {
+                        const int p = tp * 16 + pl;
+                        const float c = ep.cos[static_cast<int64_t>(rr) * 64 + p];
+                        const float s = ep.sin[static_cast<int64_t>(rr) * 64 + p];
+                        const float a = acc[tm][tp][r] * rstd * we[tp];
+                        const float b = acc[tm][tp + TN / 2][r] * rstd * wo[tp];
+                        if (row < M)
+                            *reinterpret_cast<uint32_t *>(
+                                dst + (static_cast<int64_t>(head) * M + row) * 128 + 2 * p) =
+                                pack_bf16x2(a * c - b * s, a * s + b * c);
+                    }
+                }
+        } else {
+            // V: rows rbase + tm*16 + 0..3 are consecutive -> 4 bf16 along vt's row
+#pragma unroll
+            for (int tm = 0; tm < TMW; ++tm) {
+                const int row0 = rbase + tm * 16;
+                if (row0 >= ep.ldv) continue;
+#pragma unroll
+                for (int tp = 0; tp < TN / 2; ++tp) {
+                    const int p = tp * 16 + pl;
+                    uint16_t *d0 = ep.vt + (static_cast<int64_t>(head) * 128 + 2 * p) * ep.ldv + row0;
+                    uint16_t *d1 = d0 + ep.ldv;
+                    const f32x4 e = acc[tm][tp], o = acc[tm][tp + TN / 2];
+                    *reinterpret_cast<u32x2 *>(d0) = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
+                    *reinterpret_cast<u32x2 *>(d1) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, bool W8, int EPI>
 __global__ void __launch_bounds__((BM / 64) * (BN / 128) * 64)
 k_gemm(const uint16_t *__restrict__ A, const void *__restrict__ Wv,
@@ -222,117 +343,179 @@ k_gemm(const uint16_t *__restrict__ A, const void *__restrict__ Wv,
         __syncthreads();
     }
 
-    // ---- epilogue.  Lane holds rows m0 + wm*64 + tm*16 + 4*(lane>>4) + r and
-    // output pairs P = (n0 + wn*128)/2 + tp*16 + (lane & 15): column 2P in
-    // acc[tm][tp][r], column 2P+1 in acc[tm][tp+4][r].
-    const int col0 = n0 + wn * WN;
-    if (col0 >= N) return;
-    const int rbase = m0 + wm * WM + 4 * (lane >> 4);
-    const int pl = lane & 15;
+    gemm_epilogue<EPI, TM>(acc, m0, n0, wm, wn, lane, M, N, ep);
+}
 
-    if constexpr (EPI == EPI_F32 || EPI == EPI_GATE_RES) {
+// ---------------------------------------------------------------------------
+// Ping-pong variant for bf16 weights: 256x256x64 tiles, 8 waves.  The two
+// waves of every SIMD alternate between a compute phase (64 MFMAs on
+// fragments already in registers) and a memory phase (LDS -> register
+// fragments for their next compute phase; wave group 0 also issues the
+// direct global -> LDS loads of the k-tile two steps ahead).  One workgroup
+// barrier ends every phase, so at any time one wave per SIMD feeds the
+// matrix core while the other waits on memory.
+//
+//   phase 2t   : group 0 computes k-tile t     | group 1 loads fragments of t
+//   phase 2t+1 : group 0 loads fragments of t+1| group 1 computes k-tile t
+//                (and issues k-tile t+2 -> LDS buffer t&1)
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int PP_BM = 256, PP_BN = 256;
+constexpr int PP_STAGE = (PP_BM + PP_BN) * 8;   // u32x4 per LDS buffer (64 KB)
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Barriers and waits as volatile asm with a memory clobber (no LDS or
+// global access moves across them).  The end-of-compute wait takes an
+// accumulator as input so it cannot be hoisted above the phase's MFMAs.
+__device__ __forceinline__ void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_vm0_after(float dep) {
+    asm volatile("s_waitcnt vmcnt(0)" ::"v"(dep) : "memory");
+}
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+}  // namespace
+
+template <int EPI>
+__global__ void __launch_bounds__(512, 1)
+k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
+          GemmEpi ep) {
+    constexpr int BM = PP_BM, BN = PP_BN;
+    __shared__ u32x4 lds[2 * PP_STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 2, wg = wave & 3;     // group 0: waves 0-3, group 1: waves 4-7
+    const int wm = wg, wn = grp;                  // wave tile (wm*64, wn*128)
+
+    const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+    const int total = ntm * ntn;
+    int bid = blockIdx.x;
+    {
+        const int per = total / 8, rem = total % 8, xcd = bid % 8, loc = bid / 8;
+        bid = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+    }
+    constexpr int GM = 8;
+    const int group = bid / (GM * ntn), first = group * GM;
+    const int gsz = min(ntm - first, GM);
+    const int tile_m = first + (bid % (GM * ntn)) % gsz;
+    const int tile_n = (bid % (GM * ntn)) / gsz;
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int T = K / BK;
+
+    // Group 0 issues whole k-tiles: 32 A and 32 B wave-instructions of 1 KB,
+    // 8 + 8 per wave; instruction i of wave wg writes LDS slots 64wg + 8i ..
+    // +7, lane -> slot 64wg + 8i + (lane>>3), chunk position lane&7.  The
+    // operands are read without row clamping: the caller guarantees A has
+    // a multiple of 256 rows allocated and N % 256 == 0.  The swizzled chunk
+    // (lane&7) ^ ((slot>>1)&7) only depends on the parity of i.
+    const int lrow = lane >> 3, lpos = lane & 7;
+    const int cE = lpos ^ ((lrow >> 1) & 7), cO = cE ^ 4;
+    const uint16_t *a_base = A + static_cast<int64_t>(m0) * K;
+    const int a_offE = (64 * wg + lrow) * K + cE * 8, a_offO = (64 * wg + lrow) * K + cO * 8;
+    // W row of slot 64wg + 8i + lrow: even rows fill slots 0..127, odd rows 128..255
+    const int n_of0 = wg < 2 ? 2 * (64 * wg + lrow) : 2 * (64 * wg - 128 + lrow) + 1;
+    const uint16_t *w_base = W + static_cast<int64_t>(n0) * K;
+    const int w_offE = n_of0 * K + cE * 8, w_offO = n_of0 * K + cO * 8;
+    auto issue_tile = [&](int t, int buf) {
+        u32x4 *L = lds + buf * PP_STAGE;
+        const uint16_t *ab = a_base + t * BK;
+        const uint16_t *wb = w_base + t * BK;
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
+        for (int i = 0; i < 8; ++i) {
+            const int j = wg * 8 + i;
+            __builtin_amdgcn_global_load_lds(ab + (i & 1 ? a_offO : a_offE) + i * 8 * K,
+                                             (lds_void_t *)(L + j * 64), 16, 0, 0);
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = rbase + tm * 16 + r;
-                if (row >= M) continue;
+        for (int i = 0; i < 8; ++i) {
+            const int j = wg * 8 + i;
+            __builtin_amdgcn_global_load_lds(wb + (i & 1 ? w_offO : w_offE) + i * 16 * K,
+                                             (lds_void_t *)(L + BM * 8 + j * 64), 16, 0, 0);
+        }
+    };
+
+    // LDS fragment addresses.  Every A slot this lane reads is
+    // wm*64 + tm*16 + (lane&15) and every B slot a multiple of 16 plus
+    // (lane&15), so the swizzle term (slot>>1)&7 is the same for all of them:
+    // per k-step one base address, the tiles are immediate offsets.
+    const int l16 = lane & 15;
+    const int c0 = (lane >> 4) ^ ((l16 >> 1) & 7);      // chunk position at k-step 0
+    const int offA0 = (wm * WM + l16) * 8 + c0, offA1 = offA0 ^ 4;
+    const int offB0 = BM * 8 + (wn * (WN / 2) + l16) * 8 + c0, offB1 = offB0 ^ 4;
+
+    bf16x8 af[2][TM], bfr[2][TN];
+    auto load_frags = [&](int buf) {
+        const u32x4 *L = lds + buf * PP_STAGE;
 #pragma unroll
-                for (int tp = 0; tp < TN / 2; ++tp) {
-                    const int c = col0 + 2 * (tp * 16 + pl);
-                    if (c >= N) continue;
-                    float2 *dst = reinterpret_cast<float2 *>(ep.out + static_cast<int64_t>(row) * ep.ldo + c);
-                    float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
-                    if constexpr (EPI == EPI_F32) {
-                        *dst = make_float2(e, o);
-                    } else {
-                        float2 g = *reinterpret_cast<const float2 *>(ep.gate + c);
-                        float2 x = *dst;
-                        x.x += g.x * e;
-                        x.y += g.y * o;
-                        *dst = x;
-                    }
-                }
-            }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-        const int half = N / 2;
+        for (int tm = 0; tm < TM; ++tm) {
+            af[0][tm] = __builtin_bit_cast(bf16x8, L[offA0 + tm * 128]);
+            af[1][tm] = __builtin_bit_cast(bf16x8, L[offA1 + tm * 128]);
+        }
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
+        for (int tn = 0; tn < TN; ++tn) {
+            const int o = ((tn < TN / 2 ? 0 : BN / 2) + (tn % (TN / 2)) * 16) * 8;
+            bfr[0][tn] = __builtin_bit_cast(bf16x8, L[offB0 + o]);
+            bfr[1][tn] = __builtin_bit_cast(bf16x8, L[offB1 + o]);
+        }
+    };
+
+    f32x4 acc[TM][TN];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = rbase + tm * 16 + r;
-                if (row >= M) continue;
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int tp = 0; tp < TN / 2; ++tp) {
-                    const int p = col0 / 2 + tp * 16 + pl;
-                    if (2 * p >= N) continue;
-                    float g = acc[tm][tp][r], u = acc[tm][tp + TN / 2][r];
-                    ep.act[static_cast<int64_t>(row) * half + p] = f32_to_bf16(silu_f(g) * u);
-                }
-            }
-    } else if constexpr (EPI == EPI_QKV) {
-        const int H = ep.heads;
-        const int hb = col0 / 128;
-        const int region = hb / H, head = hb % H;
-        if (region < 2) {
-            const float *nw = region == 0 ? ep.qn : ep.kn;
-            uint16_t *dst = region == 0 ? ep.q : ep.k;
-            float we[TN / 2], wo[TN / 2];
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&]() {
 #pragma unroll
-            for (int tp = 0; tp < TN / 2; ++tp) {
-                const int p = tp * 16 + pl;
-                we[tp] = nw[2 * p];
-                wo[tp] = nw[2 * p + 1];
-            }
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float ss = 0.f;
-#pragma unroll
-                    for (int tp = 0; tp < TN / 2; ++tp) {
-                        float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
-                        ss += e * e + o * o;
-                    }
-                    // sum over the 16 lanes that share this row (lane bits 0..3)
-                    ss += __shfl_xor(ss, 1, 64);
-                    ss += __shfl_xor(ss, 2, 64);
-                    ss += __shfl_xor(ss, 4, 64);
-                    ss += __shfl_xor(ss, 8, 64);
-                    const float rstd = rsqrtf(ss * (1.0f / 128.0f) + ep.qk_eps);
-                    const int row = rbase + tm * 16 + r;
-                    const int rr = min(row, M - 1);
-#pragma unroll
-                    for (int tp = 0; tp < TN / 2; ++tp) {
-                        const int p = tp * 16 + pl;
-                        const float c = ep.cos[static_cast<int64_t>(rr) * 64 + p];
-                        const float s = ep.sin[static_cast<int64_t>(rr) * 64 + p];
-                        const float a = acc[tm][tp][r] * rstd * we[tp];
-                        const float b = acc[tm][tp + TN / 2][r] * rstd * wo[tp];
-                        if (row < M)
-                            *reinterpret_cast<uint32_t *>(
-                                dst + (static_cast<int64_t>(head) * M + row) * 128 + 2 * p) =
-                                pack_bf16x2(a * c - b * s, a * s + b * c);
-                    }
-                }
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
+    };
+
+    // prologue: k-tiles 0 and 1 into LDS; group 0 takes the fragments of 0
+    if (grp == 0) {
+        issue_tile(0, 0);
+        if (T > 1) {
+            issue_tile(1, 1);
+            wait_vm16();
         } else {
-            // V: rows rbase + tm*16 + 0..3 are consecutive -> 4 bf16 along vt's row
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const int row0 = rbase + tm * 16;
-                if (row0 >= ep.ldv) continue;
-#pragma unroll
-                for (int tp = 0; tp < TN / 2; ++tp) {
-                    const int p = tp * 16 + pl;
-                    uint16_t *d0 = ep.vt + (static_cast<int64_t>(head) * 128 + 2 * p) * ep.ldv + row0;
-                    uint16_t *d1 = d0 + ep.ldv;
-                    const f32x4 e = acc[tm][tp], o = acc[tm][tp + TN / 2];
-                    *reinterpret_cast<u32x2 *>(d0) = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
-                    *reinterpret_cast<u32x2 *>(d1) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                }
-            }
+            wait_vm0();
         }
     }
+    pp_barrier();
+    if (grp == 0) {
+        load_frags(0);
+        wait_lgkm0();
+    }
+    pp_barrier();
+
+    for (int t = 0; t < T; ++t) {
+        // phase 2t
+        if (grp == 0) {
+            compute();
+            __builtin_amdgcn_sched_barrier(0);       // after all of this phase's MFMAs:
+            wait_vm0();                              // k-tile t+1 has landed
+        } else {
+            load_frags(t & 1);
+            wait_lgkm0();
+        }
+        pp_barrier();
+        // phase 2t+1
+        if (grp == 0) {
+            if (t + 2 < T) issue_tile(t + 2, t & 1);
+            if (t + 1 < T) {
+                load_frags((t + 1) & 1);
+                wait_lgkm0();
+            }
+        } else {
+            compute();
+        }
+        pp_barrier();
+    }
+
+    gemm_epilogue<EPI, TM>(acc, m0, n0, wm, wn, lane, M, N, ep);
 }
 
 template <int BM, int BN, bool W8>
@@ -359,12 +542,31 @@ static hipError_t launch_cfg(const uint16_t *A, const void *W, const uint16_t *W
     return hipGetLastError();
 }
 
+template <int EPI>
+static hipError_t launch_pp(const uint16_t *A, const uint16_t *W, int M, int N, int K, const GemmEpi &ep,
+                            hipStream_t st) {
+    const int grid = static_cast<int>(cdiv(M, PP_BM) * cdiv(N, PP_BN));
+    k_gemm_pp<EPI><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Ws, bool w8, int M, int N,
-                       int K, const GemmEpi &ep, hipStream_t st) {
+                       int K, const GemmEpi &ep, hipStream_t st, bool a_rows_padded) {
     if (M <= 0) return hipSuccess;
-    // Large problems: 256x256 tiles (8 waves).  Small ones: 128x128 (2 waves)
-    // so the grid still spreads over the chip.
+    // Large problems: 256x256 tiles (8 waves; ping-pong for bf16 weights when
+    // A's allocation covers whole 256-row tiles and N is a multiple of 256).
+    // Small ones: 128x128 (2 waves) so the grid still spreads over the chip.
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
+    if (big_tiles >= 128 && !w8 && N % 256 == 0 && (a_rows_padded || M % 256 == 0)) {
+        const uint16_t *Wb = static_cast<const uint16_t *>(W);
+        switch (ep.kind) {
+            case EPI_F32: return launch_pp<EPI_F32>(A, Wb, M, N, K, ep, st);
+            case EPI_GATE_RES: return launch_pp<EPI_GATE_RES>(A, Wb, M, N, K, ep, st);
+            case EPI_SWIGLU: return launch_pp<EPI_SWIGLU>(A, Wb, M, N, K, ep, st);
+            case EPI_QKV: return launch_pp<EPI_QKV>(A, Wb, M, N, K, ep, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (big_tiles >= 128) {
         return w8 ? launch_cfg<256, 256, true>(A, W, Ws, M, N, K, ep, st)
                   : launch_cfg<256, 256, false>(A, W, Ws, M, N, K, ep, st);
