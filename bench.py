@@ -43,6 +43,15 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-denoise", action="store_true", help="skip the 32-block image timing")
     p.add_argument("--no-int8", action="store_true", help="skip the int8-weight block timing")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
+                        "scale reference for FETCH_SIZE / WRITE_SIZE counter runs)")
+    p.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "profiles", "traffic.json"),
+                   help="measured HBM bytes per launch of the dominant kernel (from counter runs)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE run and a "
+                        "WRITE_SIZE run (both with --copy-calibration) into --traffic-json")
     return p.parse_args()
 
 
@@ -56,6 +65,94 @@ def stage_flops(S, D, H, F):
         "up": 2 * S * D * 2 * F,
         "down": 2 * S * F * D,
     }
+
+
+STAGE_SOURCE = {"qkv": "k_gemm.hip", "out": "k_gemm.hip", "up": "k_gemm.hip", "down": "k_gemm.hip",
+                "attn": "k_attn.hip", "mod": "k_misc.hip"}
+
+
+def source_sha(name):
+    import hashlib
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "diffusion_transformer_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(args, stage):
+    """HBM bytes per launch of `stage`'s kernel measured by the FETCH_SIZE and
+    WRITE_SIZE counter runs (scaled by a plain copy of known size), as
+    recorded in profiles/traffic.json; None when absent or when the kernel's
+    source has changed since the counters were taken."""
+    try:
+        with open(args.traffic_json) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(stage)
+    if not rec or rec.get("source_sha256") != source_sha(STAGE_SOURCE[stage]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def summarize_counters(fetch_csv, write_csv, out_json):
+    """Per-launch HBM bytes of the block's kernels from rocprofv3 counter
+    runs.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled so
+    that the 1 GiB calibration copy reads and writes exactly 1 GiB.  The
+    block's launches come in a fixed order (GEMV, norm, QKV, attention, OUT,
+    norm, UP, DOWN), which tells the OUT and DOWN launches of the shared
+    gated-residual product apart."""
+    import csv
+    import collections
+
+    def load(path, counter):
+        per = collections.defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            per[d] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+        return per, names
+
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per, names = load(path, counter)
+        copy_kib = sum(v for d, v in per.items() if "copyBuffer" in names[d])
+        scale = (1 << 30) / 1024.0 / copy_kib if copy_kib else None
+        order = sorted(d for d in per if "dit::" in names[d])
+        stage_of = {}
+        pending = None
+        for d in order:
+            n = names[d]
+            if "k_gemm_pp<3>" in n or "k_gemm<256, 256, false, 3>" in n:
+                stage_of[d] = "qkv"
+            elif "k_attention" in n:
+                stage_of[d] = "attn"
+            elif "k_gemm_pp<2>" in n or "k_gemm<256, 256, false, 2>" in n:
+                stage_of[d] = "up"
+            elif "k_gemm_pp<1>" in n or "k_gemm<256, 256, false, 1>" in n:
+                stage_of[d] = "down" if pending == "up" else "out"
+            elif "k_gemv" in n:
+                stage_of[d] = "mod"
+            if d in stage_of:
+                pending = stage_of[d]
+        acc = collections.defaultdict(list)
+        for d, st in stage_of.items():
+            acc[st].append(per[d])
+        for st, v in acc.items():
+            rec = res.setdefault(st, {})
+            rec[counter.lower() + "_kib_mean"] = sum(v) / len(v)
+            rec[counter.lower() + "_scale"] = scale
+            rec["launches"] = len(v)
+    for st, rec in res.items():
+        if rec.get("fetch_size_scale") and rec.get("write_size_scale"):
+            rec["bytes_per_launch"] = int(1024 * (rec["fetch_size_kib_mean"] * rec["fetch_size_scale"]
+                                                  + rec["write_size_kib_mean"] * rec["write_size_scale"]))
+        rec["source_sha256"] = source_sha(STAGE_SOURCE[st])
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
+    print(json.dumps(res, indent=1, sort_keys=True))
 
 
 def time_blocks(L, torch, ctx, bw, x, seq, sh, steps, warmup):
@@ -74,6 +171,9 @@ def time_blocks(L, torch, ctx, bw, x, seq, sh, steps, warmup):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.traffic_json)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is "
               "described in DESIGN.md and not run here.", file=sys.stderr)
@@ -87,6 +187,14 @@ def main():
 
     torch.cuda.set_device(0)
     out = {}
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: one 1 GiB device-to-device copy")
+        del src, dst
 
     # ---------------------------------------------------------------- block forward (bf16)
     sh = synth.SHAPES["s4608"]
@@ -128,7 +236,7 @@ def main():
     dom_tf = fl[dom] / (stages[dom] * 1e-3) / 1e12
     roofline = {"kernel": f"{dom} product" if dom not in ("attn", "mod") else dom, "bound": "mfma",
                 "achieved": round(dom_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(args, dom),
                 "flops_per_launch": fl[dom], "avg_ms": round(stages[dom], 4)}
     del bw, x, case
     torch.cuda.empty_cache()
@@ -249,9 +357,8 @@ def bench_images(torch, L, synth, images):
 
 
 def cpu_baseline():
-    """The CPU oracle (float64 NumPy) on one whole 512-px block forward
-    (L=64 + N=1024 rows, hidden 3072, ffn 12288): ~343 GFLOP of the same
-    per-row arithmetic as the 1024-px block, reported in the metric's unit."""
+    """The CPU oracle (float64 NumPy) on one whole block forward of the same
+    1024-px workload (same seed), reported in the metric's unit."""
     import oracle as O
     from diffusion_transformer_amd import synth
     try:
@@ -259,7 +366,7 @@ def cpu_baseline():
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    case = synth.block_case("s1088")
+    case = synth.block_case("s4608")
     sh = case["shape"]
     oa = O.Arch(sh.hidden, sh.heads, 128, sh.ffn)
     pos = O.positions(sh.L, sh.h, sh.w)
@@ -275,8 +382,8 @@ def cpu_baseline():
     log(f"cpu oracle: {dt:.1f} s for {flops / 1e9:.1f} GFLOP ({threads} threads)")
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": "one whole block forward of the float64 NumPy oracle at the 512-px block "
-                      "(L=64 + N=1024 rows, hidden 3072, 24x128 heads, ffn 12288), 343.2 GFLOP"}
+            "sample": "one whole block forward of the float64 NumPy oracle on the same 1024-px block "
+                      "(L=512 + N=4096 rows, hidden 3072, 24x128 heads, ffn 12288), 1652.6 GFLOP"}
 
 
 if __name__ == "__main__":

@@ -15,7 +15,10 @@
 //    once) the B operand.  A lane then holds one query column and 16 of its
 //    keys, so P^T is already in the B-operand layout of O^T += V^T P^T.
 //  - values arrive feature-major (vt [H, 128, Sp], as the QKV product's
-//    epilogue writes them), so V^T fragments are two 8-byte LDS reads.
+//    epilogue writes them).  The K tile's rows are placed in LDS in the key
+//    order kappa(r) = 8*((r%16)/4) + 4*(r/16) + r%4 within each 32 keys, so
+//    the 8 scores a lane holds for one 32-key step are keys 8g .. 8g+7 and
+//    each V^T fragment is a single 16-byte LDS read.
 //  - K and V^T tiles go global -> LDS directly (global_load_lds_dwordx4,
 //    no register staging), double-buffered; each lane fetches the global
 //    chunk that belongs at its LDS position under the XOR swizzle.
@@ -92,9 +95,11 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int blk = wave * 4 + i;                 // 0..15
-            const int r = blk * 4 + (lane >> 4);          // K row 0..63
+            const int r = blk * 4 + (lane >> 4);          // LDS K row 0..63
             const int c = (lane & 15) ^ (r & 15);         // global chunk for LDS position lane&15
-            const int key = min(kv0 + r, S - 1);
+            const int rr = r & 31;
+            const int kk = (r & 32) + 8 * ((rr & 15) >> 2) + 4 * (rr >> 4) + (rr & 3);   // kappa
+            const int key = min(kv0 + kk, S - 1);
             g2l16(Kh + static_cast<int64_t>(key) * HD + c * 8, L + blk * 64);
         }
 #pragma unroll
@@ -159,8 +164,8 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
             }
         }
 
-        // ---- online softmax per query column (lane); keys of this lane are
-        // kv0 + tk*16 + 4g + r
+        // ---- online softmax per query column (lane); the score in
+        // s[tk][tq][r] is key kv0 + 32*(tk/2) + 8g + 4*(tk%2) + r
         if (tail) {
 #pragma unroll
             for (int tk = 0; tk < 4; ++tk)
@@ -168,7 +173,7 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
                 for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (kv0 + tk * 16 + 4 * g + r >= S) s[tk][tq][r] = -INFINITY;
+                        if (kv0 + 32 * (tk >> 1) + 8 * g + 4 * (tk & 1) + r >= S) s[tk][tq][r] = -INFINITY;
         }
         float mt[2];
 #pragma unroll
@@ -217,12 +222,8 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
                 rsum[tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[j][tq], rsum[tq], 0, 0, 0);
 #pragma unroll
             for (int dd = 0; dd < 8; ++dd) {
-                const int d = dd * 16 + l16;
-                const u32x2 *L2 = reinterpret_cast<const u32x2 *>(L);
-                const u32x2 lo = L2[2 * vidx(d, 4 * j + (g >> 1)) + (g & 1)];
-                const u32x2 hi = L2[2 * vidx(d, 4 * j + 2 + (g >> 1)) + (g & 1)];
-                const u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
+                // keys 32j + 8g .. +7 of value row d: one 16-byte chunk
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, L[vidx(dd * 16 + l16, 4 * j + g)]);
 #pragma unroll
                 for (int tq = 0; tq < 2; ++tq)
                     oacc[dd][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[j][tq], oacc[dd][tq], 0, 0, 0);

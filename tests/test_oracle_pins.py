@@ -17,6 +17,24 @@ import oracle as O
 from diffusion_transformer_amd import synth
 
 
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    """key = value fixture (values: space-separated numbers); '#' lines cite
+    the passage the values come from."""
+    out = {}
+    with open(__import__("os").path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = (t.strip() for t in line.split("=", 1))
+            vals = [float(t) for t in v.split()]
+            out[k] = vals[0] if len(vals) == 1 else vals
+    return out
+
+
 # ---------------------------------------------------------------- positions
 
 def test_positions_printed_example_h16():
@@ -28,6 +46,18 @@ def test_positions_printed_example_h16():
     assert img[:, 2].min() == -8 and img[:, 2].max() == 7
     assert (img[:, 0] == L).all()                       # frame coordinate = L
     assert sorted(set(img[:, 1].tolist())) == list(range(-8, 8))
+
+
+def test_positions_golden_fixture():
+    g = _golden("positions_h16.txt")
+    L, h, w = int(g["L"]), int(g["h"]), int(g["w"])
+    pos = O.positions(L, h, w)
+    img = pos[L:].reshape(h, w, 3)
+    assert img[:, 0, 1].tolist() == [int(v) for v in g["rows"]]      # row coordinate down a column
+    assert img[0, :, 2].tolist() == [int(v) for v in g["cols"]]      # column coordinate along a row
+    assert (img[..., 0] == int(g["frame"])).all()
+    assert pos[0].tolist() == [int(v) for v in g["text_0"]]
+    assert pos[4].tolist() == [int(v) for v in g["text_4"]]
 
 
 def test_positions_text_and_raster_order():
@@ -454,6 +484,19 @@ def test_block_flops_config_north_star():
     arch = O.Arch(3072, 24, 128, 12288)
     f = O.block_flops(4608, arch)
     assert abs(f / 1e9 - 1652.6) < 0.1
+
+
+def test_attention_cost_golden_fixture():
+    # The quadratic (attention) share of the oracle's FLOP count, read off as
+    # a second difference in S, against the figure printed for this shape;
+    # and the size of the naive fp32 score tensor printed beside it.
+    g = _golden("attention_cost_4608.txt")
+    H, S, d = int(g["heads"]), int(g["rows"]), int(g["head_dim"])
+    arch = O.Arch(H * d, H, d, 4 * H * d)
+    f = lambda n: O.block_flops(n, arch)
+    quad = (f(S + 1) - 2 * f(S) + f(S - 1)) // 2          # coefficient of S^2
+    assert round(quad * S * S / 1e12, 2) == g["attention_tflop"]
+    assert round(H * S * S * 4 / 1e9, 2) == g["scores_fp32_gb"]
 
 
 # ---------------------------------------------------------------- planted mistakes
