@@ -103,6 +103,7 @@ def summarize_counters(fetch_csv, write_csv, out_json):
     gated-residual product apart."""
     import csv
     import collections
+    import re
 
     def load(path, counter):
         per = collections.defaultdict(float)
@@ -125,13 +126,15 @@ def summarize_counters(fetch_csv, write_csv, out_json):
         pending = None
         for d in order:
             n = names[d]
-            if "k_gemm_pp<3>" in n or "k_gemm<256, 256, false, 3>" in n:
+            epi = re.search(r"k_gemm_pp<(\d)", n) or re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
+            epi = int(epi.group(1)) if epi else None
+            if epi == 3:
                 stage_of[d] = "qkv"
             elif "k_attention" in n:
                 stage_of[d] = "attn"
-            elif "k_gemm_pp<2>" in n or "k_gemm<256, 256, false, 2>" in n:
+            elif epi == 2:
                 stage_of[d] = "up"
-            elif "k_gemm_pp<1>" in n or "k_gemm<256, 256, false, 1>" in n:
+            elif epi == 1:
                 stage_of[d] = "down" if pending == "up" else "out"
             elif "k_gemv" in n:
                 stage_of[d] = "mod"

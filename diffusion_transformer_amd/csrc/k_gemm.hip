@@ -372,16 +372,29 @@ __device__ __forceinline__ void wait_vm0_after(float dep) {
     asm volatile("s_waitcnt vmcnt(0)" ::"v"(dep) : "memory");
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm20() { asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// 16 bytes per lane global -> LDS (the LDS slot is the wave's base plus
+// lane*16).  `base` is wave-uniform and `off_bytes` a 32-bit lane offset, so
+// the load takes the scalar-base addressing form.
+__device__ __forceinline__ void dma16(const uint16_t *base, uint32_t off_bytes, u32x4 *l) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(base) + off_bytes, (lds_void_t *)l, 16, 0, 0);
+}
+// 4 bytes per lane global -> a scratch LDS word: only to pull the line
+// into L2 ahead of its real load.
+__device__ __forceinline__ void touch4(const uint16_t *base, uint32_t off_bytes, u32x4 *l) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(base) + off_bytes, (lds_void_t *)l, 4, 0, 0);
+}
 }  // namespace
 
-template <int EPI>
+template <int EPI, bool PF>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
           GemmEpi ep) {
     constexpr int BM = PP_BM, BN = PP_BN;
-    __shared__ u32x4 lds[2 * PP_STAGE];
+    __shared__ u32x4 lds[2 * PP_STAGE + 16];   // + 256 bytes: the prefetch sink
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = wave >> 2, wg = wave & 3;     // group 0: waves 0-3, group 1: waves 4-7
@@ -411,27 +424,28 @@ k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     const int lrow = lane >> 3, lpos = lane & 7;
     const int cE = lpos ^ ((lrow >> 1) & 7), cO = cE ^ 4;
     const uint16_t *a_base = A + static_cast<int64_t>(m0) * K;
-    const int a_offE = (64 * wg + lrow) * K + cE * 8, a_offO = (64 * wg + lrow) * K + cO * 8;
+    const uint32_t a_offE = 2u * ((64 * wg + lrow) * K + cE * 8), a_offO = 2u * ((64 * wg + lrow) * K + cO * 8);
     // W row of slot 64wg + 8i + lrow: even rows fill slots 0..127, odd rows 128..255
     const int n_of0 = wg < 2 ? 2 * (64 * wg + lrow) : 2 * (64 * wg - 128 + lrow) + 1;
     const uint16_t *w_base = W + static_cast<int64_t>(n0) * K;
-    const int w_offE = n_of0 * K + cE * 8, w_offO = n_of0 * K + cO * 8;
-    auto issue_tile = [&](int t, int buf) {
+    const uint32_t w_offE = 2u * (n_of0 * K + cE * 8), w_offO = 2u * (n_of0 * K + cO * 8);
+    // A k-tile is 16 wave-instructions per wave of one group: 8 for A's 256
+    // rows and 8 for W's.  issue_a / issue_w each put one half in flight.
+    auto issue_a = [&](int t, int buf) {
         u32x4 *L = lds + buf * PP_STAGE;
         const uint16_t *ab = a_base + t * BK;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma16(ab + i * 8 * K, i & 1 ? a_offO : a_offE, L + (wg * 8 + i) * 64);
+    };
+    auto issue_w = [&](int t, int buf) {
+        u32x4 *L = lds + buf * PP_STAGE;
         const uint16_t *wb = w_base + t * BK;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = wg * 8 + i;
-            __builtin_amdgcn_global_load_lds(ab + (i & 1 ? a_offO : a_offE) + i * 8 * K,
-                                             (lds_void_t *)(L + j * 64), 16, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = wg * 8 + i;
-            __builtin_amdgcn_global_load_lds(wb + (i & 1 ? w_offO : w_offE) + i * 16 * K,
-                                             (lds_void_t *)(L + BM * 8 + j * 64), 16, 0, 0);
-        }
+        for (int i = 0; i < 8; ++i) dma16(wb + i * 16 * K, i & 1 ? w_offO : w_offE, L + BM * 8 + (wg * 8 + i) * 64);
+    };
+    auto issue_tile = [&](int t, int buf) {
+        issue_a(t, buf);
+        issue_w(t, buf);
     };
 
     // LDS fragment addresses.  Every A slot this lane reads is
@@ -474,12 +488,30 @@ k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
                     acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
     };
 
+    // L2 prefetch (PF, for long reductions): with every k-tile load, group 0
+    // also touches the 128-byte line of each of the 512 rows of k-tile t+2
+    // beyond it (two 4-byte loads per lane, clamped to the last tile), so the
+    // real load two phases later hits L2.  Each issue is followed by exactly
+    // two touches, so the waits below keep fixed counts.  For short
+    // reductions the extra requests cost more than the misses they save.
+    const uint32_t pf_off = 2u * static_cast<uint32_t>((64 * wg + lane) * K);
+    auto prefetch = [&](int t) {
+        if constexpr (PF) {
+            const int tt = t < T ? t : T - 1;
+            touch4(a_base + tt * BK, pf_off, lds + 2 * PP_STAGE);
+            touch4(w_base + tt * BK, pf_off, lds + 2 * PP_STAGE);
+        }
+    };
+
     // prologue: k-tiles 0 and 1 into LDS; group 0 takes the fragments of 0
     if (grp == 0) {
         issue_tile(0, 0);
+        prefetch(2);
         if (T > 1) {
             issue_tile(1, 1);
-            wait_vm16();
+            prefetch(3);
+            if constexpr (PF) wait_vm20();
+            else wait_vm16();
         } else {
             wait_vm0();
         }
@@ -491,29 +523,47 @@ k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     }
     pp_barrier();
 
+    // Main loop.  One vector-memory instruction moves 1 KB, and a CU takes
+    // about as long to move a 64 KB k-tile into LDS as to run a phase of
+    // MFMAs, so the k-tile's loads are split between the two fragment
+    // phases: each group, right after reading its fragments of a buffer,
+    // refills the buffer that both groups have finished reading with its
+    // half of k-tile t+2 (group 1 the A rows, group 0 the W rows).  A group
+    // waits for its own half before the barrier that precedes the first read
+    // of that tile.
     for (int t = 0; t < T; ++t) {
-        // phase 2t
+        // phase 2t: group 0 computes k-tile t; group 1 reads its fragments of
+        // t (buffer t&1, which group 0 read in phase 2t-1), then sends the A
+        // half of t+2 into that buffer
         if (grp == 0) {
             compute();
             __builtin_amdgcn_sched_barrier(0);       // after all of this phase's MFMAs:
-            wait_vm0();                              // k-tile t+1 has landed
+            if constexpr (PF) wait_vm2();            // its W half of t+1 has landed
+            else wait_vm0();
         } else {
             load_frags(t & 1);
             wait_lgkm0();
+            wait_vm0();                              // its A half of t+1 has landed
+            if (t + 2 < T) issue_a(t + 2, t & 1);
         }
         pp_barrier();
-        // phase 2t+1
+        // phase 2t+1: group 0 reads its fragments of t+1, then sends the W
+        // half of t+2; group 1 computes t
         if (grp == 0) {
-            if (t + 2 < T) issue_tile(t + 2, t & 1);
             if (t + 1 < T) {
                 load_frags((t + 1) & 1);
                 wait_lgkm0();
+            }
+            if (t + 2 < T) {
+                issue_w(t + 2, t & 1);
+                prefetch(t + 4);
             }
         } else {
             compute();
         }
         pp_barrier();
     }
+    wait_vm0();   // no load into LDS may be in flight when the block ends
 
     gemm_epilogue<EPI, TM>(acc, m0, n0, wm, wn, lane, M, N, ep);
 }
@@ -546,7 +596,10 @@ template <int EPI>
 static hipError_t launch_pp(const uint16_t *A, const uint16_t *W, int M, int N, int K, const GemmEpi &ep,
                             hipStream_t st) {
     const int grid = static_cast<int>(cdiv(M, PP_BM) * cdiv(N, PP_BN));
-    k_gemm_pp<EPI><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
+    if (K >= 8192)
+        k_gemm_pp<EPI, true><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
+    else
+        k_gemm_pp<EPI, false><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
     return hipGetLastError();
 }
 
