@@ -389,6 +389,170 @@ __device__ __forceinline__ void touch4(const uint16_t *base, uint32_t off_bytes,
 }
 }  // namespace
 
+// Epilogue of the 256x256 ping-pong product, staged through the (then idle)
+// LDS so that global memory sees 16-byte accesses: a lane's accumulators
+// hold 4 rows of one column pair, which would otherwise leave as 2-, 4- or
+// 8-byte pieces.  Wave (wm, wn) holds rows wm*64 + tm*16 + 4*(lane>>4) + r
+// and column pairs (2P, 2P+1), P = wn*64 + tp*16 + (lane&15), of the tile.
+// All 512 threads take part; LDS must be free (no loads in flight).
+//  - SWIGLU: bf16 [256][128] tile, 256-byte rows, 16-byte chunks swizzled
+//    by chunk ^ (row & 15);
+//  - F32 / GATE_RES / QKV (q, k): fp32 [128][256] half tiles, 1 KB rows,
+//    16-byte chunks swizzled by chunk ^ (((row >> 2) & 1) << 3); rows
+//    0-127 are written by waves wm = 0, 1, rows 128-255 by wm = 2, 3.
+//  - QKV values (v): written straight from the accumulators (four
+//    consecutive rows of one feature are 8 contiguous bytes of vt).
+template <int EPI>
+__device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, int m0, int n0, int wm, int wn,
+                                            int lane, int tid, int M, int N, const GemmEpi &ep) {
+    const int pl = lane & 15, g = lane >> 4;
+    char *L = reinterpret_cast<char *>(lds);
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * 64 + tm * 16 + 4 * g + r;
+#pragma unroll
+                for (int tp = 0; tp < TN / 2; ++tp) {
+                    const int col = wn * 64 + tp * 16 + pl;          // output column 0..127
+                    const float gt = acc[tm][tp][r], up = acc[tm][tp + TN / 2][r];
+                    const int off = row * 256 + (((col >> 3) ^ (row & 15)) << 4) + ((col & 7) << 1);
+                    *reinterpret_cast<uint16_t *>(L + off) = f32_to_bf16(silu_f(gt) * up);
+                }
+            }
+        wait_lgkm0();
+        pp_barrier();
+        const int half = N / 2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = tid + 512 * i, row = q >> 4, c = q & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(L + row * 256 + ((c ^ (row & 15)) << 4));
+            if (m0 + row < M)
+                *reinterpret_cast<u32x4 *>(ep.act + static_cast<int64_t>(m0 + row) * half + n0 / 2 + c * 8) = v;
+        }
+    } else {
+        // QKV: the tile's two heads share a region (q, k or v) when the
+        // region width heads*128 is a multiple of 256 (checked at launch)
+        int region = 0;
+        float rs[TM][4];
+        if constexpr (EPI == EPI_QKV) {
+            region = (n0 / 128) / ep.heads;
+            if (region == 2) {
+                const int head = (n0 / 128) % ep.heads + wn;
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const int row0 = m0 + wm * 64 + tm * 16 + 4 * g;
+                    if (row0 >= ep.ldv) continue;
+#pragma unroll
+                    for (int tp = 0; tp < TN / 2; ++tp) {
+                        const int p = tp * 16 + pl;
+                        uint16_t *d0 = ep.vt + (static_cast<int64_t>(head) * 128 + 2 * p) * ep.ldv + row0;
+                        const f32x4 e = acc[tm][tp], o = acc[tm][tp + TN / 2];
+                        *reinterpret_cast<u32x2 *>(d0) = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
+                        *reinterpret_cast<u32x2 *>(d0 + ep.ldv) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                    }
+                }
+                return;
+            }
+            // per-row 1/rms over the wave's 128 columns (one head): the 16
+            // lanes with equal lane>>4 share a row
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int tp = 0; tp < TN / 2; ++tp) {
+                        const float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
+                        ss += e * e + o * o;
+                    }
+                    ss += __shfl_xor(ss, 1, 64);
+                    ss += __shfl_xor(ss, 2, 64);
+                    ss += __shfl_xor(ss, 4, 64);
+                    ss += __shfl_xor(ss, 8, 64);
+                    rs[tm][r] = rsqrtf(ss * (1.0f / 128.0f) + ep.qk_eps);
+                }
+        }
+        float2 wq[TN / 2];
+        if constexpr (EPI == EPI_QKV) {
+            const float *nw = region == 0 ? ep.qn : ep.kn;
+#pragma unroll
+            for (int tp = 0; tp < TN / 2; ++tp) wq[tp] = *reinterpret_cast<const float2 *>(nw + 2 * (tp * 16 + pl));
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            if (hf) pp_barrier();                    // half 0 has been read
+            if ((wm >> 1) == hf) {
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = (wm & 1) * 64 + tm * 16 + 4 * g + r;   // 0..127 in the half
+#pragma unroll
+                        for (int tp = 0; tp < TN / 2; ++tp) {
+                            const int col = wn * 128 + 2 * (tp * 16 + pl);     // even column 0..254
+                            float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
+                            if constexpr (EPI == EPI_QKV) {
+                                e = e * rs[tm][r] * wq[tp].x;
+                                o = o * rs[tm][r] * wq[tp].y;
+                            }
+                            const int off = row * 1024 + ((((col >> 2) ^ (((row >> 2) & 1) << 3))) << 4) + ((col & 3) << 2);
+                            *reinterpret_cast<float2 *>(L + off) = make_float2(e, o);
+                        }
+                    }
+            }
+            wait_lgkm0();
+            pp_barrier();
+            if constexpr (EPI == EPI_QKV) {
+                // thread -> 8 consecutive columns (4 rotation pairs) of one row
+                const int cg = tid & 31;
+                const int head = (n0 / 128) % ep.heads + (cg >> 4);
+                uint16_t *dst = region == 0 ? ep.q : ep.k;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int row = (tid >> 5) + 16 * i, grow = m0 + hf * 128 + row;
+                    if (grow >= M) continue;
+                    const int sw = ((row >> 2) & 1) << 3;
+                    const f32x4 v0 = *reinterpret_cast<const f32x4 *>(L + row * 1024 + (((2 * cg) ^ sw) << 4));
+                    const f32x4 v1 = *reinterpret_cast<const f32x4 *>(L + row * 1024 + (((2 * cg + 1) ^ sw) << 4));
+                    const int p0 = 4 * (cg & 15);
+                    const f32x4 cs = *reinterpret_cast<const f32x4 *>(ep.cos + static_cast<int64_t>(grow) * 64 + p0);
+                    const f32x4 sn = *reinterpret_cast<const f32x4 *>(ep.sin + static_cast<int64_t>(grow) * 64 + p0);
+                    const u32x4 o = {pack_bf16x2(v0[0] * cs[0] - v0[1] * sn[0], v0[0] * sn[0] + v0[1] * cs[0]),
+                                     pack_bf16x2(v0[2] * cs[1] - v0[3] * sn[1], v0[2] * sn[1] + v0[3] * cs[1]),
+                                     pack_bf16x2(v1[0] * cs[2] - v1[1] * sn[2], v1[0] * sn[2] + v1[1] * cs[2]),
+                                     pack_bf16x2(v1[2] * cs[3] - v1[3] * sn[3], v1[2] * sn[3] + v1[3] * cs[3])};
+                    *reinterpret_cast<u32x4 *>(dst + (static_cast<int64_t>(head) * M + grow) * 128 + 2 * p0) = o;
+                }
+            } else {
+                // thread -> 4 consecutive columns, rows tid/64 + 8i: one gate chunk
+                const int cc = tid & 63;
+                f32x4 gt = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (EPI == EPI_GATE_RES) gt = *reinterpret_cast<const f32x4 *>(ep.gate + n0 + 4 * cc);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = (tid >> 6) + 8 * i, grow = m0 + hf * 128 + row;
+                    if (grow >= M) continue;
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(
+                        L + row * 1024 + ((cc ^ (((row >> 2) & 1) << 3)) << 4));
+                    f32x4 *dst = reinterpret_cast<f32x4 *>(ep.out + static_cast<int64_t>(grow) * ep.ldo + n0 + 4 * cc);
+                    if constexpr (EPI == EPI_F32) {
+                        *dst = v;
+                    } else {
+                        f32x4 x = *dst;
+                        x[0] += gt[0] * v[0];
+                        x[1] += gt[1] * v[1];
+                        x[2] += gt[2] * v[2];
+                        x[3] += gt[3] * v[3];
+                        *dst = x;
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int EPI, bool PF>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
@@ -564,8 +728,9 @@ k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
         pp_barrier();
     }
     wait_vm0();   // no load into LDS may be in flight when the block ends
+    pp_barrier();
 
-    gemm_epilogue<EPI, TM>(acc, m0, n0, wm, wn, lane, M, N, ep);
+    pp_epilogue<EPI>(acc, lds, m0, n0, wm, wn, lane, tid, M, N, ep);
 }
 
 template <int BM, int BN, bool W8>
@@ -610,7 +775,18 @@ hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Ws, boo
     // A's allocation covers whole 256-row tiles and N is a multiple of 256).
     // Small ones: 128x128 (2 waves) so the grid still spreads over the chip.
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
-    if (big_tiles >= 128 && !w8 && N % 256 == 0 && (a_rows_padded || M % 256 == 0)) {
+    // the ping-pong kernel's staged epilogue moves 16-byte pieces and keeps
+    // the two heads of a QKV tile in one region
+    auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    bool epi_ok = false;
+    switch (ep.kind) {
+        case EPI_F32: epi_ok = al16(ep.out) && ep.ldo % 4 == 0; break;
+        case EPI_GATE_RES: epi_ok = al16(ep.out) && ep.ldo % 4 == 0 && al16(ep.gate); break;
+        case EPI_SWIGLU: epi_ok = al16(ep.act); break;
+        case EPI_QKV: epi_ok = ep.heads % 2 == 0 && al16(ep.q) && al16(ep.k) && al16(ep.cos) && al16(ep.sin); break;
+        default: break;
+    }
+    if (big_tiles >= 128 && !w8 && epi_ok && K >= 128 && N % 256 == 0 && (a_rows_padded || M % 256 == 0)) {
         const uint16_t *Wb = static_cast<const uint16_t *>(W);
         switch (ep.kind) {
             case EPI_F32: return launch_pp<EPI_F32>(A, Wb, M, N, K, ep, st);
