@@ -26,6 +26,11 @@
 //    (it sums the same bf16-rounded P the values are weighted with);
 //    the running maximum is rescaled lazily: only when a tile's maximum
 //    exceeds it by more than 2^8 (exponents stay <= 2^8, exact either way).
+//  - the exponentials are the vector-unit bottleneck, so the softmax is
+//    trimmed to them: queries are pre-multiplied by log2(e)/sqrt(128) and the
+//    score MFMAs start from minus the running maximum, so p = 2^score needs
+//    no separate scale-and-subtract; the maxima use three-input max and
+//    lane-row swaps.
 //  - blocks are remapped so that each XCD (own L2) serves whole heads.
 #include "common.h"
 #include "kernels.h"
@@ -47,6 +52,20 @@ __device__ __forceinline__ int kidx(int row, int c) { return row * 16 + (c ^ (ro
 __device__ __forceinline__ int vidx(int d, int c) { return K_U4 + d * 8 + (c ^ ((d >> 1) & 7)); }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// max with the lane 16 (32) positions away, through the gfx950 row-swap
+// permutes (no LDS round trip): swapping a value with itself leaves each
+// lane holding its own value in one result and its partner's in the other
+__device__ __forceinline__ float fmax_xor16(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float fmax_xor32(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
 
 __device__ __forceinline__ void g2l16(const void *g, u32x4 *l) {
     __builtin_amdgcn_global_load_lds(g, (lds_void *)(l), 16, 0, 0);
@@ -76,15 +95,23 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     const uint16_t *Kh = Kg + static_cast<int64_t>(h) * S * HD;
     const uint16_t *Vh = Vt + static_cast<int64_t>(h) * HD * ldv;
 
-    // queries of this lane as B operands: [tq][kstep over d]
+    // queries of this lane as B operands: [tq][kstep over d], multiplied by
+    // log2(e)/sqrt(128) (and rounded to bf16 again) so that the scores come
+    // out of the MFMAs in base-2 exponent units
+    const float sc = 0.08838834764831845f * 1.4426950408889634f;
     bf16x8 qf[2][4];
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
         const int qr = min(q0 + tq * 16 + l16, S - 1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qf[tq][ks] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(Qh + static_cast<int64_t>(qr) * HD + ks * 32 + g * 8));
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(Qh + static_cast<int64_t>(qr) * HD + ks * 32 + g * 8);
+            const u32x4 u = {pack_bf16x2(bf16lo_to_f32(w[0]) * sc, bf16hi_to_f32(w[0]) * sc),
+                             pack_bf16x2(bf16lo_to_f32(w[1]) * sc, bf16hi_to_f32(w[1]) * sc),
+                             pack_bf16x2(bf16lo_to_f32(w[2]) * sc, bf16hi_to_f32(w[2]) * sc),
+                             pack_bf16x2(bf16lo_to_f32(w[3]) * sc, bf16hi_to_f32(w[3]) * sc)};
+            qf[tq][ks] = __builtin_bit_cast(bf16x8, u);
+        }
     }
 
     const int ntiles = (S + KT - 1) / KT;
@@ -117,8 +144,11 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 #pragma unroll
         for (int j = 0; j < 2; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     rsum[0] = rsum[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mrun[2] = {-INFINITY, -INFINITY};
-    const float sc = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
+    // running maximum (base-2 units) per query; the score MFMAs start from
+    // -mb, so the scores arrive with it already subtracted.  mb = 0 and
+    // started = false until the first tile has set it.
+    float mb[2] = {0.f, 0.f};
+    bool started = false;
     const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
     const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_u);
 
@@ -149,10 +179,7 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 
         // ---- S^T = K Q^T for 64 keys x 32 queries (raw scores)
         f32x4 s[4][2];
-#pragma unroll
-        for (int tk = 0; tk < 4; ++tk)
-#pragma unroll
-            for (int tq = 0; tq < 2; ++tq) s[tk][tq] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 init[2] = {f32x4{-mb[0], -mb[0], -mb[0], -mb[0]}, f32x4{-mb[1], -mb[1], -mb[1], -mb[1]}};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -160,12 +187,16 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
                 const bf16x8 kf = __builtin_bit_cast(bf16x8, L[kidx(tk * 16 + l16, ks * 4 + g)]);
 #pragma unroll
                 for (int tq = 0; tq < 2; ++tq)
-                    s[tk][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[tq][ks], s[tk][tq], 0, 0, 0);
+                    s[tk][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[tq][ks], ks == 0 ? init[tq] : s[tk][tq], 0, 0, 0);
             }
         }
 
-        // ---- online softmax per query column (lane); the score in
-        // s[tk][tq][r] is key kv0 + 32*(tk/2) + 8g + 4*(tk%2) + r
+        // ---- online softmax per query column (lane): s[tk][tq][r] holds
+        // x = score * log2(e)/sqrt(128) - mb for key kv0 + 32*(tk/2) + 8g +
+        // 4*(tk%2) + r.  Common case: the tile's maximum of x is <= 2^8 above
+        // the running maximum and p = 2^x needs no subtraction.  Otherwise
+        // (and for the first tile) the maximum moves up by the tile's max m:
+        // the partial output and sums are scaled by 2^-m and p = 2^(x - m).
         if (tail) {
 #pragma unroll
             for (int tk = 0; tk < 4; ++tk)
@@ -178,38 +209,39 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
         float mt[2];
 #pragma unroll
         for (int tq = 0; tq < 2; ++tq) {
-            float mx = s[0][tq][0];
+            float m0 = fmaxf(s[0][tq][0], s[0][tq][1]), m1 = fmaxf(s[0][tq][2], s[0][tq][3]);
 #pragma unroll
-            for (int tk = 0; tk < 4; ++tk)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tk][tq][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            mt[tq] = mx * sc;
+            for (int tk = 1; tk < 4; ++tk) {
+                m0 = fmaxf(fmaxf(m0, s[tk][tq][0]), s[tk][tq][1]);   // v_max3
+                m1 = fmaxf(fmaxf(m1, s[tk][tq][2]), s[tk][tq][3]);
+            }
+            mt[tq] = fmax_xor32(fmax_xor16(fmaxf(m0, m1)));
         }
-        const bool grow = (mt[0] > mrun[0] + kLazy) || (mt[1] > mrun[1] + kLazy);
+        const bool grow = !started || mt[0] > kLazy || mt[1] > kLazy;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
             for (int tq = 0; tq < 2; ++tq) {
-                const float mnew = fmaxf(mrun[tq], mt[tq]);
-                const float alpha = exp2f(mrun[tq] - mnew);
-                mrun[tq] = mnew;
+                const float m = mt[tq];
+                const float alpha = __builtin_amdgcn_exp2f(-m);
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd) oacc[dd][tq] *= alpha;
                 rsum[tq] *= alpha;
+                mb[tq] += m;
+#pragma unroll
+                for (int tk = 0; tk < 4; ++tk) s[tk][tq] -= m;
             }
+            started = true;
         }
         bf16x8 pf[2][2];
 #pragma unroll
         for (int tq = 0; tq < 2; ++tq) {
-            const float nm = -mrun[tq];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const f32x4 a = s[2 * j][tq], b = s[2 * j + 1][tq];
-                u32x4 u = {pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(a[0], sc, nm)), __builtin_amdgcn_exp2f(fmaf(a[1], sc, nm))),
-                           pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(a[2], sc, nm)), __builtin_amdgcn_exp2f(fmaf(a[3], sc, nm))),
-                           pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(b[0], sc, nm)), __builtin_amdgcn_exp2f(fmaf(b[1], sc, nm))),
-                           pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(b[2], sc, nm)), __builtin_amdgcn_exp2f(fmaf(b[3], sc, nm)))};
+                u32x4 u = {pack_bf16x2(__builtin_amdgcn_exp2f(a[0]), __builtin_amdgcn_exp2f(a[1])),
+                           pack_bf16x2(__builtin_amdgcn_exp2f(a[2]), __builtin_amdgcn_exp2f(a[3])),
+                           pack_bf16x2(__builtin_amdgcn_exp2f(b[0]), __builtin_amdgcn_exp2f(b[1])),
+                           pack_bf16x2(__builtin_amdgcn_exp2f(b[2]), __builtin_amdgcn_exp2f(b[3]))};
                 pf[j][tq] = __builtin_bit_cast(bf16x8, u);
             }
         }
