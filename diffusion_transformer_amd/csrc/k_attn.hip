@@ -116,26 +116,27 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 
     const int ntiles = (S + KT - 1) / KT;
     // direct global -> LDS: wave instruction i writes 1 KB = 4 K rows or 8 V^T rows
-    auto issue_tile = [&](int t, int buf) {
+    // load i (0..7) of tile t: i < 4 the K rows, else the V^T rows
+    auto issue_one = [&](int t, int buf, int i) {
         const int kv0 = t * KT;
         u32x4 *L = lds + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int blk = wave * 4 + i;                 // 0..15
+        const int blk = wave * 4 + (i & 3);               // 0..15
+        if (i < 4) {
             const int r = blk * 4 + (lane >> 4);          // LDS K row 0..63
             const int c = (lane & 15) ^ (r & 15);         // global chunk for LDS position lane&15
             const int rr = r & 31;
             const int kk = (r & 32) + 8 * ((rr & 15) >> 2) + 4 * (rr >> 4) + (rr & 3);   // kappa
             const int key = min(kv0 + kk, S - 1);
             g2l16(Kh + static_cast<int64_t>(key) * HD + c * 8, L + blk * 64);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int blk = wave * 4 + i;                 // 0..15
+        } else {
             const int d = blk * 8 + (lane >> 3);          // V^T row 0..127
             const int c = (lane & 7) ^ ((d >> 1) & 7);
             g2l16(Vh + static_cast<int64_t>(d) * ldv + kv0 + c * 8, L + K_U4 + blk * 64);
         }
+    };
+    auto issue_tile = [&](int t, int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) issue_one(t, buf, i);
     };
 
     f32x4 oacc[8][2], rsum[2];
@@ -174,20 +175,28 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
             }
             __syncthreads();
         }
-        if (t + 1 < ntiles) issue_tile(t + 1, cur ^ 1);
         const u32x4 *L = lds + cur * STAGE;
 
-        // ---- S^T = K Q^T for 64 keys x 32 queries (raw scores)
+        // ---- S^T = K Q^T for 64 keys x 32 queries (raw scores), with the
+        // next tile's 8 loads into LDS spread between the MFMAs: issued in a
+        // row they stall the wave on the vector-memory queue.  The last tile
+        // loads itself again (into the idle buffer) to keep one code path.
+        const int tn = min(t + 1, ntiles - 1);
         f32x4 s[4][2];
         const f32x4 init[2] = {f32x4{-mb[0], -mb[0], -mb[0], -mb[0]}, f32x4{-mb[1], -mb[1], -mb[1], -mb[1]}};
+        bf16x8 kf[4][4];                                   // all K fragments first (LDS reads
+#pragma unroll                                            // may not pass the loads into LDS)
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int tk = 0; tk < 4; ++tk) kf[ks][tk] = __builtin_bit_cast(bf16x8, L[kidx(tk * 16 + l16, ks * 4 + g)]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
             for (int tk = 0; tk < 4; ++tk) {
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, L[kidx(tk * 16 + l16, ks * 4 + g)]);
+                if ((tk & 1) == 0) issue_one(tn, cur ^ 1, ks * 2 + (tk >> 1));
 #pragma unroll
                 for (int tq = 0; tq < 2; ++tq)
-                    s[tk][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[tq][ks], ks == 0 ? init[tq] : s[tk][tq], 0, 0, 0);
+                    s[tk][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tk], qf[tq][ks], ks == 0 ? init[tq] : s[tk][tq], 0, 0, 0);
             }
         }
 
