@@ -12,18 +12,22 @@
 //                 weight, then the adjacent-pair rotation with cos/sin[r];
 //                 bf16 to q, k [H, M, 128]; V heads to vt [H, 128, ldv]
 //
-// Design (CDNA4): block tile BM x BN x 64, wave tile 64 x 128 (4 x 8 MFMA
-// 16x16x32 bf16 sub-tiles), fp32 accumulators in registers, LDS double
-// buffer with register staging of the next k-tile.  LDS rows are 128 bytes
+// Design (CDNA4): wave tile 64 x 128 (4 x 8 MFMA 16x16x32 bf16 sub-tiles),
+// fp32 accumulators in registers, k-tiles of 64.  LDS rows are 128 bytes
 // (64 bf16 of K) in 16-byte chunks placed at chunk ^ ((slot >> 1) & 7), which
 // keeps both the 16-byte writes and the MFMA operand reads free of bank
 // conflicts on the 64-bank LDS.  W rows are de-interleaved into LDS (even
 // rows first, then odd rows), so each lane ends up holding output columns
 // 2p and 2p+1 in two accumulators: the rotary pairs and the SwiGLU
-// (gate, up) pairs meet in one lane without shuffles.  int8 weights are
-// dequantised (code * scale, rounded to bf16) on the way into LDS, once per
-// block.  Blocks are remapped so that each XCD works on a compact group of
-// tiles (its own L2), in groups of 8 row-tiles.
+// (gate, up) pairs meet in one lane without shuffles.  Blocks are remapped
+// so that each XCD works on a compact group of tiles (its own L2), in groups
+// of 8 row-tiles.  Two kernels:
+//  - k_gemm_p3, bf16 weights, 256x256 tiles: a two-group ping-pong schedule
+//    with direct global -> LDS loads (below);
+//  - k_gemm, int8 weights and small or ragged shapes: 256x256 or 128x128
+//    tiles, LDS double buffer with register staging of the next k-tile;
+//    int8 weights are dequantised (code * scale, rounded to bf16) on the way
+//    into LDS, once per block.
 #include "common.h"
 #include "kernels.h"
 
@@ -347,46 +351,27 @@ k_gemm(const uint16_t *__restrict__ A, const void *__restrict__ Wv,
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant for bf16 weights: 256x256x64 tiles, 8 waves.  The two
-// waves of every SIMD alternate between a compute phase (64 MFMAs on
-// fragments already in registers) and a memory phase (LDS -> register
-// fragments for their next compute phase; wave group 0 also issues the
-// direct global -> LDS loads of the k-tile two steps ahead).  One workgroup
-// barrier ends every phase, so at any time one wave per SIMD feeds the
-// matrix core while the other waits on memory.
+// Ping-pong product for bf16 weights: 256x256x64 tiles, 8 waves in two groups
+// of four (one wave of each group per SIMD).  The two waves of every SIMD
+// alternate between a compute phase (64 MFMAs on fragments already in
+// registers) and a memory phase (LDS -> register fragments for their next
+// compute phase, plus their share of the global -> LDS loads).  One
+// workgroup barrier ends every phase, so at any time one wave per SIMD feeds
+// the matrix core while the other works on memory:
 //
-//   phase 2t   : group 0 computes k-tile t     | group 1 loads fragments of t
-//   phase 2t+1 : group 0 loads fragments of t+1| group 1 computes k-tile t
-//                (and issues k-tile t+2 -> LDS buffer t&1)
+//   phase 2t   : group 0 computes k-tile t      | group 1 reads fragments of t
+//   phase 2t+1 : group 0 reads fragments of t+1 | group 1 computes k-tile t
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int PP_BM = 256, PP_BN = 256;
-constexpr int PP_STAGE = (PP_BM + PP_BN) * 8;   // u32x4 per LDS buffer (64 KB)
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Barriers and waits as volatile asm with a memory clobber (no LDS or
-// global access moves across them).  The end-of-compute wait takes an
-// accumulator as input so it cannot be hoisted above the phase's MFMAs.
+// global access moves across them).
 __device__ __forceinline__ void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_vm0_after(float dep) {
-    asm volatile("s_waitcnt vmcnt(0)" ::"v"(dep) : "memory");
-}
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm20() { asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// 16 bytes per lane global -> LDS (the LDS slot is the wave's base plus
-// lane*16).  `base` is wave-uniform and `off_bytes` a 32-bit lane offset, so
-// the load takes the scalar-base addressing form.
-__device__ __forceinline__ void dma16(const uint16_t *base, uint32_t off_bytes, u32x4 *l) {
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(base) + off_bytes, (lds_void_t *)l, 16, 0, 0);
-}
-// 4 bytes per lane global -> a scratch LDS word: only to pull the line
-// into L2 ahead of its real load.
-__device__ __forceinline__ void touch4(const uint16_t *base, uint32_t off_bytes, u32x4 *l) {
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(base) + off_bytes, (lds_void_t *)l, 4, 0, 0);
-}
 }  // namespace
 
 // Epilogue of the 256x256 ping-pong product, staged through the (then idle)
@@ -553,14 +538,50 @@ __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, in
     }
 }
 
-template <int EPI, bool PF>
+// ---------------------------------------------------------------------------
+// The loads.  A memory phase interleaves its global -> LDS loads with its
+// fragment reads (three 16-byte fragment reads, one 1 KB load, eight times)
+// instead of issuing them after the reads: the LDS read port and the load
+// path then work at the same time.  For that the
+// loads must go to buffers that nobody reads in that phase, which two 64 KB
+// buffers cannot give.  The LDS (160 KB) holds three A buffers and two W
+// buffers; A(t) is read by group 0 in phase 2t-1 and group 1 in phase 2t,
+// W's two 128-row halves separately (group 0 reads output columns 0-127 in
+// phase 2t-1, group 1 columns 128-255 in phase 2t):
+//   phase 2t   (group 1 reads t):   group 1 loads W half 0 and A rows 0-127
+//                                   of k-tile t+2;
+//   phase 2t+1 (group 0 reads t+1): group 0 loads W half 1 of t+2 and A
+//                                   rows 128-255 of t+3.
+// Every load has at least two phases to land, and every memory phase ends
+// with a wait for all but the loads issued in it.  Within a W half, even
+// rows fill the first 64 slots and odd rows the next 64, so a lane's
+// accumulators again hold output columns 2p and 2p+1.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int P3_NA = 3, P3_NW = 2;
+constexpr int P3_BUF = 256 * 8;   // u32x4 per buffer: 256 rows of 128 bytes
+// Raw buffer descriptor over [base, base + 2 GiB): no range clamping is
+// relied on, the loads stay inside the operands by construction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), 0x7fffffff, 0x00020000);
+}
+// 16 bytes per lane, buffer -> LDS (slot = the wave's base plus lane*16)
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, u32x4 *l) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)l, 16, voff, soff, 0, 0);
+}
+}  // namespace
+
+template <int EPI>
 __global__ void __launch_bounds__(512, 1)
-k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
+k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
           GemmEpi ep) {
     constexpr int BM = PP_BM, BN = PP_BN;
-    __shared__ u32x4 lds[2 * PP_STAGE + 16];   // + 256 bytes: the prefetch sink
+    __shared__ u32x4 lds[(P3_NA + P3_NW) * P3_BUF];   // 160 KB
+    u32x4 *const Abuf = lds;
+    u32x4 *const Wbuf = lds + P3_NA * P3_BUF;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6;
     const int grp = wave >> 2, wg = wave & 3;     // group 0: waves 0-3, group 1: waves 4-7
     const int wm = wg, wn = grp;                  // wave tile (wm*64, wn*128)
 
@@ -579,61 +600,78 @@ k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     const int m0 = tile_m * BM, n0 = tile_n * BN;
     const int T = K / BK;
 
-    // Group 0 issues whole k-tiles: 32 A and 32 B wave-instructions of 1 KB,
-    // 8 + 8 per wave; instruction i of wave wg writes LDS slots 64wg + 8i ..
-    // +7, lane -> slot 64wg + 8i + (lane>>3), chunk position lane&7.  The
-    // operands are read without row clamping: the caller guarantees A has
-    // a multiple of 256 rows allocated and N % 256 == 0.  The swizzled chunk
-    // (lane&7) ^ ((slot>>1)&7) only depends on the parity of i.
-    const int lrow = lane >> 3, lpos = lane & 7;
-    const int cE = lpos ^ ((lrow >> 1) & 7), cO = cE ^ 4;
-    const uint16_t *a_base = A + static_cast<int64_t>(m0) * K;
-    const uint32_t a_offE = 2u * ((64 * wg + lrow) * K + cE * 8), a_offO = 2u * ((64 * wg + lrow) * K + cO * 8);
-    // W row of slot 64wg + 8i + lrow: even rows fill slots 0..127, odd rows 128..255
-    const int n_of0 = wg < 2 ? 2 * (64 * wg + lrow) : 2 * (64 * wg - 128 + lrow) + 1;
-    const uint16_t *w_base = W + static_cast<int64_t>(n0) * K;
-    const uint32_t w_offE = 2u * (n_of0 * K + cE * 8), w_offO = 2u * (n_of0 * K + cO * 8);
-    // A k-tile is 16 wave-instructions per wave of one group: 8 for A's 256
-    // rows and 8 for W's.  issue_a / issue_w each put one half in flight.
-    auto issue_a = [&](int t, int buf) {
-        u32x4 *L = lds + buf * PP_STAGE;
-        const uint16_t *ab = a_base + t * BK;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dma16(ab + i * 8 * K, i & 1 ? a_offO : a_offE, L + (wg * 8 + i) * 64);
+    // Loads: a wave's instruction i (0..3) within a 128-row half writes the
+    // half's LDS slots 8(4wg + i) .. +7: lane -> slot 8(4wg + i) + (lane>>3),
+    // chunk position lane&7, which holds global chunk
+    // (lane&7) ^ (slot>>1 & 7) = (lane&7) ^ (lane>>4) ^ 4(i&1).
+    // The operands are read without row clamping: A has whole 256-row tiles
+    // allocated and N % 256 == 0.  Buffer loads keep the three address parts
+    // apart: the tile base in the descriptor, the lane's row and chunk in a
+    // 32-bit vector offset, the k-tile and the instruction's row step in a
+    // scalar offset.
+    const int lrow = lane >> 3;
+    const int cE = (lane & 7) ^ (lane >> 4), cO = cE ^ 4;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + static_cast<int64_t>(m0) * K);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(W + static_cast<int64_t>(n0) * K);
+    const int ah = grp ^ 1;                        // the A and W halves this group loads
+    // instruction i reads rows 8i (A) or 16i (W, de-interleaved) further
+    // down than instruction 0
+    const int wrow0 = 128 * ah + (wg < 2 ? 2 * (32 * wg + lrow) : 2 * (32 * wg - 64 + lrow) + 1);
+    const uint32_t a_offE = 2u * static_cast<uint32_t>((128 * ah + 32 * wg + lrow) * K + cE * 8);
+    const uint32_t a_offO = 2u * static_cast<uint32_t>((128 * ah + 32 * wg + lrow) * K + cO * 8);
+    const uint32_t w_offE = 2u * static_cast<uint32_t>(wrow0 * K + cE * 8);
+    const uint32_t w_offO = 2u * static_cast<uint32_t>(wrow0 * K + cO * 8);
+    // load i (0..3) of the W half or the A half this group loads (half
+    // grp ^ 1 of both), of k-tile kt.  Past the last k-tile the source is
+    // clamped to it: those loads land in a buffer nobody reads any more, and
+    // every memory phase issues the same number of loads.
+    auto issue_w = [&](int kt, int i) {
+        const int ks = min(kt, T - 1);
+        bdma16(rW, (i & 1) ? w_offO : w_offE, 2u * static_cast<uint32_t>(ks * BK + i * 16 * K),
+               Wbuf + (kt & 1) * P3_BUF + (128 * ah + 8 * (4 * wg + i)) * 8);
     };
-    auto issue_w = [&](int t, int buf) {
-        u32x4 *L = lds + buf * PP_STAGE;
-        const uint16_t *wb = w_base + t * BK;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dma16(wb + i * 16 * K, i & 1 ? w_offO : w_offE, L + BM * 8 + (wg * 8 + i) * 64);
-    };
-    auto issue_tile = [&](int t, int buf) {
-        issue_a(t, buf);
-        issue_w(t, buf);
+    auto issue_a = [&](int kt, int i) {
+        const int ks = min(kt, T - 1);
+        bdma16(rA, (i & 1) ? a_offO : a_offE, 2u * static_cast<uint32_t>(ks * BK + i * 8 * K),
+               Abuf + (kt % 3) * P3_BUF + (128 * ah + 8 * (4 * wg + i)) * 8);
     };
 
-    // LDS fragment addresses.  Every A slot this lane reads is
-    // wm*64 + tm*16 + (lane&15) and every B slot a multiple of 16 plus
-    // (lane&15), so the swizzle term (slot>>1)&7 is the same for all of them:
-    // per k-step one base address, the tiles are immediate offsets.
+    // fragment slots: A wm*64 + tm*16 + (lane&15) in A(kt % 3); W
+    // 128*wn + {0, 64} + tp*16 + (lane&15) in W(kt & 1)
     const int l16 = lane & 15;
-    const int c0 = (lane >> 4) ^ ((l16 >> 1) & 7);      // chunk position at k-step 0
+    const int c0 = (lane >> 4) ^ ((l16 >> 1) & 7);
     const int offA0 = (wm * WM + l16) * 8 + c0, offA1 = offA0 ^ 4;
-    const int offB0 = BM * 8 + (wn * (WN / 2) + l16) * 8 + c0, offB1 = offB0 ^ 4;
+    const int offB0 = (128 * wn + l16) * 8 + c0, offB1 = offB0 ^ 4;
 
     bf16x8 af[2][TM], bfr[2][TN];
-    auto load_frags = [&](int buf) {
-        const u32x4 *L = lds + buf * PP_STAGE;
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            af[0][tm] = __builtin_bit_cast(bf16x8, L[offA0 + tm * 128]);
-            af[1][tm] = __builtin_bit_cast(bf16x8, L[offA1 + tm * 128]);
+    auto frag = [&](const u32x4 *La, const u32x4 *Lw, int f) {   // fragment read f of 24
+        if (f < 2 * TM) {
+            const int ks = f & 1, tm = f >> 1;
+            af[ks][tm] = __builtin_bit_cast(bf16x8, La[(ks ? offA1 : offA0) + tm * 128]);
+        } else {
+            const int ks = (f - 2 * TM) & 1, tn = (f - 2 * TM) >> 1;
+            const int o = ((tn < TN / 2 ? 0 : 64) + (tn % (TN / 2)) * 16) * 8;
+            bfr[ks][tn] = __builtin_bit_cast(bf16x8, Lw[(ks ? offB1 : offB0) + o]);
         }
+    };
+    // fragments of k-tile kt only (prologue)
+    auto load_frags = [&](int kt) {
+        const u32x4 *La = Abuf + (kt % 3) * P3_BUF, *Lw = Wbuf + (kt & 1) * P3_BUF;
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const int o = ((tn < TN / 2 ? 0 : BN / 2) + (tn % (TN / 2)) * 16) * 8;
-            bfr[0][tn] = __builtin_bit_cast(bf16x8, L[offB0 + o]);
-            bfr[1][tn] = __builtin_bit_cast(bf16x8, L[offB1 + o]);
+        for (int f = 0; f < 24; ++f) frag(La, Lw, f);
+    };
+    // memory phase: fragments of k-tile kt, with W loads 0-3 of k-tile kw
+    // and A loads 0-3 of k-tile ka in between
+    auto memory = [&](int kt, int kw, int ka) {
+        const u32x4 *La = Abuf + (kt % 3) * P3_BUF, *Lw = Wbuf + (kt & 1) * P3_BUF;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) frag(La, Lw, 3 * r + q);
+            __builtin_amdgcn_sched_barrier(0);
+            if (r < 4) issue_w(kw, r);
+            else issue_a(ka, r - 4);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -652,34 +690,20 @@ k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
                     acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
     };
 
-    // L2 prefetch (PF, for long reductions): with every k-tile load, group 0
-    // also touches the 128-byte line of each of the 512 rows of k-tile t+2
-    // beyond it (two 4-byte loads per lane, clamped to the last tile), so the
-    // real load two phases later hits L2.  Each issue is followed by exactly
-    // two touches, so the waits below keep fixed counts.  For short
-    // reductions the extra requests cost more than the misses they save.
-    const uint32_t pf_off = 2u * static_cast<uint32_t>((64 * wg + lane) * K);
-    auto prefetch = [&](int t) {
-        if constexpr (PF) {
-            const int tt = t < T ? t : T - 1;
-            touch4(a_base + tt * BK, pf_off, lds + 2 * PP_STAGE);
-            touch4(w_base + tt * BK, pf_off, lds + 2 * PP_STAGE);
+    // prologue: k-tiles 0 and 1 whole, and A rows 128-255 of k-tile 2 (group
+    // 0's load of the phase before the first); all land before the first read
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            issue_a(kt, i);
+            issue_w(kt, i);
         }
-    };
-
-    // prologue: k-tiles 0 and 1 into LDS; group 0 takes the fragments of 0
     if (grp == 0) {
-        issue_tile(0, 0);
-        prefetch(2);
-        if (T > 1) {
-            issue_tile(1, 1);
-            prefetch(3);
-            if constexpr (PF) wait_vm20();
-            else wait_vm16();
-        } else {
-            wait_vm0();
-        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) issue_a(2, i);
     }
+    wait_vm0();
     pp_barrier();
     if (grp == 0) {
         load_frags(0);
@@ -687,43 +711,36 @@ k_gemm_pp(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     }
     pp_barrier();
 
-    // Main loop.  One vector-memory instruction moves 1 KB, and a CU takes
-    // about as long to move a 64 KB k-tile into LDS as to run a phase of
-    // MFMAs, so the k-tile's loads are split between the two fragment
-    // phases: each group, right after reading its fragments of a buffer,
-    // refills the buffer that both groups have finished reading with its
-    // half of k-tile t+2 (group 1 the A rows, group 0 the W rows).  A group
-    // waits for its own half before the barrier that precedes the first read
-    // of that tile.
+    // Main loop.  At the end of a memory phase the group's loads issued two
+    // memory phases earlier have landed:
+    //   end of 2t:   group 1 its W half 0 and A rows 0-127 of t+1 (phase
+    //                2t-2), read by group 0 in 2t+1 (A rows 128-255 of t+1
+    //                came from group 0 in 2t-3, waited for at the end of 2t-1);
+    //   end of 2t+1: group 0 its W half 1 of t+1 (2t-1), read by group 1 in
+    //                2t+2.
     for (int t = 0; t < T; ++t) {
-        // phase 2t: group 0 computes k-tile t; group 1 reads its fragments of
-        // t (buffer t&1, which group 0 read in phase 2t-1), then sends the A
-        // half of t+2 into that buffer
+        // phase 2t: group 0 computes k-tile t; group 1 reads its fragments
+        // of t and loads W half 0 and A rows 0-127 of t+2
         if (grp == 0) {
             compute();
-            __builtin_amdgcn_sched_barrier(0);       // after all of this phase's MFMAs:
-            if constexpr (PF) wait_vm2();            // its W half of t+1 has landed
-            else wait_vm0();
+            __builtin_amdgcn_sched_barrier(0);
         } else {
-            load_frags(t & 1);
+            memory(t, t + 2, t + 2);
             wait_lgkm0();
-            wait_vm0();                              // its A half of t+1 has landed
-            if (t + 2 < T) issue_a(t + 2, t & 1);
+            wait_vm8();
         }
         pp_barrier();
-        // phase 2t+1: group 0 reads its fragments of t+1, then sends the W
-        // half of t+2; group 1 computes t
+        // phase 2t+1: group 0 reads its fragments of t+1 and loads W half 1
+        // of t+2 and A rows 128-255 of t+3; group 1 computes t
         if (grp == 0) {
             if (t + 1 < T) {
-                load_frags((t + 1) & 1);
+                memory(t + 1, t + 2, t + 3);
                 wait_lgkm0();
-            }
-            if (t + 2 < T) {
-                issue_w(t + 2, t & 1);
-                prefetch(t + 4);
+                wait_vm8();
             }
         } else {
             compute();
+            __builtin_amdgcn_sched_barrier(0);
         }
         pp_barrier();
     }
@@ -761,10 +778,7 @@ template <int EPI>
 static hipError_t launch_pp(const uint16_t *A, const uint16_t *W, int M, int N, int K, const GemmEpi &ep,
                             hipStream_t st) {
     const int grid = static_cast<int>(cdiv(M, PP_BM) * cdiv(N, PP_BN));
-    if (K >= 8192)
-        k_gemm_pp<EPI, true><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
-    else
-        k_gemm_pp<EPI, false><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
+    k_gemm_p3<EPI><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
     return hipGetLastError();
 }
 
