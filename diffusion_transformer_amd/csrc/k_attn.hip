@@ -7,9 +7,17 @@
 // maximum grows; the score scale is applied in fp32).
 //
 // Design (CDNA4, 64-wide waves, MFMA 16x16x32 bf16):
-//  - block = 4 waves = 128 queries of one head; each wave owns 32 queries.
-//    Two blocks share a CU (<= 256 registers per lane, 64 KB LDS each), so
-//    each SIMD interleaves one wave's exponentials with the other's MFMAs.
+//  - block = 8 waves = 256 queries of one head, one block per CU; each wave
+//    owns 32 queries.  The waves form two groups of four (one wave of each
+//    per SIMD) that run half a key tile apart, so that on every SIMD one
+//    wave feeds the matrix core while the other computes exponentials:
+//
+//      phase 2j   : group 0  PV(j-1), QK(j)   | group 1  softmax(j-1), loads K(j+1)
+//      phase 2j+1 : group 0  softmax(j), loads V(j+1) | group 1  PV(j-1), QK(j)
+//
+//    (QK(j): scores of key tile j; softmax(j): their exponentials and the
+//    running maximum; PV(j): the output and row-sum products of tile j).
+//    A workgroup barrier ends every phase.
 //  - the wave computes the TRANSPOSED scores S^T = K Q^T for a 64-key tile:
 //    K (from LDS) is the A operand, the wave's queries (registers, loaded
 //    once) the B operand.  A lane then holds one query column and 16 of its
@@ -19,18 +27,21 @@
 //    order kappa(r) = 8*((r%16)/4) + 4*(r/16) + r%4 within each 32 keys, so
 //    the 8 scores a lane holds for one 32-key step are keys 8g .. 8g+7 and
 //    each V^T fragment is a single 16-byte LDS read.
-//  - K and V^T tiles go global -> LDS directly (global_load_lds_dwordx4,
-//    no register staging), double-buffered; each lane fetches the global
-//    chunk that belongs at its LDS position under the XOR swizzle.
+//  - K and V^T tiles go global -> LDS directly (buffer loads into LDS, no
+//    register staging), issued during the softmax phases two tiles ahead:
+//    K(j) is read in phases 2j and 2j+1 (three K buffers), V(j) in phases
+//    2j+1 to 2j+3 (four V buffers); each load has two or more phases to
+//    land.  In the
+//    matrix phases the LDS fragment reads run two batches ahead of the MFMAs,
+//    the first batch already issued at the end of the wave's softmax phase.
 //  - the row sum is one more MFMA per 32 keys with an all-ones A operand
-//    (it sums the same bf16-rounded P the values are weighted with);
-//    the running maximum is rescaled lazily: only when a tile's maximum
-//    exceeds it by more than 2^8 (exponents stay <= 2^8, exact either way).
-//  - the exponentials are the vector-unit bottleneck, so the softmax is
-//    trimmed to them: queries are pre-multiplied by log2(e)/sqrt(128) and the
-//    score MFMAs start from minus the running maximum, so p = 2^score needs
-//    no separate scale-and-subtract; the maxima use three-input max and
-//    lane-row swaps.
+//    (it sums the same bf16-rounded P the values are weighted with); the
+//    running maximum is rescaled lazily: only when a tile's maximum exceeds
+//    it by more than 2^8 (exponents stay <= 2^8, exact either way).
+//  - the softmax is trimmed to the exponentials: queries are pre-multiplied
+//    by log2(e)/sqrt(128) and the score MFMAs start from minus the running
+//    maximum, so p = 2^score needs no separate scale-and-subtract; the
+//    maxima use three-input max and lane-row swaps.
 //  - blocks are remapped so that each XCD (own L2) serves whole heads.
 #include "common.h"
 #include "kernels.h"
@@ -38,18 +49,18 @@
 namespace dit {
 
 namespace {
-constexpr int QB = 128;   // queries per block
+constexpr int QB = 256;   // queries per block
 constexpr int QW = 32;    // queries per wave
 constexpr int KT = 64;    // keys per tile
 constexpr int HD = 128;   // head dim
-constexpr int NT = 256;
+constexpr int NT = 512;
 constexpr int K_U4 = KT * 16;     // K tile: 64 rows x 16 chunks of 16 B
 constexpr int V_U4 = HD * 8;      // V^T tile: 128 rows x 8 chunks
-constexpr int STAGE = K_U4 + V_U4;
+constexpr int NKB = 3, NVB = 4;   // K and V^T buffers
 constexpr float kLazy = 8.0f;     // rescale when the maximum grows by > 2^8
 
 __device__ __forceinline__ int kidx(int row, int c) { return row * 16 + (c ^ (row & 15)); }
-__device__ __forceinline__ int vidx(int d, int c) { return K_U4 + d * 8 + (c ^ ((d >> 1) & 7)); }
+__device__ __forceinline__ int vidx(int d, int c) { return d * 8 + (c ^ ((d >> 1) & 7)); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -67,17 +78,23 @@ __device__ __forceinline__ float fmax_xor32(float v) {
     return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
-__device__ __forceinline__ void g2l16(const void *g, u32x4 *l) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)(l), 16, 0, 0);
-}
+__device__ __forceinline__ void att_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void att_wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void att_wait_vm4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+// lgkmcnt(0) as the builtin (vmcnt and expcnt fields at their maxima), so
+// that the compiler's own wait insertion knows the LDS accesses completed
+__device__ __forceinline__ void att_lgkm_done() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 }  // namespace
 
-__global__ void __launch_bounds__(NT, 2)
+__global__ void __launch_bounds__(NT, 1)
 k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
             const uint16_t *__restrict__ Vt, int S, int ldv, int heads, uint16_t *__restrict__ O,
             int ldo) {
-    __shared__ u32x4 lds[2 * STAGE];
+    __shared__ u32x4 lds[NKB * K_U4 + NVB * V_U4];   // 112 KB
+    u32x4 *const Kb = lds;
+    u32x4 *const Vb = lds + NKB * K_U4;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 2, wg = wave & 3;
     const int g = lane >> 4, l16 = lane & 15;
 
     // XCD-compact order: consecutive work ids on one XCD share a head
@@ -115,31 +132,45 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     }
 
     const int ntiles = (S + KT - 1) / KT;
-    // direct global -> LDS: wave instruction i writes 1 KB = 4 K rows or 8 V^T rows
-    // load i (0..7) of tile t: i < 4 the K rows, else the V^T rows
-    auto issue_one = [&](int t, int buf, int i) {
-        const int kv0 = t * KT;
-        u32x4 *L = lds + buf * STAGE;
-        const int blk = wave * 4 + (i & 3);               // 0..15
-        if (i < 4) {
-            const int r = blk * 4 + (lane >> 4);          // LDS K row 0..63
-            const int c = (lane & 15) ^ (r & 15);         // global chunk for LDS position lane&15
-            const int rr = r & 31;
-            const int kk = (r & 32) + 8 * ((rr & 15) >> 2) + 4 * (rr >> 4) + (rr & 3);   // kappa
-            const int key = min(kv0 + kk, S - 1);
-            g2l16(Kh + static_cast<int64_t>(key) * HD + c * 8, L + blk * 64);
-        } else {
-            const int d = blk * 8 + (lane >> 3);          // V^T row 0..127
-            const int c = (lane & 7) ^ ((d >> 1) & 7);
-            g2l16(Vh + static_cast<int64_t>(d) * ldv + kv0 + c * 8, L + K_U4 + blk * 64);
+    // Direct global -> LDS through buffer loads, one wave instruction = 1 KB:
+    // load i (0..3) of this wave moves LDS K rows r = 16wg + 4i + (lane>>4)
+    // or V^T rows d = 32wg + 8i + (lane>>3) of a tile; each lane fetches the
+    // global chunk that belongs at its LDS position under the XOR swizzle.
+    // Both offsets are one per-lane base XOR (i's chunk bits) plus a uniform
+    // step:
+    //   K row r holds key kappa(r) = 32(wg>>1) + 4(wg&1) + (lane>>4) + 8i and
+    //     chunk (lane&15) ^ (4i + (lane>>4));
+    //   V^T row d takes chunk (lane&7) ^ (lane>>4) ^ 4(i&1).
+    // The K descriptor ends at row S, so keys past S read as zeros (their
+    // scores are masked); the V^T descriptor covers all Sp columns.
+    const __amdgpu_buffer_rsrc_t rK =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Kh), static_cast<short>(0), S * HD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rV =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Vh), static_cast<short>(0), HD * ldv * 2, 0x00020000);
+    const int lg = lane >> 4;
+    const uint32_t k_lane = static_cast<uint32_t>((32 * (wg >> 1) + 4 * (wg & 1) + lg) * HD * 2 + (((lane & 15) ^ lg) << 4));
+    const uint32_t v_lane = static_cast<uint32_t>((32 * wg + (lane >> 3)) * ldv * 2 + ((((lane & 7) ^ lg)) << 4));
+    auto issue_k = [&](int t, int i) {
+        const uint32_t off = (k_lane ^ static_cast<uint32_t>(i << 6)) + static_cast<uint32_t>((t * KT + 8 * i) * HD * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void *)(Kb + (t % NKB) * K_U4 + (wg * 4 + i) * 64), 16, off, 0, 0, 0);
+    };
+    auto issue_v = [&](int t, int i) {
+        const uint32_t off = (v_lane ^ static_cast<uint32_t>((i & 1) << 6)) + static_cast<uint32_t>(8 * i * ldv * 2 + t * KT * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void *)(Vb + (t % NVB) * V_U4 + (wg * 4 + i) * 64), 16, off, 0, 0, 0);
+    };
+    // keys >= S of the last tile: zero their values in LDS, so that a 0
+    // weight never meets padding (which may hold anything); by group 0
+    const int last = ntiles - 1, valid_last = S - last * KT;
+    auto zero_tail = [&]() {
+        if (valid_last == KT) return;
+        uint16_t *V16 = reinterpret_cast<uint16_t *>(Vb + (last % NVB) * V_U4);
+        for (int e = tid; e < HD * KT; e += NT / 2) {
+            const int d = e / KT, key = e % KT;
+            if (key >= valid_last) V16[vidx(d, key >> 3) * 8 + (key & 7)] = 0;
         }
     };
-    auto issue_tile = [&](int t, int buf) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) issue_one(t, buf, i);
-    };
 
-    f32x4 oacc[8][2], rsum[2];
+    f32x4 oacc[8][2], rsum[2], s[4][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -152,61 +183,80 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     bool started = false;
     const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
     const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_u);
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) pf[j][tq] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
-    issue_tile(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
-        const int kv0 = t * KT;
-        const bool tail = kv0 + KT > S;
-        if (tail) {
-            // keys >= S: zero their values so that 0-weight * garbage stays 0
-            u32x4 *L = lds + cur * STAGE;
-            uint16_t *V16 = reinterpret_cast<uint16_t *>(L + K_U4);
-            const int valid = S - kv0;
-            for (int e = tid; e < HD * KT; e += NT) {
-                const int d = e / KT, key = e % KT;
-                if (key >= valid) {
-                    const int c = key >> 3;
-                    V16[(d * 8 + (c ^ ((d >> 1) & 7))) * 8 + (key & 7)] = 0;
-                }
-            }
-            __syncthreads();
+    // ---- the matrix phase: O^T += V^T P^T and the row sums of tile tv (two
+    // 32-key steps; its first V^T fragments are already in fa), then
+    // S^T = K Q^T of tile tk (64 keys x 32 queries; s[tk][tq][r] holds
+    // x = score * log2(e)/sqrt(128) - mb for key 32*(tk/2) + 8g + 4*(tk%2) + r).
+    // The LDS reads go in quarters of 4 fragments, each issued two quarters
+    // before the MFMAs that use it (at most 8 reads in flight).
+    bf16x8 fa[8], fb[8];
+    auto prefetch_v = [&](int t) {   // V^T fragments of keys 8g .. 8g+7 of tile t >= -1
+        const u32x4 *L = Vb + ((t + NVB) % NVB) * V_U4;
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) fa[dd] = __builtin_bit_cast(bf16x8, L[vidx(dd * 16 + l16, g)]);
+    };
+    // quarter h (0, 1) of the V^T fragments of 32-key step j; of the K
+    // fragments of k-step ks
+    auto read_v4 = [&](bf16x8 *f, const u32x4 *L, int j, int h) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            f[u] = __builtin_bit_cast(bf16x8, L[vidx((4 * h + u) * 16 + l16, 4 * j + g)]);
+    };
+    auto read_k4 = [&](bf16x8 *f, const u32x4 *L, int ks) {
+#pragma unroll
+        for (int tk = 0; tk < 4; ++tk) f[tk] = __builtin_bit_cast(bf16x8, L[kidx(tk * 16 + l16, ks * 4 + g)]);
+    };
+    auto pv4 = [&](const bf16x8 *f, int j, int h) {   // value rows 64h .. 64h+63 of step j
+        if (h == 0) {
+#pragma unroll
+            for (int tq = 0; tq < 2; ++tq)
+                rsum[tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[j][tq], rsum[tq], 0, 0, 0);
         }
-        const u32x4 *L = lds + cur * STAGE;
-
-        // ---- S^T = K Q^T for 64 keys x 32 queries (raw scores), with the
-        // next tile's 8 loads into LDS spread between the MFMAs: issued in a
-        // row they stall the wave on the vector-memory queue.  The last tile
-        // loads itself again (into the idle buffer) to keep one code path.
-        const int tn = min(t + 1, ntiles - 1);
-        f32x4 s[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int tq = 0; tq < 2; ++tq)
+                oacc[4 * h + u][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[u], pf[j][tq], oacc[4 * h + u][tq], 0, 0, 0);
+    };
+    auto qk4 = [&](const bf16x8 *f, int ks) {
         const f32x4 init[2] = {f32x4{-mb[0], -mb[0], -mb[0], -mb[0]}, f32x4{-mb[1], -mb[1], -mb[1], -mb[1]}};
-        bf16x8 kf[4][4];                                   // all K fragments first (LDS reads
-#pragma unroll                                            // may not pass the loads into LDS)
-        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int tk = 0; tk < 4; ++tk) kf[ks][tk] = __builtin_bit_cast(bf16x8, L[kidx(tk * 16 + l16, ks * 4 + g)]);
+        for (int tk = 0; tk < 4; ++tk)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-            for (int tk = 0; tk < 4; ++tk) {
-                if ((tk & 1) == 0) issue_one(tn, cur ^ 1, ks * 2 + (tk >> 1));
-#pragma unroll
-                for (int tq = 0; tq < 2; ++tq)
-                    s[tk][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tk], qf[tq][ks], ks == 0 ? init[tq] : s[tk][tq], 0, 0, 0);
-            }
-        }
+            for (int tq = 0; tq < 2; ++tq)
+                s[tk][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[tk], qf[tq][ks], ks == 0 ? init[tq] : s[tk][tq], 0, 0, 0);
+    };
+    // tv = -1 (the first matrix phase) reads V^T buffer NVB-1, which is
+    // zeroed before the loop, with P = 0; tk = ntiles (the last) computes
+    // scores that are never used: the phase has no branches
+    auto mma = [&](int tv, int tk) {
+        const u32x4 *LK = Kb + (tk % NKB) * K_U4;
+        const u32x4 *LV = Vb + ((tv + NVB) % NVB) * V_U4;
+#define DIT_STEP(read, use) do { read; __builtin_amdgcn_sched_barrier(0); use; __builtin_amdgcn_sched_barrier(0); } while (0)
+        DIT_STEP(read_v4(fb, LV, 1, 0), pv4(fa, 0, 0));
+        DIT_STEP(read_v4(fb + 4, LV, 1, 1), pv4(fa + 4, 0, 1));
+        DIT_STEP(read_k4(fa, LK, 0), pv4(fb, 1, 0));
+        DIT_STEP(read_k4(fa + 4, LK, 1), pv4(fb + 4, 1, 1));
+        DIT_STEP(read_k4(fb, LK, 2), qk4(fa, 0));
+        DIT_STEP(read_k4(fb + 4, LK, 3), qk4(fa + 4, 1));
+        qk4(fb, 2);
+        qk4(fb + 4, 3);
+#undef DIT_STEP
+    };
 
-        // ---- online softmax per query column (lane): s[tk][tq][r] holds
-        // x = score * log2(e)/sqrt(128) - mb for key kv0 + 32*(tk/2) + 8g +
-        // 4*(tk%2) + r.  Common case: the tile's maximum of x is <= 2^8 above
-        // the running maximum and p = 2^x needs no subtraction.  Otherwise
-        // (and for the first tile) the maximum moves up by the tile's max m:
-        // the partial output and sums are scaled by 2^-m and p = 2^(x - m).
-        if (tail) {
+    // ---- online softmax of tile t: common case, the tile's maximum of x is
+    // <= 2^8 above the running maximum and p = 2^x needs no subtraction.
+    // Otherwise (and for the first tile) the maximum moves up by the tile's
+    // max m: the partial output and sums are scaled by 2^-m and p = 2^(x - m).
+    auto softmax = [&](int t) {
+        const int kv0 = t * KT;
+        if (kv0 + KT > S) {
 #pragma unroll
             for (int tk = 0; tk < 4; ++tk)
 #pragma unroll
@@ -241,7 +291,6 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
             }
             started = true;
         }
-        bf16x8 pf[2][2];
 #pragma unroll
         for (int tq = 0; tq < 2; ++tq) {
 #pragma unroll
@@ -254,25 +303,73 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
                 pf[j][tq] = __builtin_bit_cast(bf16x8, u);
             }
         }
+    };
 
-        // ---- O^T += V^T P^T and the row sums, two 32-key steps
+    // prologue: group 0 loads K(0) and K(1), group 1 V(0) and V(1); V^T
+    // buffer NVB-1 (first used by V(NVB-1)) is zeroed for the branch-free
+    // first matrix phase
+    for (int t = 0; t < min(2, ntiles); ++t)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int tq = 0; tq < 2; ++tq)
-                rsum[tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[j][tq], rsum[tq], 0, 0, 0);
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                // keys 32j + 8g .. +7 of value row d: one 16-byte chunk
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, L[vidx(dd * 16 + l16, 4 * j + g)]);
-#pragma unroll
-                for (int tq = 0; tq < 2; ++tq)
-                    oacc[dd][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[j][tq], oacc[dd][tq], 0, 0, 0);
-            }
+        for (int i = 0; i < 4; ++i) {
+            if (grp == 0) issue_k(t, i);
+            else issue_v(t, i);
         }
+    for (int e = tid; e < V_U4; e += NT) Vb[(NVB - 1) * V_U4 + e] = u32x4{0u, 0u, 0u, 0u};
+    att_wait_vm0();
+    att_lgkm_done();
+    att_barrier();
+    if (grp == 0 && last == 0) zero_tail();
+    att_lgkm_done();
+    att_barrier();
+    if (grp == 0) {
+        prefetch_v(-1);
+        att_lgkm_done();
+    }
 
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile t+1 have landed
-        __syncthreads();                 // everyone's have, and nobody still reads tile t
+    // Main loop over the phases.  Loads and waits: group 1 issues K(j+2) in
+    // phase 2j (K(j+2) reuses the buffer of K(j-1), last read in 2j-1) and
+    // waits for K(j+1) at the end of 2j+1 (read from 2j+2 on); group 0
+    // issues V(j+2) in phase 2j+1 (the buffer of V(j-2), last read in 2j-1)
+    // and waits for V(j) at the end of 2j, where it also zeroes the padding
+    // keys of the last tile's values (read from 2j+1 on: each group fetches
+    // the first V^T fragments of tile j at the end of its softmax phase
+    // before PV(j)).  A wait leaves in flight the 4 loads issued after the
+    // ones it needs, if there were any.
+    for (int j = 0; j <= ntiles; ++j) {
+        // phase 2j
+        if (grp == 0) {
+            mma(j - 1, j);
+            if (j + 1 < ntiles) att_wait_vm4();   // V(j) has landed, V(j+1) may not
+            else att_wait_vm0();
+            if (j == last && j > 0) zero_tail();
+            att_lgkm_done();
+        } else {
+            if (j >= 1) softmax(j - 1);
+            if (j + 2 < ntiles) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) issue_k(j + 2, i);
+            }
+            prefetch_v(j - 1);
+            att_lgkm_done();
+        }
+        att_barrier();
+        // phase 2j+1
+        if (grp == 0) {
+            if (j < ntiles) {
+                softmax(j);
+                if (j + 2 < ntiles) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) issue_v(j + 2, i);
+                }
+                prefetch_v(j);
+                att_lgkm_done();
+            }
+        } else {
+            mma(j - 1, j);
+            if (j + 2 < ntiles) att_wait_vm4();   // K(j+1) has landed, K(j+2) may not
+            else att_wait_vm0();
+        }
+        att_barrier();
     }
 
     // ---- normalise and store o[q][h*128 + d], d = dd*16 + 4g + r
