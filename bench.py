@@ -126,7 +126,7 @@ def summarize_counters(fetch_csv, write_csv, out_json):
         pending = None
         for d in order:
             n = names[d]
-            epi = re.search(r"k_gemm_pp<(\d)", n) or re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
+            epi = re.search(r"k_gemm_p3<(\d)>", n) or re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
             epi = int(epi.group(1)) if epi else None
             if epi == 3:
                 stage_of[d] = "qkv"
