@@ -296,7 +296,7 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
     c->stream = static_cast<hipStream_t>(stream);
     c->arch = *arch;
     c->max_rows = max_rows;
-    c->max_rows_pad = round_up(max_rows, 2304);   // whole 256- and 288-row product tiles
+    c->max_rows_pad = round_up(max_rows, 256);   // whole 256-row product tiles
 
     const size_t S = c->max_rows_pad, D = arch->hidden, F = arch->ffn, H = arch->heads;
     const size_t sizes[] = {

@@ -47,9 +47,8 @@ struct GemmEpi {
 
 // C = A[M,K] * W[N,K]^T, A bf16; W bf16 (w8 = false) or int8 with bf16
 // scales [N, K/32] (w8 = true); then the epilogue.  K % 64 == 0, N % 64 == 0.
-// a_rows_padded: A's allocation holds at least M rounded up to a multiple of
-// 2304 rows (so whole 256- and 288-row tiles can be read; rows past M are
-// read and their results discarded).
+// a_rows_padded: A's allocation holds at least M rounded up to 256 rows
+// (rows past M are read and their results discarded).
 hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Wscale, bool w8, int M,
                        int N, int K, const GemmEpi &epi, hipStream_t st, bool a_rows_padded);
 
