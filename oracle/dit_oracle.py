@@ -22,7 +22,7 @@ Sources (web pages; cited by title and section):
         D3c qk-prep).
   [GZ]  "gizai:dit" module reference: types Block, Sequence, Modulation;
         functions sinusoids, gluRows, gatedInto, normedInto, prepOf, silu,
-        Block.forward; constants HEAD, QKV/OUT/UP/DOWN.
+        Block.forward, Block.parallel; constants HEAD, QKV/OUT/UP/DOWN.
 
 Readings of points the pages leave open are listed in the repository's
 design notes; the ones that shape the arithmetic are restated where used.
@@ -33,6 +33,9 @@ except `block_forward`/`denoise` as a whole, whose composition is pinned
 only through its parts, a pure-Python brute-force twin on tiny shapes and
 structural invariants (identity when all gates are zero, permutation
 equivariance of rows); no page prints a block output.
+`parallel_block_forward` is pinned to the sequential block: its update is
+the sum of the sequential block's attention-only and MLP-only updates (gate
+of the other half zero) under the same shift, scale and gate.
 """
 
 from __future__ import annotations
@@ -339,6 +342,54 @@ def block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, rows):
     return y, o, x1, a
 
 
+def parallel_block_forward(x, bw: BlockWeights, vec, cos, sin, arch: Arch,
+                           keep: bool = False):
+    """The parallel block ([GZ] Block.parallel): one modulated norm feeds
+    both the attention and the SwiGLU MLP, and one gate scales their sum:
+    x + gate * (attention(h) W_out^T + swiglu(h W_up^T) W_down^T) with
+    h = norm(x) (1 + scale) + shift.  The modulation has three rows
+    (shift, scale, gate; w_mod [3D, D]); UP's rows are gate/up interleaved
+    as in the sequential block.  Returns the new rows (float64) and, with
+    keep=True, the intermediates (mod, h, q, k, v after prep, o, a)."""
+    x = np.asarray(x, F64)
+    S, D = x.shape
+    H, d = arch.heads, arch.head_dim
+    m = modulation(vec, bw.w_mod, 3)
+    shift, scale, gate = m
+    h = modulated_norm(x, shift, scale, arch, bw.norm1)
+    qkv = linear(h, bw.w_qkv)
+    q = head_prep(heads_of(qkv[:, 0:H * d], H, d), bw.q_norm, arch.qk_eps, cos, sin)
+    k = head_prep(heads_of(qkv[:, H * d:2 * H * d], H, d), bw.k_norm, arch.qk_eps, cos, sin)
+    v = heads_of(qkv[:, 2 * H * d:3 * H * d], H, d)
+    o = attention(q, k, v).transpose(1, 0, 2).reshape(S, H * d)
+    a = swiglu_interleaved(linear(h, bw.w_up))
+    y = x + gate * (linear(o, bw.w_out) + linear(a, bw.w_down))
+    if not keep:
+        return y
+    return y, dict(mod=m, h=h, q=q, k=k, v=v, o=o, a=a)
+
+
+def parallel_block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, rows):
+    """Parallel-block output for the selected rows only (same arithmetic as
+    parallel_block_forward; keys and values need every row).  Returns
+    (y[rows], o[rows], a[rows])."""
+    x = np.asarray(x, F64)
+    rows = np.asarray(rows)
+    H, d = arch.heads, arch.head_dim
+    shift, scale, gate = modulation(vec, bw.w_mod, 3)
+    h = modulated_norm(x, shift, scale, arch, bw.norm1)
+    wq = np.asarray(bw.w_qkv, F64)
+    q = heads_of(linear(h[rows], wq[0:H * d]), H, d)
+    k = heads_of(linear(h, wq[H * d:2 * H * d]), H, d)
+    v = heads_of(linear(h, wq[2 * H * d:]), H, d)
+    q = head_prep(q, bw.q_norm, arch.qk_eps, cos[rows], sin[rows])
+    k = head_prep(k, bw.k_norm, arch.qk_eps, cos, sin)
+    o = attention(q, k, v).transpose(1, 0, 2).reshape(len(rows), H * d)
+    a = swiglu_interleaved(linear(h[rows], bw.w_up))
+    y = x[rows] + gate * (linear(o, bw.w_out) + linear(a, bw.w_down))
+    return y, o, a
+
+
 # ---------------------------------------------------------------------------
 # [HC] s.1 int8lin weights: one bf16 scale per block of 32
 # ---------------------------------------------------------------------------
@@ -435,9 +486,12 @@ def denoise(x_lat, ctx_feats, mw: ModelWeights, cos, sin, sigmas, arch: Arch,
 # FLOP accounting (algorithmic: 2*M*N*K per product, 4*H*S^2*d attention)
 # ---------------------------------------------------------------------------
 
-def block_flops(S: int, arch: Arch) -> int:
+def block_flops(S: int, arch: Arch, chunks: int = 6) -> int:
+    """Algorithmic FLOPs of one block over S rows: 2mnk per product, 4 H S^2 d
+    for the attention, the modulation GEMV (6 rows of modulation for the
+    sequential block, 3 for the parallel one)."""
     D, F, H, d = arch.hidden, arch.ffn, arch.heads, arch.head_dim
     lin = 2 * S * D * (3 * H * d) + 2 * S * (H * d) * D + 2 * S * D * (2 * F) + 2 * S * F * D
     att = 4 * H * S * S * d
-    gemv = 2 * (6 * D) * D
+    gemv = 2 * (chunks * D) * D
     return lin + att + gemv

@@ -399,6 +399,75 @@ def test_block_precision_consistency():
     assert np.abs(y - y32).max() < 1e-5
 
 
+# ---------------------------------------------------------------- parallel block
+
+def _parallel(W3, pos, x, vecc, arch=TINY):
+    c, s = O.rope_tables(pos, arch.axes)
+    return O.parallel_block_forward(x, O.BlockWeights(**W3), vecc, c, s, arch)
+
+
+def _with_mod(W, w_mod):
+    W2 = dict(W)
+    W2["w_mod"] = w_mod
+    return W2
+
+
+@pytest.mark.parametrize("rms", [False, True])
+def test_parallel_block_is_sum_of_sequential_halves(rms):
+    # [GZ] Block.parallel: one norm feeds both halves and one gate scales
+    # their sum.  The sequential block ([GZ] Block.forward, pinned by its own
+    # brute force) with its MLP gate zero is x + gate * attention-half; with
+    # its attention gate zero its MLP reads norm(x) itself.  So the parallel
+    # update is the sum of those two updates, with (shift, scale, gate)
+    # copied into both halves' modulation rows.
+    arch = O.Arch(16, 2, 8, 12, axes=(2, 2, 4), norm="rms" if rms else "layer")
+    W, pos, x, vecc = _tiny_case(seed=21, rms=rms)
+    D = arch.hidden
+    w3 = W["w_mod"][:3 * D].copy()                      # shift, scale, gate
+    zero = np.zeros((D, D))
+    attn_only = np.concatenate([w3, w3[:2 * D], zero])   # gate_m = 0
+    mlp_only = np.concatenate([w3[:2 * D], zero, w3])    # gate_a = 0
+    W3 = _with_mod(W, w3)
+    if rms:
+        W3["norm2"] = W3["norm1"]                       # one norm weight for both halves
+        W["norm2"] = W["norm1"]
+    y = _parallel(W3, pos, x, vecc, arch)
+    ya = _oracle_block(_with_mod(W, attn_only), pos, x, vecc, arch)
+    ym = _oracle_block(_with_mod(W, mlp_only), pos, x, vecc, arch)
+    ref = x + (ya - x) + (ym - x)
+    assert np.abs(y - ref).max() < 1e-12, np.abs(y - ref).max()
+    assert np.abs(ya - x).max() > 1e-3 and np.abs(ym - x).max() > 1e-3
+
+
+def test_parallel_block_zero_gate_is_identity():
+    W, pos, x, vecc = _tiny_case(seed=22)
+    D = TINY.hidden
+    w3 = W["w_mod"][:3 * D].copy()
+    w3[2 * D:] = 0
+    assert (_parallel(_with_mod(W, w3), pos, x, vecc) == x).all()
+
+
+def test_parallel_block_rows_matches_full():
+    W, pos, x, vecc = _tiny_case(seed=23, S_L=3, h=3, w=3)
+    W3 = _with_mod(W, W["w_mod"][:3 * TINY.hidden].copy())
+    c, s = O.rope_tables(pos, TINY.axes)
+    bw = O.BlockWeights(**W3)
+    y, inter = O.parallel_block_forward(x, bw, vecc, c, s, TINY, keep=True)
+    rows = np.array([1, 5, 11])
+    yr, o, a = O.parallel_block_forward_rows(x, bw, vecc, c, s, TINY, rows)
+    assert np.allclose(yr, y[rows], atol=1e-12)
+    assert np.allclose(o, inter["o"][rows], atol=1e-12)
+    assert np.allclose(a, inter["a"][rows], atol=1e-12)
+
+
+def test_parallel_block_flops():
+    # same four products and attention as the sequential block; a GEMV of
+    # three modulation rows instead of six
+    arch = O.Arch(3072, 24, 128, 12288)
+    d = O.block_flops(4608, arch) - O.block_flops(4608, arch, chunks=3)
+    assert d == 2 * 3 * 3072 * 3072
+
+
 # ---------------------------------------------------------------- time vector, modulation
 
 def test_time_vector_brute_force():
