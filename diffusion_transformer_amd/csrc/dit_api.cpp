@@ -32,8 +32,11 @@ struct dit_ctx {
     float *mod = nullptr, *vec = nullptr, *temb = nullptr, *t1 = nullptr, *fmod = nullptr;
     uint16_t *h = nullptr, *h2 = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr,
              *a = nullptr, *latb = nullptr, *ctxb = nullptr;
+    // parallel block: [attention output | SwiGLU output] per row, the one A
+    // operand of its fused output product
+    uint16_t *oa = nullptr;
     float *seq = nullptr, *vel = nullptr;
-    size_t bytes[8] = {};
+    size_t bytes[9] = {};
     std::string err;
     // stage timing
     bool timing = false;
@@ -150,7 +153,7 @@ dit_status check_ctx(dit_ctx *c) {
     return DIT_OK;
 }
 
-dit_status check_block(dit_ctx *c, const dit_block *b) {
+dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false) {
     if (!b) return fail(c, DIT_EINVAL, "block is NULL");
     if (b->wtype != DIT_W_BF16 && b->wtype != DIT_W_INT8_B32) return fail(c, DIT_EINVAL, "unknown wtype %d", b->wtype);
     for (int i = 0; i < 4; ++i) {
@@ -160,8 +163,8 @@ dit_status check_block(dit_ctx *c, const dit_block *b) {
     }
     if (!b->w_mod) return fail(c, DIT_EINVAL, "block w_mod is NULL");
     if (!b->norm_w[2] || !b->norm_w[3]) return fail(c, DIT_EINVAL, "head-norm weights are NULL");
-    if (c->arch.norm == DIT_NORM_RMS && (!b->norm_w[0] || !b->norm_w[1]))
-        return fail(c, DIT_EINVAL, "RMSNorm needs norm weights NORM1 and NORM2");
+    if (c->arch.norm == DIT_NORM_RMS && (!b->norm_w[0] || (!parallel && !b->norm_w[1])))
+        return fail(c, DIT_EINVAL, parallel ? "RMSNorm needs norm weight NORM1" : "RMSNorm needs norm weights NORM1 and NORM2");
     return DIT_OK;
 }
 
@@ -243,6 +246,100 @@ dit_status block_forward(dit_ctx *c, const dit_block *b, float *x, const float *
     return DIT_OK;
 }
 
+// The parallel block's launch sequence ([GZ] Block.parallel; validated
+// arguments): modulation (shift, scale, gate), one modulated norm, then for
+// bf16 weights at ping-pong sizes one product over [QKV | UP] (head-norm +
+// rotary epilogue on the QKV columns, SwiGLU on the rest, written beside the
+// attention output) and one gated-residual product over [o | a] with
+// [W_out | W_down] (k < D from W_out, the rest from W_down); otherwise the
+// same as four products.
+dit_status parallel_block_forward(dit_ctx *c, const dit_block *b, float *x, const float *vec, const float *cs,
+                                  const float *sn, int S) {
+    const dit_arch &A = c->arch;
+    const int D = A.hidden, F = A.ffn, H = A.heads;
+    const int Sp = round_up(S, 64);
+    const bool w8 = b->wtype == DIT_W_INT8_B32;
+    const bool rms = A.norm == DIT_NORM_RMS;
+    hipStream_t st = c->stream;
+    float *mod = c->mod;
+
+    {
+        Stage t(c, DIT_ST_MOD);
+        DIT_LAUNCH(c, launch_gemv(b->w_mod, vec, 3 * D, D, true, mod, st), "modulation");
+    }
+    {
+        Stage t(c, DIT_ST_NORM1);
+        DIT_LAUNCH(c, launch_modnorm(x, S, D, mod, mod + D, b->norm_w[0], rms, A.eps, c->h, st), "norm");
+    }
+    GemmEpi e{};
+    e.kind = EPI_QKV;
+    e.q = c->q;
+    e.k = c->k;
+    e.vt = c->vt;
+    e.heads = H;
+    e.ldv = Sp;
+    e.qn = b->norm_w[2];
+    e.kn = b->norm_w[3];
+    e.cos = cs;
+    e.sin = sn;
+    e.qk_eps = A.qk_eps;
+    GemmEpi fin = e;
+    fin.kind = EPI_QKV_SWIGLU;
+    fin.w2 = static_cast<const uint16_t *>(b->w[2]);
+    fin.n_split = 3 * D;
+    fin.act = c->oa + D;
+    fin.ld_act = D + F;
+    GemmEpi g{};
+    g.kind = EPI_GATE_RES;
+    g.out = x;
+    g.ldo = D;
+    g.gate = mod + 2 * D;
+    GemmEpi gk = g;
+    gk.w2 = static_cast<const uint16_t *>(b->w[3]);
+    gk.k_split = D;
+    const bool fused = !w8 && gemm_pingpong_ok(S, 3 * D + 2 * F, D, false, fin, true) &&
+                       gemm_pingpong_ok(S, D, D + F, false, gk, true);
+    if (fused) {
+        {
+            Stage t(c, DIT_ST_PAR_IN);
+            DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], nullptr, false, S, 3 * D + 2 * F, D, fin, st, true), "qkv+up");
+        }
+        {
+            Stage t(c, DIT_ST_ATTN);
+            DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->oa, D + F, st), "attention");
+        }
+        {
+            Stage t(c, DIT_ST_PAR_OUT);
+            DIT_LAUNCH(c, launch_gemm(c->oa, b->w[1], nullptr, false, S, D, D + F, gk, st, true), "out+down");
+        }
+        return DIT_OK;
+    }
+    {
+        Stage t(c, DIT_ST_QKV);
+        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], b->scale[0], w8, S, 3 * D, D, e, st, true), "qkv");
+    }
+    GemmEpi u{};
+    u.kind = EPI_SWIGLU;
+    u.act = c->a;
+    {
+        Stage t(c, DIT_ST_UP);
+        DIT_LAUNCH(c, launch_gemm(c->h, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st, true), "up");
+    }
+    {
+        Stage t(c, DIT_ST_ATTN);
+        DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
+    }
+    {
+        Stage t(c, DIT_ST_OUT);
+        DIT_LAUNCH(c, launch_gemm(c->o, b->w[1], b->scale[1], w8, S, D, D, g, st, true), "out");
+    }
+    {
+        Stage t(c, DIT_ST_DOWN);
+        DIT_LAUNCH(c, launch_gemm(c->a, b->w[3], b->scale[3], w8, S, D, F, g, st, true), "down");
+    }
+    return DIT_OK;
+}
+
 dit_status time_vector(dit_ctx *c, const uint16_t *w1, const uint16_t *w2, float t, float *vec) {
     const dit_arch &A = c->arch;
     hipStream_t st = c->stream;
@@ -306,6 +403,7 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
         S * D * 2, S * F * 2,                                          // o a
         S * size_t(arch->latent) * 2, S * size_t(arch->text_dim) * 2,  // latb ctxb
         S * D * 4, S * size_t(arch->latent) * 4,                       // seq vel
+        S * (D + F) * 2,                                               // oa
     };
     size_t off[sizeof sizes / sizeof sizes[0]];
     size_t total = 0;
@@ -335,8 +433,9 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
     c->ctxb = reinterpret_cast<uint16_t *>(p + off[13]);
     c->seq = reinterpret_cast<float *>(p + off[14]);
     c->vel = reinterpret_cast<float *>(p + off[15]);
-    const size_t dbg[8] = {sizes[0], sizes[5], sizes[7], sizes[8], sizes[9], sizes[10], sizes[6], sizes[11]};
-    for (int i = 0; i < 8; ++i) c->bytes[i] = dbg[i];
+    c->oa = reinterpret_cast<uint16_t *>(p + off[16]);
+    const size_t dbg[9] = {sizes[0], sizes[5], sizes[7], sizes[8], sizes[9], sizes[10], sizes[6], sizes[11], sizes[16]};
+    for (int i = 0; i < 9; ++i) c->bytes[i] = dbg[i];
     *out = c;
     return DIT_OK;
 }
@@ -481,6 +580,16 @@ dit_status dit_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const f
     return block_forward(ctx, b, x, vec, cos_t, sin_t, L + N);
 }
 
+dit_status dit_parallel_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const float *vec,
+                                      const float *cos_t, const float *sin_t, int L, int N) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
+    DIT_TRY(check_block(ctx, b, true));
+    DIT_TRY(check_rows(ctx, L, N));
+    DIT_TRY(check_ctx(ctx));
+    return parallel_block_forward(ctx, b, x, vec, cos_t, sin_t, L + N);
+}
+
 dit_status dit_prologue(dit_ctx *ctx, const dit_model *m, const float *ctx_feats, int L, float *txt) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (!ctx_feats || !txt) return fail(ctx, DIT_EINVAL, "ctx_feats or txt is NULL");
@@ -568,14 +677,14 @@ dit_status dit_dequant_int8_b32(dit_ctx *ctx, const int8_t *q, const uint16_t *s
 
 dit_status dit_debug_copy(dit_ctx *ctx, int which, void *dst, int64_t bytes) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
-    if (which < 0 || which > 7) return fail(ctx, DIT_ERANGE, "buffer %d outside 0..7", which);
+    if (which < 0 || which > 8) return fail(ctx, DIT_ERANGE, "buffer %d outside 0..8", which);
     if (bytes <= 0) return DIT_OK;
     if (!dst) return fail(ctx, DIT_EINVAL, "dst is NULL");
     if (static_cast<size_t>(bytes) > ctx->bytes[which])
         return fail(ctx, DIT_ERANGE, "%lld bytes exceed buffer %d (%zu bytes)", static_cast<long long>(bytes), which,
                     ctx->bytes[which]);
     DIT_TRY(check_ctx(ctx));
-    const void *p[8] = {ctx->mod, ctx->h, ctx->q, ctx->k, ctx->vt, ctx->o, ctx->h2, ctx->a};
+    const void *p[9] = {ctx->mod, ctx->h, ctx->q, ctx->k, ctx->vt, ctx->o, ctx->h2, ctx->a, ctx->oa};
     if (hipMemcpyAsync(dst, p[which], static_cast<size_t>(bytes), hipMemcpyDeviceToDevice, ctx->stream) != hipSuccess)
         return fail(ctx, DIT_EDEVICE, "debug copy failed");
     return DIT_OK;

@@ -117,7 +117,7 @@ __device__ __forceinline__ void gemm_epilogue(f32x4 (&acc)[TMW][TN], int m0, int
             }
         }
     } else if constexpr (EPI == EPI_SWIGLU) {
-        const int half = N / 2;
+        const int half = ep.ld_act ? ep.ld_act : N / 2;
 #pragma unroll
         for (int tm = 0; tm < TMW; ++tm) {
             __builtin_amdgcn_sched_barrier(0);
@@ -408,7 +408,7 @@ __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, in
             }
         wait_lgkm0();
         pp_barrier();
-        const int half = N / 2;
+        const int half = ep.ld_act ? ep.ld_act : N / 2;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int q = tid + 512 * i, row = q >> 4, c = q & 15;
@@ -571,7 +571,7 @@ __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 }
 }  // namespace
 
-template <int EPI>
+template <int EPI, bool KS>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
           GemmEpi ep) {
@@ -612,23 +612,40 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     const int lrow = lane >> 3;
     const int cE = (lane & 7) ^ (lane >> 4), cO = cE ^ 4;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + static_cast<int64_t>(m0) * K);
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(W + static_cast<int64_t>(n0) * K);
+    // The weight rows of this tile.  Two-weight products: the SwiGLU columns
+    // of EPI_QKV_SWIGLU read the second weight; with KS the k-tiles past
+    // k_split read the second weight's rows (row length K - k_split).
+    bool swi = false;
+    const uint16_t *Wt = W + static_cast<int64_t>(n0) * K;
+    if constexpr (EPI == EPI_QKV_SWIGLU) {
+        swi = n0 >= ep.n_split;
+        if (swi) Wt = ep.w2 + static_cast<int64_t>(n0 - ep.n_split) * K;
+    }
+    const int K1 = KS ? ep.k_split : K, K2 = K - K1, T1 = K1 / BK;
+    if constexpr (KS) Wt = W + static_cast<int64_t>(n0) * K1;
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wt);
+    const __amdgpu_buffer_rsrc_t rW2 = make_rsrc(KS ? ep.w2 + static_cast<int64_t>(n0) * K2 : Wt);
     const int ah = grp ^ 1;                        // the A and W halves this group loads
     // instruction i reads rows 8i (A) or 16i (W, de-interleaved) further
     // down than instruction 0
     const int wrow0 = 128 * ah + (wg < 2 ? 2 * (32 * wg + lrow) : 2 * (32 * wg - 64 + lrow) + 1);
     const uint32_t a_offE = 2u * static_cast<uint32_t>((128 * ah + 32 * wg + lrow) * K + cE * 8);
     const uint32_t a_offO = 2u * static_cast<uint32_t>((128 * ah + 32 * wg + lrow) * K + cO * 8);
-    const uint32_t w_offE = 2u * static_cast<uint32_t>(wrow0 * K + cE * 8);
-    const uint32_t w_offO = 2u * static_cast<uint32_t>(wrow0 * K + cO * 8);
+    const uint32_t w_offE = 2u * static_cast<uint32_t>(wrow0 * K1 + cE * 8);
+    const uint32_t w_offO = 2u * static_cast<uint32_t>(wrow0 * K1 + cO * 8);
+    const uint32_t w2_offE = 2u * static_cast<uint32_t>(wrow0 * K2 + cE * 8);
+    const uint32_t w2_offO = 2u * static_cast<uint32_t>(wrow0 * K2 + cO * 8);
     // load i (0..3) of the W half or the A half this group loads (half
     // grp ^ 1 of both), of k-tile kt.  Past the last k-tile the source is
     // clamped to it: those loads land in a buffer nobody reads any more, and
     // every memory phase issues the same number of loads.
     auto issue_w = [&](int kt, int i) {
         const int ks = min(kt, T - 1);
-        bdma16(rW, (i & 1) ? w_offO : w_offE, 2u * static_cast<uint32_t>(ks * BK + i * 16 * K),
-               Wbuf + (kt & 1) * P3_BUF + (128 * ah + 8 * (4 * wg + i)) * 8);
+        u32x4 *dst = Wbuf + (kt & 1) * P3_BUF + (128 * ah + 8 * (4 * wg + i)) * 8;
+        if (KS && ks >= T1)
+            bdma16(rW2, (i & 1) ? w2_offO : w2_offE, 2u * static_cast<uint32_t>((ks - T1) * BK + i * 16 * K2), dst);
+        else
+            bdma16(rW, (i & 1) ? w_offO : w_offE, 2u * static_cast<uint32_t>(ks * BK + i * 16 * K1), dst);
     };
     auto issue_a = [&](int kt, int i) {
         const int ks = min(kt, T - 1);
@@ -747,7 +764,12 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     wait_vm0();   // no load into LDS may be in flight when the block ends
     pp_barrier();
 
-    pp_epilogue<EPI>(acc, lds, m0, n0, wm, wn, lane, tid, M, N, ep);
+    if constexpr (EPI == EPI_QKV_SWIGLU) {
+        if (swi) pp_epilogue<EPI_SWIGLU>(acc, lds, m0, n0 - ep.n_split, wm, wn, lane, tid, M, N - ep.n_split, ep);
+        else pp_epilogue<EPI_QKV>(acc, lds, m0, n0, wm, wn, lane, tid, M, ep.n_split, ep);
+    } else {
+        pp_epilogue<EPI>(acc, lds, m0, n0, wm, wn, lane, tid, M, N, ep);
+    }
 }
 
 template <int BM, int BN, bool W8>
@@ -774,42 +796,60 @@ static hipError_t launch_cfg(const uint16_t *A, const void *W, const uint16_t *W
     return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool KS = false>
 static hipError_t launch_pp(const uint16_t *A, const uint16_t *W, int M, int N, int K, const GemmEpi &ep,
                             hipStream_t st) {
     const int grid = static_cast<int>(cdiv(M, PP_BM) * cdiv(N, PP_BN));
-    k_gemm_p3<EPI><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
+    k_gemm_p3<EPI, KS><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
     return hipGetLastError();
+}
+
+bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &ep, bool a_rows_padded) {
+    // Large problems: 256x256 tiles (8 waves; ping-pong for bf16 weights when
+    // A's allocation covers whole 256-row tiles and N is a multiple of 256).
+    const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
+    // the ping-pong kernel's staged epilogue moves 16-byte pieces and keeps
+    // the two heads of a QKV tile in one region
+    auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const bool qkv_ok = ep.heads % 2 == 0 && al16(ep.q) && al16(ep.k) && al16(ep.cos) && al16(ep.sin);
+    const bool act_ok = al16(ep.act) && ep.ld_act % 8 == 0;
+    bool epi_ok = false;
+    switch (ep.kind) {
+        case EPI_F32: epi_ok = al16(ep.out) && ep.ldo % 4 == 0; break;
+        case EPI_GATE_RES: epi_ok = al16(ep.out) && ep.ldo % 4 == 0 && al16(ep.gate); break;
+        case EPI_SWIGLU: epi_ok = act_ok; break;
+        case EPI_QKV: epi_ok = qkv_ok; break;
+        case EPI_QKV_SWIGLU:
+            epi_ok = qkv_ok && act_ok && ep.w2 && ep.n_split > 0 && ep.n_split % 256 == 0 && ep.n_split < N;
+            break;
+        default: break;
+    }
+    if (ep.k_split > 0)
+        epi_ok = epi_ok && ep.kind == EPI_GATE_RES && ep.w2 && ep.k_split % BK == 0 && ep.k_split >= 128 &&
+                 K - ep.k_split >= 128;
+    return big_tiles >= 128 && !w8 && epi_ok && K >= 128 && N % 256 == 0 && (a_rows_padded || M % 256 == 0);
 }
 
 hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Ws, bool w8, int M, int N,
                        int K, const GemmEpi &ep, hipStream_t st, bool a_rows_padded) {
     if (M <= 0) return hipSuccess;
-    // Large problems: 256x256 tiles (8 waves; ping-pong for bf16 weights when
-    // A's allocation covers whole 256-row tiles and N is a multiple of 256).
-    // Small ones: 128x128 (2 waves) so the grid still spreads over the chip.
-    const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
-    // the ping-pong kernel's staged epilogue moves 16-byte pieces and keeps
-    // the two heads of a QKV tile in one region
-    auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-    bool epi_ok = false;
-    switch (ep.kind) {
-        case EPI_F32: epi_ok = al16(ep.out) && ep.ldo % 4 == 0; break;
-        case EPI_GATE_RES: epi_ok = al16(ep.out) && ep.ldo % 4 == 0 && al16(ep.gate); break;
-        case EPI_SWIGLU: epi_ok = al16(ep.act); break;
-        case EPI_QKV: epi_ok = ep.heads % 2 == 0 && al16(ep.q) && al16(ep.k) && al16(ep.cos) && al16(ep.sin); break;
-        default: break;
-    }
-    if (big_tiles >= 128 && !w8 && epi_ok && K >= 128 && N % 256 == 0 && (a_rows_padded || M % 256 == 0)) {
+    if (gemm_pingpong_ok(M, N, K, w8, ep, a_rows_padded)) {
         const uint16_t *Wb = static_cast<const uint16_t *>(W);
+        if (ep.k_split > 0) return launch_pp<EPI_GATE_RES, true>(A, Wb, M, N, K, ep, st);
         switch (ep.kind) {
             case EPI_F32: return launch_pp<EPI_F32>(A, Wb, M, N, K, ep, st);
             case EPI_GATE_RES: return launch_pp<EPI_GATE_RES>(A, Wb, M, N, K, ep, st);
             case EPI_SWIGLU: return launch_pp<EPI_SWIGLU>(A, Wb, M, N, K, ep, st);
             case EPI_QKV: return launch_pp<EPI_QKV>(A, Wb, M, N, K, ep, st);
+            case EPI_QKV_SWIGLU: return launch_pp<EPI_QKV_SWIGLU>(A, Wb, M, N, K, ep, st);
             default: return hipErrorInvalidValue;
         }
     }
+    // the two-weight forms exist only as the ping-pong kernel
+    if (ep.kind == EPI_QKV_SWIGLU || ep.k_split > 0) return hipErrorInvalidValue;
+    // otherwise 256x256 tiles with register staging, or for small problems
+    // 128x128 (2 waves) so that the grid still spreads over the chip
+    const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
     if (big_tiles >= 128) {
         return w8 ? launch_cfg<256, 256, true>(A, W, Ws, M, N, K, ep, st)
                   : launch_cfg<256, 256, false>(A, W, Ws, M, N, K, ep, st);

@@ -29,7 +29,7 @@ hipError_t launch_modnorm(const float *x, int rows, int D, const float *shift, c
                           const float *norm_w, bool rms, float eps, uint16_t *out, hipStream_t st);
 
 // ---- products (k_gemm.hip) -------------------------------------------------
-enum EpiKind { EPI_F32 = 0, EPI_GATE_RES = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+enum EpiKind { EPI_F32 = 0, EPI_GATE_RES = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_QKV_SWIGLU = 4 };
 
 struct GemmEpi {
     int kind;
@@ -43,6 +43,16 @@ struct GemmEpi {
     const float *qn, *kn;  // [128] head-norm weights
     const float *cos, *sin;// [M, 64]
     float qk_eps;
+    int ld_act;            // EPI_SWIGLU: row stride of act (0: N/2)
+    // Two-weight products of the parallel block (bf16 weights only):
+    //  EPI_QKV_SWIGLU: columns < n_split take W [n_split, K] and the QKV
+    //    epilogue; columns >= n_split take w2 [N - n_split, K] and the SwiGLU
+    //    epilogue into act (column n_split + c -> act column c/2)
+    //  k_split > 0: k < k_split multiplies W [N, k_split], k >= k_split
+    //    multiplies w2 [N, K - k_split]; A is one [M, K] operand
+    const uint16_t *w2;
+    int n_split;
+    int k_split;
 };
 
 // C = A[M,K] * W[N,K]^T, A bf16; W bf16 (w8 = false) or int8 with bf16
@@ -51,6 +61,9 @@ struct GemmEpi {
 // (rows past M are read and their results discarded).
 hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Wscale, bool w8, int M,
                        int N, int K, const GemmEpi &epi, hipStream_t st, bool a_rows_padded);
+// Whether launch_gemm runs this product as the 256x256 ping-pong kernel (the
+// only one that takes EPI_QKV_SWIGLU and k_split > 0; asked before using them).
+bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &epi, bool a_rows_padded);
 
 // ---- attention (k_attn.hip) ------------------------------------------------
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int heads,

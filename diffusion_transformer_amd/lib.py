@@ -26,7 +26,7 @@ _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, ERANGE, ENOMEM, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 STAGES = ("mod", "norm1", "qkv", "attn", "out", "norm2", "up", "down", "time", "img_in", "final",
-          "euler", "txt_in")
+          "euler", "txt_in", "par_in", "par_out")
 W_BF16, W_INT8_B32 = 0, 1
 NORM_LAYER, NORM_RMS = 0, 1
 _NAMES = {0: "DIT_OK", -1: "DIT_EINVAL", -2: "DIT_ERANGE", -3: "DIT_ENOMEM", -4: "DIT_EDEVICE",
@@ -73,6 +73,7 @@ _SIGS = {
     "dit_linear": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, _P]),
     "dit_attention": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, _P]),
     "dit_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
+    "dit_parallel_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_prologue": (C.c_int, [_P, C.POINTER(Model), _P, C.c_int, _P]),
     "dit_denoise_step": (C.c_int, [_P, C.POINTER(Model), _P, _P, _P, _P, C.c_int, C.c_int,
                                    C.c_float, C.c_float, _P]),
@@ -208,6 +209,12 @@ class Context:
 
     def block_forward(self, block: "BlockWeights", x, vec, cos, sin, L, N):
         self._call("dit_block_forward", C.byref(block.struct), _ptr(x, torch.float32, "x"),
+                   _ptr(vec, torch.float32, "vec"), _ptr(cos, torch.float32, "cos"),
+                   _ptr(sin, torch.float32, "sin"), L, N)
+
+    def parallel_block_forward(self, block: "BlockWeights", x, vec, cos, sin, L, N):
+        """The parallel block ([GZ] Block.parallel); block.w_mod is [3D, D]."""
+        self._call("dit_parallel_block_forward", C.byref(block.struct), _ptr(x, torch.float32, "x"),
                    _ptr(vec, torch.float32, "vec"), _ptr(cos, torch.float32, "cos"),
                    _ptr(sin, torch.float32, "sin"), L, N)
 

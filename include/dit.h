@@ -11,7 +11,7 @@
  *        attention, s.4.4 fused qk-prep.
  *   [GZ] "gizai:dit" module reference: Arch, Block, Modulation, Sequence,
  *        Work, gluRows, gatedInto, normedInto, prepOf, sinusoids,
- *        Block.forward, HEAD, CHUNK.
+ *        Block.forward, Block.parallel, HEAD, CHUNK.
  *
  * Conventions (all entry points):
  *  - Every tensor argument is a DEVICE pointer to caller-owned memory on the
@@ -198,6 +198,19 @@ dit_status dit_attention(dit_ctx *ctx, const uint16_t *q, const uint16_t *k, con
 dit_status dit_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const float *vec,
                              const float *cos, const float *sin, int L, int N);
 
+/* The parallel block ([GZ] Block.parallel): one modulated norm feeds both
+ * the attention and the SwiGLU MLP, and one gate scales their sum:
+ *   (shift, scale, gate) = w_mod * silu(vec)          w_mod bf16 [3D, D]
+ *   h = norm1(x) * (1 + scale) + shift
+ *   x += gate * ( OUT(attention(prep(Q(h)), prep(K(h)), V(h)))
+ *                 + DOWN(swiglu(UP(h))) )
+ * with the same weights, prep, rotary tables and row ranges as
+ * dit_block_forward; NORM2 is not used (RMSNorm needs only NORM1).  For bf16
+ * weights the four products run as two ([QKV | UP] on h, [OUT | DOWN] on the
+ * concatenated [attention output | SwiGLU output] rows). */
+dit_status dit_parallel_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const float *vec,
+                                      const float *cos, const float *sin, int L, int N);
+
 /* Text rows of the sequence, step-invariant ([K4] Appendix B, D2 hoists
  * them out of the Euler loop): txt fp32 [L, D] = ctx_feats * w_txt^T with
  * ctx_feats fp32 [L, text_dim] (taken to bf16 for the product). */
@@ -242,7 +255,9 @@ typedef enum {
     DIT_ST_FINAL = 10,  /* final modulation, norm and product */
     DIT_ST_EULER = 11,  /* Euler update (+ velocity copy) */
     DIT_ST_TXT_IN = 12, /* prologue: text features -> bf16, text-in product */
-    DIT_NSTAGES = 13
+    DIT_ST_PAR_IN = 13, /* parallel block: [QKV | UP] product, both epilogues */
+    DIT_ST_PAR_OUT = 14,/* parallel block: [OUT | DOWN] product + gated residual */
+    DIT_NSTAGES = 15
 } dit_stage;
 
 /* Per-stage timing, a measurement aid ([K4] s.3: every op of the busy time
@@ -266,7 +281,10 @@ dit_status dit_timing_read(dit_ctx *ctx, double *ms, int64_t *count);
  *   2 q    bf16 [H, S, 128]   3 k   bf16 [H, S, 128] (after head norm + rotary)
  *   4 vt   bf16 [H, 128, Sp]  5 o   bf16 [S, D] (attention output)
  *   6 h2   bf16 [S, D]        7 a   bf16 [S, F] (SwiGLU output)
- * Errors: DIT_ERANGE if `which` is outside 0..7 or `bytes` exceeds the
+ *   8 oa   bf16 [S, D + F]   (parallel block with bf16 weights: attention
+ *                             output | SwiGLU output; with int8 weights
+ *                             those are in 5 and 7)
+ * Errors: DIT_ERANGE if `which` is outside 0..8 or `bytes` exceeds the
  * workspace buffer (bytes <= 0 is a no-op). */
 dit_status dit_debug_copy(dit_ctx *ctx, int which, void *dst, int64_t bytes);
 

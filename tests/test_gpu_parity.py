@@ -298,6 +298,85 @@ def test_block_rejects_bad_rows(ctx_tiny):
         assert e.value.status == L.ERANGE
 
 
+# --------------------------------------------------------------- parallel block
+
+def _parallel_case(name, **kw):
+    case = synth.block_case(name, **kw)
+    D = case["shape"].hidden
+    case["block"]["w_mod"] = np.ascontiguousarray(case["block"]["w_mod"][:3 * D])   # shift, scale, gate
+    return case
+
+
+def _parallel_gpu(ctx, case):
+    sh = case["shape"]
+    seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    x = L.dev_f32(case["x"])
+    ctx.parallel_block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    torch.cuda.synchronize()
+    return x
+
+
+@pytest.mark.parametrize("name,norm,norm_std", [("tiny", "layer", 0.0), ("tiny", "rms", 0.1),
+                                                 ("s1088", "layer", 0.0)])
+def test_parallel_block_full_parity(name, norm, norm_std):
+    # below the ping-pong sizes: the four-product form
+    case = _parallel_case(name, norm_std=norm_std, rms=(norm == "rms"))
+    sh = case["shape"]
+    la, oa = arch_pair(sh, norm)
+    ctx = L.Context(la, max_rows=sh.S)
+    say("parallel block", name, norm, "S =", sh.S)
+    got = np_of(_parallel_gpu(ctx, case))
+    D, F = sh.hidden, sh.ffn
+    cs, sn, vec = _oracle_inputs(case, oa)
+    y, ref = O.parallel_block_forward(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, keep=True)
+    compare(f"{name}/mod", np_of(ctx.debug_copy(0, torch.float32, (3, D))), ref["mod"], rel=1e-4, abs_=1e-4)
+    compare(f"{name}/h", np_of(ctx.debug_copy(1, torch.bfloat16, (sh.S, D))), ref["h"], bf16_stored=True)
+    compare(f"{name}/o", np_of(ctx.debug_copy(5, torch.bfloat16, (sh.S, D))), ref["o"], bf16_stored=True)
+    compare(f"{name}/a", np_of(ctx.debug_copy(7, torch.bfloat16, (sh.S, F))), ref["a"], bf16_stored=True)
+    compare(f"{name}/y", got, y)
+    compare(f"{name}/delta", got - case["x"], y - case["x"])
+    ctx.close()
+
+
+@pytest.mark.parametrize("name", ["s4608", "s4608_int8"])
+def test_parallel_block_full_size_sampled_rows(ctx_big, name):
+    # s4608 with bf16 weights runs the two fused products ([QKV | UP] with
+    # both epilogues, [OUT | DOWN] over the concatenated rows); int8 the four
+    case = _parallel_case(name)
+    sh = case["shape"]
+    _, oa = arch_pair(sh)
+    D, F = sh.hidden, sh.ffn
+    say("parallel block", name, "S =", sh.S)
+    got = np_of(_parallel_gpu(ctx_big, case))
+    if sh.int8:
+        o_got = np_of(ctx_big.debug_copy(5, torch.bfloat16, (sh.S, D)))
+        a_got = np_of(ctx_big.debug_copy(7, torch.bfloat16, (sh.S, F)))
+    else:
+        oa_got = np_of(ctx_big.debug_copy(8, torch.bfloat16, (sh.S, D + F)))
+        o_got, a_got = oa_got[:, :D], oa_got[:, D:]
+    cs, sn, vec = _oracle_inputs(case, oa)
+    rows = synth.rows_sample(sh.S, 48, L=sh.L)
+    y, o, a = O.parallel_block_forward_rows(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, rows)
+    # int8 weights: tolerance relative to the reference's largest magnitude
+    # (as for the sequential block's int8 workload)
+    sc = (lambda r: max(1.0, REL * float(np.abs(r).max()) / ABS)) if sh.int8 else (lambda r: 1.0)
+    compare(f"{name}/o", o_got[rows], o, abs_=ABS * sc(o), bf16_stored=True)
+    compare(f"{name}/a", a_got[rows], a, abs_=ABS * sc(a), bf16_stored=True)
+    compare(f"{name}/y", got[rows], y, abs_=ABS * sc(y))
+    d = y - case["x"][rows]
+    compare(f"{name}/delta", got[rows] - case["x"][rows], d, abs_=ABS * sc(d))
+
+
+@pytest.mark.parametrize("name", ["tiny", "s4608"])
+def test_parallel_block_zero_gate_is_identity(ctx_tiny, ctx_big, name):
+    case = _parallel_case(name)
+    D = case["shape"].hidden
+    case["block"]["w_mod"][2 * D:] = 0.0
+    x = _parallel_gpu(ctx_tiny if name == "tiny" else ctx_big, case)
+    assert (np_of(x) == case["x"]).all()
+
+
 # --------------------------------------------------------------- denoise
 
 def test_denoise_twin(ctx_tiny):
