@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-denoise", action="store_true", help="skip the 32-block image timing")
     p.add_argument("--no-int8", action="store_true", help="skip the int8-weight block timing")
+    p.add_argument("--no-parallel", action="store_true", help="skip the parallel-block timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
                         "scale reference for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -68,7 +69,7 @@ def stage_flops(S, D, H, F):
 
 
 STAGE_SOURCE = {"qkv": "k_gemm.hip", "out": "k_gemm.hip", "up": "k_gemm.hip", "down": "k_gemm.hip",
-                "attn": "k_attn.hip", "mod": "k_misc.hip"}
+                "attn": "k_attn.hip", "mod": "k_misc.hip", "par_in": "k_gemm.hip", "par_out": "k_gemm.hip"}
 
 
 def source_sha(name):
@@ -126,9 +127,14 @@ def summarize_counters(fetch_csv, write_csv, out_json):
         pending = None
         for d in order:
             n = names[d]
-            epi = re.search(r"k_gemm_p3<(\d)>", n) or re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
+            pp = re.search(r"k_gemm_p3<(\d), (true|false)>", n)
+            epi = pp or re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
             epi = int(epi.group(1)) if epi else None
-            if epi == 3:
+            if pp and pp.group(2) == "true":
+                stage_of[d] = "par_out"          # parallel block: [OUT | DOWN] over [o | a]
+            elif epi == 4:
+                stage_of[d] = "par_in"           # parallel block: [QKV | UP]
+            elif epi == 3:
                 stage_of[d] = "qkv"
             elif "k_attention" in n:
                 stage_of[d] = "attn"
@@ -158,15 +164,16 @@ def summarize_counters(fetch_csv, write_csv, out_json):
     print(json.dumps(res, indent=1, sort_keys=True))
 
 
-def time_blocks(L, torch, ctx, bw, x, seq, sh, steps, warmup):
+def time_blocks(L, torch, ctx, bw, x, seq, sh, steps, warmup, parallel=False):
+    fwd = ctx.parallel_block_forward if parallel else ctx.block_forward
     for _ in range(warmup):
-        ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        fwd(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     for _ in range(steps):
-        ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        fwd(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
     e1.record(st)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
@@ -241,7 +248,30 @@ def main():
                 "achieved": round(dom_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(args, dom),
                 "flops_per_launch": fl[dom], "avg_ms": round(stages[dom], 4)}
-    del bw, x, case
+    del bw, x
+
+    # ---------------------------------------------------------------- parallel block (bf16)
+    par = None
+    if not args.no_parallel:
+        log("parallel block (one norm, [QKV | UP] and [OUT | DOWN] products)")
+        pb = dict(case["block"])
+        pb["w_mod"] = np.ascontiguousarray(pb["w_mod"][:3 * D])
+        bwp = L.BlockWeights.from_host(pb)
+        xp = L.dev_f32(case["x"])
+        par_flops = total_flops - 2 * 3 * D * D
+        msp = time_blocks(L, torch, ctx, bwp, xp, seq, sh, args.steps, args.warmup, parallel=True)
+        ctx.timing(True)
+        for _ in range(args.steps):
+            ctx.parallel_block_forward(bwp, xp, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        tmp = ctx.timing_read()
+        ctx.timing(False)
+        par_tf = par_flops / (msp * 1e-3) / 1e12
+        par = {"ms": round(msp, 4), "tflops": round(par_tf, 2),
+               "frac_bf16_peak": round(par_tf / PEAK_BF16_TFLOPS, 4), "flops_per_step": par_flops,
+               "stages_ms": {k: round(v[0] / v[1], 4) for k, v in tmp.items() if v[1]}}
+        log(f"parallel block: {msp:.3f} ms  {par_tf:.1f} TFLOP/s")
+        del bwp, xp
+    del case
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- int8 block
@@ -287,6 +317,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
         "int8_block_tflops": None if int8_tf is None else round(int8_tf, 2),
+        "parallel_block": par,
     }
     if img:
         out.update(img)
