@@ -19,7 +19,8 @@ Sources (web pages; cited by title and section):
   [K4]  "944 -> 346 ms: optimizing FLUX.2 klein-4B on one TPU v6e chip":
         s.2 The two inference paths (cast points), s.4.3 Pallas flash
         attention, s.4.4 Fused qk-prep kernel, Appendix B (D3 rope relayout,
-        D3c qk-prep).
+        D3c qk-prep and the double block's per-stream prep, D4 the double
+        blocks' per-stream weight names).
   [GZ]  "gizai:dit" module reference: types Block, Sequence, Modulation;
         functions sinusoids, gluRows, gatedInto, normedInto, prepOf, silu,
         Block.forward, Block.parallel; constants HEAD, QKV/OUT/UP/DOWN.
@@ -36,6 +37,9 @@ equivariance of rows); no page prints a block output.
 `parallel_block_forward` is pinned to the sequential block: its update is
 the sum of the sequential block's attention-only and MLP-only updates (gate
 of the other half zero) under the same shift, scale and gate.
+`double_block_forward` is pinned to it as well: with the same weights in
+both streams it is the sequential block, and with no text rows it is the
+sequential block of the image weights.
 """
 
 from __future__ import annotations
@@ -388,6 +392,52 @@ def parallel_block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, 
     a = swiglu_interleaved(linear(h[rows], bw.w_up))
     y = x[rows] + gate * (linear(o, bw.w_out) + linear(a, bw.w_down))
     return y, o, a
+
+
+def double_block_forward(x, bw_txt: BlockWeights, bw_img: BlockWeights, vec, cos, sin,
+                         arch: Arch, L: int, keep: bool = False):
+    """The double-stream block ([K4] Appendix B, D3c wiring and the D4 key
+    names: text and image streams with their own attention and MLP weights,
+    joint attention over both): rows [0, L) are the text stream, rows [L, S)
+    the image stream.  Each stream takes its own six modulation rows, norms,
+    QKV product and head prep (q/k norms, rotary with its rows of the joint
+    table); the attention runs over all S rows, text rows first; each
+    stream's output, norms and MLP use that stream's weights (each stream is
+    the sequential block's arithmetic on its own rows, with the attention
+    shared).  Returns the new rows (float64) and, with keep=True, the
+    intermediates (h, q, k, v after prep, o, x1, a) over all rows."""
+    x = np.asarray(x, F64)
+    S, D = x.shape
+    H, d = arch.heads, arch.head_dim
+    streams = ((bw_txt, slice(0, L)), (bw_img, slice(L, S)))
+    mods, hs, qs, ks, vs = [], [], [], [], []
+    for bw, r in streams:
+        m = modulation(vec, bw.w_mod, 6)
+        mods.append(m)
+        h = modulated_norm(x[r], m[0], m[1], arch, bw.norm1)
+        qkv = linear(h, bw.w_qkv)
+        qs.append(head_prep(heads_of(qkv[:, 0:H * d], H, d), bw.q_norm, arch.qk_eps, cos[r], sin[r]))
+        ks.append(head_prep(heads_of(qkv[:, H * d:2 * H * d], H, d), bw.k_norm, arch.qk_eps, cos[r], sin[r]))
+        vs.append(heads_of(qkv[:, 2 * H * d:3 * H * d], H, d))
+        hs.append(h)
+    q = np.concatenate(qs, axis=1)
+    k = np.concatenate(ks, axis=1)
+    v = np.concatenate(vs, axis=1)
+    o = attention(q, k, v).transpose(1, 0, 2).reshape(S, H * d)
+    y = np.empty_like(x)
+    x1s, as_ = [], []
+    for (bw, r), m in zip(streams, mods):
+        shift_a, scale_a, gate_a, shift_m, scale_m, gate_m = m
+        x1 = x[r] + gate_a * linear(o[r], bw.w_out)
+        h2 = modulated_norm(x1, shift_m, scale_m, arch, bw.norm2)
+        a = swiglu_interleaved(linear(h2, bw.w_up))
+        y[r] = x1 + gate_m * linear(a, bw.w_down)
+        x1s.append(x1)
+        as_.append(a)
+    if not keep:
+        return y
+    return y, dict(h=np.concatenate(hs), q=q, k=k, v=v, o=o, x1=np.concatenate(x1s),
+                   a=np.concatenate(as_))
 
 
 # ---------------------------------------------------------------------------

@@ -468,6 +468,53 @@ def test_parallel_block_flops():
     assert d == 2 * 3 * 3072 * 3072
 
 
+# ---------------------------------------------------------------- double-stream block
+
+def _double(Wt, Wi, pos, x, vecc, L, arch=TINY):
+    c, s = O.rope_tables(pos, arch.axes)
+    return O.double_block_forward(x, O.BlockWeights(**Wt), O.BlockWeights(**Wi), vecc, c, s, arch, L)
+
+
+@pytest.mark.parametrize("rms", [False, True])
+def test_double_block_same_weights_is_sequential_block(rms):
+    # one weight set in both streams: every step is row-wise except the
+    # attention, which is joint in both forms -- the sequential block
+    arch = O.Arch(16, 2, 8, 12, axes=(2, 2, 4), norm="rms" if rms else "layer")
+    W, pos, x, vecc = _tiny_case(seed=31, S_L=3, rms=rms)
+    y = _double(W, W, pos, x, vecc, 3, arch)
+    ref = _oracle_block(W, pos, x, vecc, arch)
+    assert np.abs(y - ref).max() < 1e-12, np.abs(y - ref).max()
+
+
+def test_double_block_streams_use_their_own_weights():
+    Wt, pos, x, vecc = _tiny_case(seed=32, S_L=3)
+    Wi, _, _, _ = _tiny_case(seed=33, S_L=3)
+    L = 3
+    y = _double(Wt, Wi, pos, x, vecc, L)
+    # no text rows: the sequential block of the image weights
+    c, s = O.rope_tables(pos[L:], TINY.axes)
+    y0 = O.double_block_forward(x[L:], O.BlockWeights(**Wt), O.BlockWeights(**Wi), vecc, c, s, TINY, 0)
+    assert np.abs(y0 - _oracle_block(Wi, pos[L:], x[L:], vecc, TINY)).max() < 1e-12
+    # changing the text MLP moves text rows only; changing the image MLP image rows only
+    Wt2 = dict(Wt); Wt2["w_down"] = Wt["w_down"] * 2.0
+    y2 = _double(Wt2, Wi, pos, x, vecc, L)
+    assert (y2[L:] == y[L:]).all() and not np.allclose(y2[:L], y[:L])
+    Wi2 = dict(Wi); Wi2["w_up"] = Wi["w_up"][::-1].copy()
+    y3 = _double(Wt, Wi2, pos, x, vecc, L)
+    assert (y3[:L] == y[:L]).all() and not np.allclose(y3[L:], y[L:])
+    # the attention is joint: changing the text QKV moves image rows too
+    Wt4 = dict(Wt); Wt4["w_qkv"] = Wt["w_qkv"] * 1.5
+    y4 = _double(Wt4, Wi, pos, x, vecc, L)
+    assert not np.allclose(y4[L:], y[L:])
+
+
+def test_double_block_zero_modulation_is_identity():
+    Wt, pos, x, vecc = _tiny_case(seed=34)
+    Wi, _, _, _ = _tiny_case(seed=35)
+    Wt["w_mod"] = np.zeros_like(Wt["w_mod"]); Wi["w_mod"] = np.zeros_like(Wi["w_mod"])
+    assert (_double(Wt, Wi, pos, x, vecc, 2) == x).all()
+
+
 # ---------------------------------------------------------------- time vector, modulation
 
 def test_time_vector_brute_force():
