@@ -340,6 +340,106 @@ dit_status parallel_block_forward(dit_ctx *c, const dit_block *b, float *x, cons
     return DIT_OK;
 }
 
+// The double-stream block's launch sequence ([K4] Appendix B, double blocks;
+// validated arguments): rows [0, L) take the text stream's weights and
+// modulation, rows [L, S) the image stream's; each product runs once per
+// stream over its rows (the image stream's from row L of the operands; QKV
+// writes q, k and vt at the stream's row offset), the attention once over
+// all rows.  The modulation buffer holds the text stream's six rows, then
+// the image stream's.
+dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block *bi, float *x, const float *vec,
+                                const float *cs, const float *sn, int L, int N) {
+    const dit_arch &A = c->arch;
+    const int D = A.hidden, F = A.ffn, H = A.heads;
+    const int S = L + N, Sp = round_up(S, 64);
+    const bool rms = A.norm == DIT_NORM_RMS;
+    hipStream_t st = c->stream;
+    struct Stream {
+        const dit_block *b;
+        int r0, rows;
+        float *mod;
+    };
+    const Stream sts[2] = {{bt, 0, L, c->mod}, {bi, L, N, c->mod + 6 * D}};
+    for (const Stream &t : sts) {
+        Stage tm(c, DIT_ST_MOD);
+        DIT_LAUNCH(c, launch_gemv(t.b->w_mod, vec, 6 * D, D, true, t.mod, st), "modulation");
+    }
+    for (const Stream &t : sts) {
+        if (!t.rows) continue;
+        Stage tm(c, DIT_ST_NORM1);
+        DIT_LAUNCH(c, launch_modnorm(x + int64_t(t.r0) * D, t.rows, D, t.mod, t.mod + D, t.b->norm_w[0], rms, A.eps,
+                                     c->h + int64_t(t.r0) * D, st),
+                   "norm1");
+    }
+    for (const Stream &t : sts) {
+        if (!t.rows) continue;
+        const bool w8 = t.b->wtype == DIT_W_INT8_B32;
+        GemmEpi e{};
+        e.kind = EPI_QKV;
+        e.q = c->q;
+        e.k = c->k;
+        e.vt = c->vt;
+        e.heads = H;
+        e.ldv = Sp;
+        e.qn = t.b->norm_w[2];
+        e.kn = t.b->norm_w[3];
+        e.cos = cs + int64_t(t.r0) * 64;
+        e.sin = sn + int64_t(t.r0) * 64;
+        e.qk_eps = A.qk_eps;
+        e.row_base = t.r0;
+        e.rows_total = S;
+        Stage tm(c, DIT_ST_QKV);
+        DIT_LAUNCH(c, launch_gemm(c->h + int64_t(t.r0) * D, t.b->w[0], t.b->scale[0], w8, t.rows, 3 * D, D, e, st, true),
+                   "qkv");
+    }
+    {
+        Stage tm(c, DIT_ST_ATTN);
+        DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
+    }
+    for (const Stream &t : sts) {
+        if (!t.rows) continue;
+        const bool w8 = t.b->wtype == DIT_W_INT8_B32;
+        GemmEpi g{};
+        g.kind = EPI_GATE_RES;
+        g.out = x + int64_t(t.r0) * D;
+        g.ldo = D;
+        g.gate = t.mod + 2 * D;
+        Stage tm(c, DIT_ST_OUT);
+        DIT_LAUNCH(c, launch_gemm(c->o + int64_t(t.r0) * D, t.b->w[1], t.b->scale[1], w8, t.rows, D, D, g, st, true),
+                   "out");
+    }
+    for (const Stream &t : sts) {
+        if (!t.rows) continue;
+        Stage tm(c, DIT_ST_NORM2);
+        DIT_LAUNCH(c, launch_modnorm(x + int64_t(t.r0) * D, t.rows, D, t.mod + 3 * D, t.mod + 4 * D, t.b->norm_w[1], rms,
+                                     A.eps, c->h2 + int64_t(t.r0) * D, st),
+                   "norm2");
+    }
+    for (const Stream &t : sts) {
+        if (!t.rows) continue;
+        const bool w8 = t.b->wtype == DIT_W_INT8_B32;
+        GemmEpi u{};
+        u.kind = EPI_SWIGLU;
+        u.act = c->a + int64_t(t.r0) * F;
+        Stage tm(c, DIT_ST_UP);
+        DIT_LAUNCH(c, launch_gemm(c->h2 + int64_t(t.r0) * D, t.b->w[2], t.b->scale[2], w8, t.rows, 2 * F, D, u, st, true),
+                   "up");
+    }
+    for (const Stream &t : sts) {
+        if (!t.rows) continue;
+        const bool w8 = t.b->wtype == DIT_W_INT8_B32;
+        GemmEpi g{};
+        g.kind = EPI_GATE_RES;
+        g.out = x + int64_t(t.r0) * D;
+        g.ldo = D;
+        g.gate = t.mod + 5 * D;
+        Stage tm(c, DIT_ST_DOWN);
+        DIT_LAUNCH(c, launch_gemm(c->a + int64_t(t.r0) * F, t.b->w[3], t.b->scale[3], w8, t.rows, D, F, g, st, true),
+                   "down");
+    }
+    return DIT_OK;
+}
+
 dit_status time_vector(dit_ctx *c, const uint16_t *w1, const uint16_t *w2, float t, float *vec) {
     const dit_arch &A = c->arch;
     hipStream_t st = c->stream;
@@ -396,11 +496,14 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
     c->max_rows_pad = round_up(max_rows, 256);   // whole 256-row product tiles
 
     const size_t S = c->max_rows_pad, D = arch->hidden, F = arch->ffn, H = arch->heads;
+    // h, h2, o, a: one more 256-row tile, read (not used) when the double-
+    // stream block runs the image rows as a product starting at row L
+    const size_t Sx = S + 256;
     const size_t sizes[] = {
-        6 * D * 4, D * 4, size_t(arch->time_dim) * 4, D * 4, 2 * D * 4,  // mod vec temb t1 fmod
-        S * D * 2, S * D * 2,                                          // h h2
+        12 * D * 4, D * 4, size_t(arch->time_dim) * 4, D * 4, 2 * D * 4,  // mod (2 x 6 rows) vec temb t1 fmod
+        Sx * D * 2, Sx * D * 2,                                        // h h2
         H * S * 128 * 2, H * S * 128 * 2, H * 128 * S * 2,             // q k vt
-        S * D * 2, S * F * 2,                                          // o a
+        Sx * D * 2, Sx * F * 2,                                        // o a
         S * size_t(arch->latent) * 2, S * size_t(arch->text_dim) * 2,  // latb ctxb
         S * D * 4, S * size_t(arch->latent) * 4,                       // seq vel
         S * (D + F) * 2,                                               // oa
@@ -588,6 +691,17 @@ dit_status dit_parallel_block_forward(dit_ctx *ctx, const dit_block *b, float *x
     DIT_TRY(check_rows(ctx, L, N));
     DIT_TRY(check_ctx(ctx));
     return parallel_block_forward(ctx, b, x, vec, cos_t, sin_t, L + N);
+}
+
+dit_status dit_double_block_forward(dit_ctx *ctx, const dit_block *txt, const dit_block *img, float *x,
+                                    const float *vec, const float *cos_t, const float *sin_t, int L, int N) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
+    DIT_TRY(check_block(ctx, txt));
+    DIT_TRY(check_block(ctx, img));
+    DIT_TRY(check_rows(ctx, L, N));
+    DIT_TRY(check_ctx(ctx));
+    return double_block_forward(ctx, txt, img, x, vec, cos_t, sin_t, L, N);
 }
 
 dit_status dit_prologue(dit_ctx *ctx, const dit_model *m, const float *ctx_feats, int L, float *txt) {

@@ -78,6 +78,24 @@ __device__ __forceinline__ void dequant16(u32x4 q, float s, u32x4 &lo, u32x4 &hi
 
 }  // namespace
 
+// Four consecutive rows of two value features into V^T (d0: feature 2p,
+// d1: feature 2p+1): col is the first row's column in vt, valid the number
+// of those rows that exist.  Whole aligned groups leave as 8-byte stores,
+// others one bf16 at a time (a stream's first or last rows).
+__device__ __forceinline__ void store_v4(uint16_t *d0, uint16_t *d1, f32x4 e, f32x4 o, int col, int valid) {
+    if (valid >= 4 && (col & 3) == 0) {
+        *reinterpret_cast<u32x2 *>(d0) = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
+        *reinterpret_cast<u32x2 *>(d1) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (r < valid) {
+                d0[r] = f32_to_bf16(e[r]);
+                d1[r] = f32_to_bf16(o[r]);
+            }
+    }
+}
+
 // Epilogue shared by the products (wave tile TMW*16 rows x 128 columns).
 // Lane holds rows m0 + wm*TMW*16 + tm*16 + 4*(lane>>4) + r and output pairs
 // P = (n0 + wn*128)/2 + tp*16 + (lane & 15): column 2P in acc[tm][tp][r],
@@ -175,7 +193,8 @@ __device__ __forceinline__ void gemm_epilogue(f32x4 (&acc)[TMW][TN], int m0, int
                         const float b = acc[tm][tp + TN / 2][r] * rstd * wo[tp];
                         if (row < M)
                             *reinterpret_cast<uint32_t *>(
-                                dst + (static_cast<int64_t>(head) * M + row) * 128 + 2 * p) =
+                                dst + (static_cast<int64_t>(head) * (ep.rows_total ? ep.rows_total : M) +
+                                       ep.row_base + row) * 128 + 2 * p) =
                                 pack_bf16x2(a * c - b * s, a * s + b * c);
                     }
                 }
@@ -184,15 +203,13 @@ __device__ __forceinline__ void gemm_epilogue(f32x4 (&acc)[TMW][TN], int m0, int
 #pragma unroll
             for (int tm = 0; tm < TMW; ++tm) {
                 const int row0 = rbase + tm * 16;
-                if (row0 >= ep.ldv) continue;
+                if (row0 >= M) continue;
 #pragma unroll
                 for (int tp = 0; tp < TN / 2; ++tp) {
                     const int p = tp * 16 + pl;
-                    uint16_t *d0 = ep.vt + (static_cast<int64_t>(head) * 128 + 2 * p) * ep.ldv + row0;
-                    uint16_t *d1 = d0 + ep.ldv;
+                    uint16_t *d0 = ep.vt + (static_cast<int64_t>(head) * 128 + 2 * p) * ep.ldv + ep.row_base + row0;
                     const f32x4 e = acc[tm][tp], o = acc[tm][tp + TN / 2];
-                    *reinterpret_cast<u32x2 *>(d0) = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
-                    *reinterpret_cast<u32x2 *>(d1) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                    store_v4(d0, d0 + ep.ldv, e, o, ep.row_base + row0, M - row0);
                 }
             }
         }
@@ -428,14 +445,13 @@ __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, in
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) {
                     const int row0 = m0 + wm * 64 + tm * 16 + 4 * g;
-                    if (row0 >= ep.ldv) continue;
+                    if (row0 >= M) continue;
 #pragma unroll
                     for (int tp = 0; tp < TN / 2; ++tp) {
                         const int p = tp * 16 + pl;
-                        uint16_t *d0 = ep.vt + (static_cast<int64_t>(head) * 128 + 2 * p) * ep.ldv + row0;
+                        uint16_t *d0 = ep.vt + (static_cast<int64_t>(head) * 128 + 2 * p) * ep.ldv + ep.row_base + row0;
                         const f32x4 e = acc[tm][tp], o = acc[tm][tp + TN / 2];
-                        *reinterpret_cast<u32x2 *>(d0) = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
-                        *reinterpret_cast<u32x2 *>(d0 + ep.ldv) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                        store_v4(d0, d0 + ep.ldv, e, o, ep.row_base + row0, M - row0);
                     }
                 }
                 return;
@@ -508,7 +524,8 @@ __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, in
                                      pack_bf16x2(v0[2] * cs[1] - v0[3] * sn[1], v0[2] * sn[1] + v0[3] * cs[1]),
                                      pack_bf16x2(v1[0] * cs[2] - v1[1] * sn[2], v1[0] * sn[2] + v1[1] * cs[2]),
                                      pack_bf16x2(v1[2] * cs[3] - v1[3] * sn[3], v1[2] * sn[3] + v1[3] * cs[3])};
-                    *reinterpret_cast<u32x4 *>(dst + (static_cast<int64_t>(head) * M + grow) * 128 + 2 * p0) = o;
+                    *reinterpret_cast<u32x4 *>(dst + (static_cast<int64_t>(head) * (ep.rows_total ? ep.rows_total : M) +
+                                                      ep.row_base + grow) * 128 + 2 * p0) = o;
                 }
             } else {
                 // thread -> 4 consecutive columns, rows tid/64 + 8i: one gate chunk

@@ -53,6 +53,12 @@ struct GemmEpi {
     const uint16_t *w2;
     int n_split;
     int k_split;
+    // EPI_QKV over a row range of a longer sequence (the double-stream
+    // block's streams): local row r is row row_base + r of q, k ([H,
+    // rows_total, 128]; rows_total 0 means M) and column row_base + r of vt;
+    // cos and sin are passed already offset to row_base.
+    int row_base;
+    int rows_total;
 };
 
 // C = A[M,K] * W[N,K]^T, A bf16; W bf16 (w8 = false) or int8 with bf16

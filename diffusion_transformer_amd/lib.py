@@ -74,6 +74,8 @@ _SIGS = {
     "dit_attention": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, _P]),
     "dit_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_parallel_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
+    "dit_double_block_forward": (C.c_int, [_P, C.POINTER(Block), C.POINTER(Block), _P, _P, _P, _P, C.c_int,
+                                           C.c_int]),
     "dit_prologue": (C.c_int, [_P, C.POINTER(Model), _P, C.c_int, _P]),
     "dit_denoise_step": (C.c_int, [_P, C.POINTER(Model), _P, _P, _P, _P, C.c_int, C.c_int,
                                    C.c_float, C.c_float, _P]),
@@ -217,6 +219,12 @@ class Context:
         self._call("dit_parallel_block_forward", C.byref(block.struct), _ptr(x, torch.float32, "x"),
                    _ptr(vec, torch.float32, "vec"), _ptr(cos, torch.float32, "cos"),
                    _ptr(sin, torch.float32, "sin"), L, N)
+
+    def double_block_forward(self, txt: "BlockWeights", img: "BlockWeights", x, vec, cos, sin, L, N):
+        """The double-stream block: rows [0, L) take `txt`, the rest `img`."""
+        self._call("dit_double_block_forward", C.byref(txt.struct), C.byref(img.struct),
+                   _ptr(x, torch.float32, "x"), _ptr(vec, torch.float32, "vec"),
+                   _ptr(cos, torch.float32, "cos"), _ptr(sin, torch.float32, "sin"), L, N)
 
     def prologue(self, model: "ModelWeights", ctx_feats, L, txt):
         self._call("dit_prologue", C.byref(model.struct), _ptr(ctx_feats, torch.float32, "ctx"),

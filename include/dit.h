@@ -211,6 +211,18 @@ dit_status dit_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const f
 dit_status dit_parallel_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const float *vec,
                                       const float *cos, const float *sin, int L, int N);
 
+/* The double-stream block ([K4] Appendix B: the FLUX.2 double blocks, one
+ * set of attention and MLP weights per stream, the q/k preparation run per
+ * stream with its rows of the joint rotary table, the attention joint):
+ * rows [0, L) of x are the text stream and use `txt` (its w_mod [6D, D],
+ * norms, head norms and the four linears), rows [L, L+N) the image stream
+ * and use `img`; each stream's rows get exactly dit_block_forward's
+ * arithmetic with its own weights, except that the attention runs once
+ * over all L + N rows (text first).  Both blocks must have the same wtype
+ * rules as dit_block_forward; arguments and errors as dit_block_forward. */
+dit_status dit_double_block_forward(dit_ctx *ctx, const dit_block *txt, const dit_block *img, float *x,
+                                    const float *vec, const float *cos, const float *sin, int L, int N);
+
 /* Text rows of the sequence, step-invariant ([K4] Appendix B, D2 hoists
  * them out of the Euler loop): txt fp32 [L, D] = ctx_feats * w_txt^T with
  * ctx_feats fp32 [L, text_dim] (taken to bf16 for the product). */
@@ -278,6 +290,8 @@ dit_status dit_timing_read(dit_ctx *ctx, double *ms, int64_t *count);
  * uses the workspace.  Buffers, packed for that call's S = L + N with
  * Sp = S rounded up to 64:
  *   0 mod  fp32 [6, D]        1 h   bf16 [S, D] (norm1 output)
+ *          (double-stream block: [12, D], the text stream's six rows
+ *          then the image stream's)
  *   2 q    bf16 [H, S, 128]   3 k   bf16 [H, S, 128] (after head norm + rotary)
  *   4 vt   bf16 [H, 128, Sp]  5 o   bf16 [S, D] (attention output)
  *   6 h2   bf16 [S, D]        7 a   bf16 [S, F] (SwiGLU output)

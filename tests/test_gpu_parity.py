@@ -377,6 +377,64 @@ def test_parallel_block_zero_gate_is_identity(ctx_tiny, ctx_big, name):
     assert (np_of(x) == case["x"]).all()
 
 
+# --------------------------------------------------------------- double-stream block
+
+def _double_case(name):
+    # the image stream takes the workload's block, the text stream a second
+    # draw of the same shapes (another seed)
+    case = synth.block_case(name)
+    other = synth.block_case(name, seed=case["shape"].seed + 100)
+    case["txt_block"] = other["block"]
+    return case
+
+
+def _double_gpu(ctx, case):
+    sh = case["shape"]
+    seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
+    bt = L.BlockWeights.from_host(case["txt_block"])
+    bi = L.BlockWeights.from_host(case["block"])
+    x = L.dev_f32(case["x"])
+    ctx.double_block_forward(bt, bi, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    torch.cuda.synchronize()
+    return x
+
+
+@pytest.mark.parametrize("name", ["tiny", "s1088", "s4608"])
+def test_double_block_full_parity(ctx_big, name):
+    case = _double_case(name)
+    sh = case["shape"]
+    la, oa = arch_pair(sh)
+    ctx = ctx_big if name == "s4608" else L.Context(la, max_rows=sh.S)
+    say("double block", name, "L =", sh.L, "N =", sh.N)
+    got = np_of(_double_gpu(ctx, case))
+    D, F, H = sh.hidden, sh.ffn, sh.heads
+    S, Sp = sh.S, (sh.S + 63) // 64 * 64
+    cs, sn, vec = _oracle_inputs(case, oa)
+    y, ref = O.double_block_forward(case["x"], oracle_block(case["txt_block"]), oracle_block(case["block"]),
+                                    vec, cs, sn, oa, sh.L, keep=True)
+    mods = np_of(ctx.debug_copy(0, torch.float32, (12, D)))
+    compare(f"{name}/mod-txt", mods[:6], O.modulation(vec, case["txt_block"]["w_mod"], 6), rel=1e-4, abs_=1e-4)
+    compare(f"{name}/mod-img", mods[6:], O.modulation(vec, case["block"]["w_mod"], 6), rel=1e-4, abs_=1e-4)
+    compare(f"{name}/h", np_of(ctx.debug_copy(1, torch.bfloat16, (S, D))), ref["h"], bf16_stored=True)
+    compare(f"{name}/q", np_of(ctx.debug_copy(2, torch.bfloat16, (H, S, 128))), ref["q"], bf16_stored=True)
+    compare(f"{name}/k", np_of(ctx.debug_copy(3, torch.bfloat16, (H, S, 128))), ref["k"], bf16_stored=True)
+    v = np_of(ctx.debug_copy(4, torch.bfloat16, (H, 128, Sp)))[:, :, :S].transpose(0, 2, 1)
+    compare(f"{name}/v", v, ref["v"], bf16_stored=True)
+    compare(f"{name}/o", np_of(ctx.debug_copy(5, torch.bfloat16, (S, D))), ref["o"], bf16_stored=True)
+    compare(f"{name}/a", np_of(ctx.debug_copy(7, torch.bfloat16, (S, F))), ref["a"], bf16_stored=True)
+    compare(f"{name}/y", got, y)
+    compare(f"{name}/delta", got - case["x"], y - case["x"])
+    if ctx is not ctx_big:
+        ctx.close()
+
+
+def test_double_block_zero_modulation_is_identity(ctx_tiny):
+    case = _double_case("tiny")
+    case["block"]["w_mod"][:] = 0.0
+    case["txt_block"]["w_mod"][:] = 0.0
+    assert (np_of(_double_gpu(ctx_tiny, case)) == case["x"]).all()
+
+
 # --------------------------------------------------------------- denoise
 
 def test_denoise_twin(ctx_tiny):
