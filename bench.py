@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--no-denoise", action="store_true", help="skip the 32-block image timing")
     p.add_argument("--no-int8", action="store_true", help="skip the int8-weight block timing")
     p.add_argument("--no-parallel", action="store_true", help="skip the parallel-block timing")
+    p.add_argument("--no-double", action="store_true", help="skip the double-stream block timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
                         "scale reference for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -271,6 +272,40 @@ def main():
                "stages_ms": {k: round(v[0] / v[1], 4) for k, v in tmp.items() if v[1]}}
         log(f"parallel block: {msp:.3f} ms  {par_tf:.1f} TFLOP/s")
         del bwp, xp
+
+    # ---------------------------------------------------------------- double-stream block (bf16)
+    dbl = None
+    if not args.no_double:
+        log("double-stream block (text and image weights, joint attention)")
+        other = synth.block_case("s4608", seed=sh.seed + 100)
+        bwt = L.BlockWeights.from_host(other["block"])
+        bwi = L.BlockWeights.from_host(case["block"])
+        xd = L.dev_f32(case["x"])
+        dbl_flops = total_flops + 2 * 6 * D * D          # a second modulation GEMV
+
+        def dfwd():
+            ctx.double_block_forward(bwt, bwi, xd, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        for _ in range(args.warmup):
+            dfwd()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            dfwd()
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        msd = e0.elapsed_time(e1) / args.steps
+        ctx.timing(True)
+        for _ in range(args.steps):
+            dfwd()
+        tmd = ctx.timing_read()
+        ctx.timing(False)
+        dbl_tf = dbl_flops / (msd * 1e-3) / 1e12
+        dbl = {"ms": round(msd, 4), "tflops": round(dbl_tf, 2),
+               "frac_bf16_peak": round(dbl_tf / PEAK_BF16_TFLOPS, 4), "flops_per_step": dbl_flops,
+               "stages_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in tmd.items() if v[1]}}
+        log(f"double-stream block: {msd:.3f} ms  {dbl_tf:.1f} TFLOP/s")
+        del bwt, bwi, xd, other
     del case
     torch.cuda.empty_cache()
 
@@ -318,6 +353,7 @@ def main():
         "roofline": roofline,
         "int8_block_tflops": None if int8_tf is None else round(int8_tf, 2),
         "parallel_block": par,
+        "double_block": dbl,
     }
     if img:
         out.update(img)

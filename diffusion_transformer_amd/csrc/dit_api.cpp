@@ -371,42 +371,60 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
                                      c->h + int64_t(t.r0) * D, st),
                    "norm1");
     }
-    for (const Stream &t : sts) {
-        if (!t.rows) continue;
-        const bool w8 = t.b->wtype == DIT_W_INT8_B32;
-        GemmEpi e{};
-        e.kind = EPI_QKV;
-        e.q = c->q;
-        e.k = c->k;
-        e.vt = c->vt;
-        e.heads = H;
-        e.ldv = Sp;
-        e.qn = t.b->norm_w[2];
-        e.kn = t.b->norm_w[3];
-        e.cos = cs + int64_t(t.r0) * 64;
-        e.sin = sn + int64_t(t.r0) * 64;
-        e.qk_eps = A.qk_eps;
-        e.row_base = t.r0;
-        e.rows_total = S;
+    // one launch per product for both streams (image tiles first) when both
+    // take the ping-pong kernel; int8 weights of either stream: two launches
+    const bool w8 = bt->wtype == DIT_W_INT8_B32 || bi->wtype == DIT_W_INT8_B32;
+    auto two = [&](int kind, const uint16_t *a_base, int64_t a_ld, const GemmEpi (&ep)[2], int w, int n, int k) {
+        const Stream &ti = sts[1], &tt = sts[0];
+        if (w8) {
+            hipError_t e = hipSuccess;
+            for (int i = 1; i >= 0 && e == hipSuccess; --i) {
+                const Stream &t = sts[i];
+                if (t.rows)
+                    e = launch_gemm(a_base + int64_t(t.r0) * a_ld, t.b->w[w], t.b->scale[w], t.b->wtype == DIT_W_INT8_B32,
+                                    t.rows, n, k, ep[i], st, true);
+            }
+            return e;
+        }
+        (void)kind;
+        return launch_gemm2(a_base + int64_t(ti.r0) * a_ld, ti.b->w[w], nullptr, ti.rows, ep[1],
+                            a_base + int64_t(tt.r0) * a_ld, tt.b->w[w], nullptr, tt.rows, ep[0], false, n, k, st);
+    };
+    {
+        GemmEpi e[2]{};
+        for (int i = 0; i < 2; ++i) {
+            const Stream &t = sts[i];
+            e[i].kind = EPI_QKV;
+            e[i].q = c->q;
+            e[i].k = c->k;
+            e[i].vt = c->vt;
+            e[i].heads = H;
+            e[i].ldv = Sp;
+            e[i].qn = t.b->norm_w[2];
+            e[i].kn = t.b->norm_w[3];
+            e[i].cos = cs + int64_t(t.r0) * 64;
+            e[i].sin = sn + int64_t(t.r0) * 64;
+            e[i].qk_eps = A.qk_eps;
+            e[i].row_base = t.r0;
+            e[i].rows_total = S;
+        }
         Stage tm(c, DIT_ST_QKV);
-        DIT_LAUNCH(c, launch_gemm(c->h + int64_t(t.r0) * D, t.b->w[0], t.b->scale[0], w8, t.rows, 3 * D, D, e, st, true),
-                   "qkv");
+        DIT_LAUNCH(c, two(EPI_QKV, c->h, D, e, 0, 3 * D, D), "qkv");
     }
     {
         Stage tm(c, DIT_ST_ATTN);
         DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
     }
-    for (const Stream &t : sts) {
-        if (!t.rows) continue;
-        const bool w8 = t.b->wtype == DIT_W_INT8_B32;
-        GemmEpi g{};
-        g.kind = EPI_GATE_RES;
-        g.out = x + int64_t(t.r0) * D;
-        g.ldo = D;
-        g.gate = t.mod + 2 * D;
+    {
+        GemmEpi g[2]{};
+        for (int i = 0; i < 2; ++i) {
+            g[i].kind = EPI_GATE_RES;
+            g[i].out = x + int64_t(sts[i].r0) * D;
+            g[i].ldo = D;
+            g[i].gate = sts[i].mod + 2 * D;
+        }
         Stage tm(c, DIT_ST_OUT);
-        DIT_LAUNCH(c, launch_gemm(c->o + int64_t(t.r0) * D, t.b->w[1], t.b->scale[1], w8, t.rows, D, D, g, st, true),
-                   "out");
+        DIT_LAUNCH(c, two(EPI_GATE_RES, c->o, D, g, 1, D, D), "out");
     }
     for (const Stream &t : sts) {
         if (!t.rows) continue;
@@ -415,27 +433,25 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
                                      A.eps, c->h2 + int64_t(t.r0) * D, st),
                    "norm2");
     }
-    for (const Stream &t : sts) {
-        if (!t.rows) continue;
-        const bool w8 = t.b->wtype == DIT_W_INT8_B32;
-        GemmEpi u{};
-        u.kind = EPI_SWIGLU;
-        u.act = c->a + int64_t(t.r0) * F;
+    {
+        GemmEpi u[2]{};
+        for (int i = 0; i < 2; ++i) {
+            u[i].kind = EPI_SWIGLU;
+            u[i].act = c->a + int64_t(sts[i].r0) * F;
+        }
         Stage tm(c, DIT_ST_UP);
-        DIT_LAUNCH(c, launch_gemm(c->h2 + int64_t(t.r0) * D, t.b->w[2], t.b->scale[2], w8, t.rows, 2 * F, D, u, st, true),
-                   "up");
+        DIT_LAUNCH(c, two(EPI_SWIGLU, c->h2, D, u, 2, 2 * F, D), "up");
     }
-    for (const Stream &t : sts) {
-        if (!t.rows) continue;
-        const bool w8 = t.b->wtype == DIT_W_INT8_B32;
-        GemmEpi g{};
-        g.kind = EPI_GATE_RES;
-        g.out = x + int64_t(t.r0) * D;
-        g.ldo = D;
-        g.gate = t.mod + 5 * D;
+    {
+        GemmEpi g[2]{};
+        for (int i = 0; i < 2; ++i) {
+            g[i].kind = EPI_GATE_RES;
+            g[i].out = x + int64_t(sts[i].r0) * D;
+            g[i].ldo = D;
+            g[i].gate = sts[i].mod + 5 * D;
+        }
         Stage tm(c, DIT_ST_DOWN);
-        DIT_LAUNCH(c, launch_gemm(c->a + int64_t(t.r0) * F, t.b->w[3], t.b->scale[3], w8, t.rows, D, F, g, st, true),
-                   "down");
+        DIT_LAUNCH(c, two(EPI_GATE_RES, c->a, F, g, 3, D, F), "down");
     }
     return DIT_OK;
 }

@@ -591,7 +591,7 @@ __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 template <int EPI, bool KS>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
-          GemmEpi ep) {
+          GemmEpi ep, const uint16_t *__restrict__ A2, const uint16_t *__restrict__ W2, int M2, GemmEpi ep2) {
     constexpr int BM = PP_BM, BN = PP_BN;
     __shared__ u32x4 lds[(P3_NA + P3_NW) * P3_BUF];   // 160 KB
     u32x4 *const Abuf = lds;
@@ -602,13 +602,25 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     const int grp = wave >> 2, wg = wave & 3;     // group 0: waves 0-3, group 1: waves 4-7
     const int wm = wg, wn = grp;                  // wave tile (wm*64, wn*128)
 
-    const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
-    const int total = ntm * ntn;
+    // Two products can share a launch (the double-stream block's streams:
+    // same N and K, their own rows, weights and epilogue): tiles past the
+    // first product's are the second's.
+    const int ntn = (N + BN - 1) / BN;
+    const int T0 = ((M + BM - 1) / BM) * ntn;
+    const int total = T0 + ((M2 + BM - 1) / BM) * ntn;
     int bid = blockIdx.x;
     {
         const int per = total / 8, rem = total % 8, xcd = bid % 8, loc = bid / 8;
         bid = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
     }
+    if (bid >= T0) {
+        bid -= T0;
+        A = A2;
+        W = W2;
+        M = M2;
+        ep = ep2;
+    }
+    const int ntm = (M + BM - 1) / BM;
     constexpr int GM = 8;
     const int group = bid / (GM * ntn), first = group * GM;
     const int gsz = min(ntm - first, GM);
@@ -817,7 +829,16 @@ template <int EPI, bool KS = false>
 static hipError_t launch_pp(const uint16_t *A, const uint16_t *W, int M, int N, int K, const GemmEpi &ep,
                             hipStream_t st) {
     const int grid = static_cast<int>(cdiv(M, PP_BM) * cdiv(N, PP_BN));
-    k_gemm_p3<EPI, KS><<<grid, 512, 0, st>>>(A, W, M, N, K, ep);
+    k_gemm_p3<EPI, KS><<<grid, 512, 0, st>>>(A, W, M, N, K, ep, nullptr, nullptr, 0, ep);
+    return hipGetLastError();
+}
+
+// Two products of one epilogue kind, same N and K, in one ping-pong launch.
+template <int EPI>
+static hipError_t launch_pp2(const uint16_t *A, const uint16_t *W, int M, const GemmEpi &ep, const uint16_t *A2,
+                             const uint16_t *W2, int M2, const GemmEpi &ep2, int N, int K, hipStream_t st) {
+    const int grid = static_cast<int>((cdiv(M, PP_BM) + cdiv(M2, PP_BM)) * cdiv(N, PP_BN));
+    k_gemm_p3<EPI, false><<<grid, 512, 0, st>>>(A, W, M, N, K, ep, A2, W2, M2, ep2);
     return hipGetLastError();
 }
 
@@ -845,6 +866,28 @@ bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &ep, bool a_ro
         epi_ok = epi_ok && ep.kind == EPI_GATE_RES && ep.w2 && ep.k_split % BK == 0 && ep.k_split >= 128 &&
                  K - ep.k_split >= 128;
     return big_tiles >= 128 && !w8 && epi_ok && K >= 128 && N % 256 == 0 && (a_rows_padded || M % 256 == 0);
+}
+
+hipError_t launch_gemm2(const uint16_t *A, const void *W, const uint16_t *Ws, int M, const GemmEpi &ep,
+                        const uint16_t *A2, const void *W2, const uint16_t *Ws2, int M2, const GemmEpi &ep2,
+                        bool w8, int N, int K, hipStream_t st) {
+    const bool one = M > 0 && M2 > 0 && ep.kind == ep2.kind && ep.kind != EPI_QKV_SWIGLU && ep.k_split == 0 &&
+                     ep2.k_split == 0 && gemm_pingpong_ok(M + M2, N, K, w8, ep, true) &&
+                     gemm_pingpong_ok(M + M2, N, K, w8, ep2, true);
+    if (!one) {
+        hipError_t e = hipSuccess;
+        if (M > 0) e = launch_gemm(A, W, Ws, w8, M, N, K, ep, st, true);
+        if (e == hipSuccess && M2 > 0) e = launch_gemm(A2, W2, Ws2, w8, M2, N, K, ep2, st, true);
+        return e;
+    }
+    const uint16_t *Wb = static_cast<const uint16_t *>(W), *Wb2 = static_cast<const uint16_t *>(W2);
+    switch (ep.kind) {
+        case EPI_F32: return launch_pp2<EPI_F32>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
+        case EPI_GATE_RES: return launch_pp2<EPI_GATE_RES>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
+        case EPI_SWIGLU: return launch_pp2<EPI_SWIGLU>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
+        case EPI_QKV: return launch_pp2<EPI_QKV>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Ws, bool w8, int M, int N,

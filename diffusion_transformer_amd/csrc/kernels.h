@@ -67,6 +67,13 @@ struct GemmEpi {
 // (rows past M are read and their results discarded).
 hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Wscale, bool w8, int M,
                        int N, int K, const GemmEpi &epi, hipStream_t st, bool a_rows_padded);
+// Two products with the same N, K, epilogue kind and weight type (the
+// double-stream block's streams), each A with whole 256-row tiles
+// allocated: one ping-pong launch over both tile sets when both qualify,
+// else launch_gemm for each.  M or M2 may be 0.
+hipError_t launch_gemm2(const uint16_t *A, const void *W, const uint16_t *Ws, int M, const GemmEpi &ep,
+                        const uint16_t *A2, const void *W2, const uint16_t *Ws2, int M2, const GemmEpi &ep2,
+                        bool w8, int N, int K, hipStream_t st);
 // Whether launch_gemm runs this product as the 256x256 ping-pong kernel (the
 // only one that takes EPI_QKV_SWIGLU and k_split > 0; asked before using them).
 bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &epi, bool a_rows_padded);
