@@ -37,6 +37,8 @@ equivariance of rows); no page prints a block output.
 `parallel_block_forward` is pinned to the sequential block: its update is
 the sum of the sequential block's attention-only and MLP-only updates (gate
 of the other half zero) under the same shift, scale and gate.
+`block_forward_runs` is pinned to it: one run, or equal vectors in every
+run, is the block; a run with zero gates keeps its rows.
 `double_block_forward` is pinned to it as well: with the same weights in
 both streams it is the sequential block, and with no text rows it is the
 sequential block of the image weights.
@@ -344,6 +346,44 @@ def block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, rows):
     a = swiglu_interleaved(linear(h2, bw.w_up))
     y = x1 + gate_m * linear(a, bw.w_down)
     return y, o, x1, a
+
+
+def block_forward_runs(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arch,
+                       keep: bool = False):
+    """The block with several modulation rows ([GZ] Sequence: map gives each
+    row its modulation row; Modulation holds [modulation rows, hidden]
+    shift/scale/gate; runsOf/gatedInto: (first, end, row) runs of rows that
+    share one).  vecs [R, D] are the conditioning vectors of the R
+    modulation rows; runs lists (first, end, row) covering rows [0, S) in
+    order.  Every row takes the norm shifts/scales and gates of its run's
+    modulation row; the products and the joint attention are unchanged."""
+    x = np.asarray(x, F64)
+    S, D = x.shape
+    H, d = arch.heads, arch.head_dim
+    mods = [modulation(v, bw.w_mod, 6) for v in np.asarray(vecs, F64)]
+    per_row = np.empty((6, S, D))
+    end = 0
+    for r0, r1, m in runs:                  # contiguous, in order, covering [0, S)
+        if r0 != end or r1 <= r0:
+            raise ValueError(f"runs must tile the rows in order: {runs}")
+        per_row[:, r0:r1] = mods[m][:, None, :]
+        end = r1
+    if end != S:
+        raise ValueError(f"runs end at {end}, not {S}")
+    shift_a, scale_a, gate_a, shift_m, scale_m, gate_m = per_row
+    h = modulated_norm(x, shift_a, scale_a, arch, bw.norm1)
+    qkv = linear(h, bw.w_qkv)
+    q = head_prep(heads_of(qkv[:, 0:H * d], H, d), bw.q_norm, arch.qk_eps, cos, sin)
+    k = head_prep(heads_of(qkv[:, H * d:2 * H * d], H, d), bw.k_norm, arch.qk_eps, cos, sin)
+    v = heads_of(qkv[:, 2 * H * d:3 * H * d], H, d)
+    o = attention(q, k, v).transpose(1, 0, 2).reshape(S, H * d)
+    x1 = x + gate_a * linear(o, bw.w_out)
+    h2 = modulated_norm(x1, shift_m, scale_m, arch, bw.norm2)
+    a = swiglu_interleaved(linear(h2, bw.w_up))
+    y = x1 + gate_m * linear(a, bw.w_down)
+    if not keep:
+        return y
+    return y, dict(mods=np.array(mods), h=h, q=q, k=k, v=v, o=o, x1=x1, h2=h2, a=a)
 
 
 def parallel_block_forward(x, bw: BlockWeights, vec, cos, sin, arch: Arch,

@@ -468,6 +468,43 @@ def test_parallel_block_flops():
     assert d == 2 * 3 * 3072 * 3072
 
 
+# ---------------------------------------------------------------- modulation runs
+
+def _runs(W, pos, x, vecs, runs, arch=TINY):
+    c, s = O.rope_tables(pos, arch.axes)
+    return O.block_forward_runs(x, O.BlockWeights(**W), vecs, runs, c, s, arch)
+
+
+def test_runs_one_row_is_the_block():
+    W, pos, x, vecc = _tiny_case(seed=41)
+    S = len(pos)
+    ref = _oracle_block(W, pos, x, vecc, TINY)
+    assert np.abs(_runs(W, pos, x, vecc[None], [(0, S, 0)]) - ref).max() < 1e-12
+    # equal vectors in several runs: the same block
+    runs = [(0, 2, 1), (2, 4, 0), (4, S, 2)]
+    assert np.abs(_runs(W, pos, x, np.stack([vecc] * 3), runs) - ref).max() < 1e-12
+
+
+def test_runs_rows_take_their_own_modulation():
+    W, pos, x, vecc = _tiny_case(seed=42)
+    S, D = len(pos), TINY.hidden
+    rng = np.random.default_rng(43)
+    vecs = np.stack([vecc, rng.standard_normal(D)])
+    runs = [(0, 2, 1), (2, S, 0)]
+    y = _runs(W, pos, x, vecs, runs)
+    assert not np.allclose(y, _oracle_block(W, pos, x, vecc, TINY))
+    # a modulation row whose gates are zero leaves its run's rows unchanged:
+    # with W_mod's gate rows zero and both shift/scale rows nonzero, no row moves
+    Wz = dict(W); Wz["w_mod"] = W["w_mod"].copy()
+    Wz["w_mod"][2 * D:3 * D] = 0; Wz["w_mod"][5 * D:6 * D] = 0
+    assert (_runs(Wz, pos, x, vecs, runs) == x).all()
+    # run order and the vector of an unused row do not matter
+    vecs3 = np.stack([vecc, vecs[1], rng.standard_normal(D)])
+    assert (_runs(W, pos, x, vecs3, runs) == y).all()
+    with pytest.raises(ValueError):
+        _runs(W, pos, x, vecs, [(0, 2, 1), (3, S, 0)])
+
+
 # ---------------------------------------------------------------- double-stream block
 
 def _double(Wt, Wi, pos, x, vecc, L, arch=TINY):
