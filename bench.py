@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-int8", action="store_true", help="skip the int8-weight block timing")
     p.add_argument("--no-parallel", action="store_true", help="skip the parallel-block timing")
     p.add_argument("--no-double", action="store_true", help="skip the double-stream block timing")
+    p.add_argument("--no-runs", action="store_true", help="skip the timing of the block with modulation runs")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
                         "scale reference for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -180,6 +181,31 @@ def time_blocks(L, torch, ctx, bw, x, seq, sh, steps, warmup, parallel=False):
     return e0.elapsed_time(e1) / steps
 
 
+def time_call(torch, fn, steps, warmup):
+    """Average ms of fn() over steps calls on the current stream, after warmup calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def stage_split(ctx, fn, steps):
+    """Per-stage ms per call from the library's stage timers over steps calls."""
+    ctx.timing(True)
+    for _ in range(steps):
+        fn()
+    t = ctx.timing_read()
+    ctx.timing(False)
+    return {k: round(v[0] / steps, 4) for k, v in t.items() if v[1]}
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -285,27 +311,35 @@ def main():
 
         def dfwd():
             ctx.double_block_forward(bwt, bwi, xd, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
-        for _ in range(args.warmup):
-            dfwd()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(torch.cuda.current_stream())
-        for _ in range(args.steps):
-            dfwd()
-        e1.record(torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        msd = e0.elapsed_time(e1) / args.steps
-        ctx.timing(True)
-        for _ in range(args.steps):
-            dfwd()
-        tmd = ctx.timing_read()
-        ctx.timing(False)
+        msd = time_call(torch, dfwd, args.steps, args.warmup)
         dbl_tf = dbl_flops / (msd * 1e-3) / 1e12
         dbl = {"ms": round(msd, 4), "tflops": round(dbl_tf, 2),
                "frac_bf16_peak": round(dbl_tf / PEAK_BF16_TFLOPS, 4), "flops_per_step": dbl_flops,
-               "stages_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in tmd.items() if v[1]}}
+               "stages_ms_per_step": stage_split(ctx, dfwd, args.steps)}
         log(f"double-stream block: {msd:.3f} ms  {dbl_tf:.1f} TFLOP/s")
         del bwt, bwi, xd, other
+
+    # ---------------------------------------------------------------- modulation runs (bf16)
+    runs_res = None
+    if not args.no_runs:
+        log("block with two modulation rows (text rows on one, image rows on the other)")
+        bwr = L.BlockWeights.from_host(case["block"])
+        xr = L.dev_f32(case["x"])
+        vecs = torch.empty((2, D), dtype=torch.float32, device="cuda")
+        vecs[0].copy_(seq.vec)
+        vecs[1].copy_(torch.from_numpy(synth.normal((D,), seed=sh.seed + 200, std=0.13)).float())
+        runs = [(0, sh.L, 1), (sh.L, S, 0)]
+        runs_flops = total_flops + 2 * 6 * D * D         # a second modulation GEMV
+
+        def rfwd():
+            ctx.block_forward_runs(bwr, xr, vecs, runs, seq.cos, seq.sin, sh.L, sh.N)
+        msr = time_call(torch, rfwd, args.steps, args.warmup)
+        runs_tf = runs_flops / (msr * 1e-3) / 1e12
+        runs_res = {"ms": round(msr, 4), "tflops": round(runs_tf, 2),
+                    "frac_bf16_peak": round(runs_tf / PEAK_BF16_TFLOPS, 4), "flops_per_step": runs_flops,
+                    "runs": runs, "stages_ms_per_step": stage_split(ctx, rfwd, args.steps)}
+        log(f"block with modulation runs: {msr:.3f} ms  {runs_tf:.1f} TFLOP/s")
+        del bwr, xr, vecs
     del case
     torch.cuda.empty_cache()
 
@@ -354,6 +388,7 @@ def main():
         "int8_block_tflops": None if int8_tf is None else round(int8_tf, 2),
         "parallel_block": par,
         "double_block": dbl,
+        "runs_block": runs_res,
     }
     if img:
         out.update(img)

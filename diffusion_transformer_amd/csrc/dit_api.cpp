@@ -50,6 +50,11 @@ struct dit_ctx {
 
 namespace {
 
+// modulation rows the workspace holds (six vectors of D each): the runs
+// form of the block takes at most this many conditioning vectors; the
+// double-stream block uses two
+constexpr int kMaxModRows = 8;
+
 thread_local std::string g_err;
 
 dit_status fail(dit_ctx *c, dit_status s, const char *fmt, ...) {
@@ -456,6 +461,91 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
     return DIT_OK;
 }
 
+// The block with several modulation rows over runs of rows ([GZ] Sequence
+// map/runs, Modulation, gatedInto: one gated product per run; validated
+// arguments, runs[i] = (first, end, row) on the host, tiling [0, S)).  The
+// norms run per run with the run's shift and scale; QKV, the attention and
+// UP once over all rows; OUT and DOWN per run with the run's gate, two runs
+// per launch.
+dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const float *vecs, int R, const int32_t *runs,
+                              int n_runs, const float *cs, const float *sn, int S) {
+    const dit_arch &A = c->arch;
+    const int D = A.hidden, F = A.ffn, H = A.heads;
+    const int Sp = round_up(S, 64);
+    const bool w8 = b->wtype == DIT_W_INT8_B32;
+    const bool rms = A.norm == DIT_NORM_RMS;
+    hipStream_t st = c->stream;
+    float *mod = c->mod;
+    for (int r = 0; r < R; ++r) {
+        Stage t(c, DIT_ST_MOD);
+        DIT_LAUNCH(c, launch_gemv(b->w_mod, vecs + int64_t(r) * D, 6 * D, D, true, mod + int64_t(r) * 6 * D, st),
+                   "modulation");
+    }
+    auto norms = [&](const float *shift_of, int which, uint16_t *out, const float *nw) -> dit_status {
+        for (int i = 0; i < n_runs; ++i) {
+            const int f = runs[3 * i], e = runs[3 * i + 1], m = runs[3 * i + 2];
+            const float *mr = mod + int64_t(m) * 6 * D;
+            Stage t(c, which);
+            DIT_LAUNCH(c, launch_modnorm(x + int64_t(f) * D, e - f, D, mr + (shift_of - mod), mr + (shift_of - mod) + D,
+                                         nw, rms, A.eps, out + int64_t(f) * D, st),
+                       "norm");
+        }
+        return DIT_OK;
+    };
+    // OUT / DOWN: x[run] += gate(run) * (a_base[run] W^T), two runs per launch
+    auto gated = [&](const uint16_t *a_base, int lda, int w, int K, int gate_at, int stage) -> dit_status {
+        for (int i = 0; i < n_runs; i += 2) {
+            GemmEpi g[2]{};
+            int f[2] = {0, 0}, rows[2] = {0, 0};
+            for (int j = 0; j < 2 && i + j < n_runs; ++j) {
+                f[j] = runs[3 * (i + j)];
+                rows[j] = runs[3 * (i + j) + 1] - f[j];
+                g[j].kind = EPI_GATE_RES;
+                g[j].out = x + int64_t(f[j]) * D;
+                g[j].ldo = D;
+                g[j].gate = mod + int64_t(runs[3 * (i + j) + 2]) * 6 * D + gate_at;
+            }
+            Stage t(c, stage);
+            DIT_LAUNCH(c, launch_gemm2(a_base + int64_t(f[0]) * lda, b->w[w], b->scale[w], rows[0], g[0],
+                                       a_base + int64_t(f[1]) * lda, b->w[w], b->scale[w], rows[1], g[1], w8, D, K, st),
+                       "gated product");
+        }
+        return DIT_OK;
+    };
+    DIT_TRY(norms(mod, DIT_ST_NORM1, c->h, b->norm_w[0]));
+    GemmEpi e{};
+    e.kind = EPI_QKV;
+    e.q = c->q;
+    e.k = c->k;
+    e.vt = c->vt;
+    e.heads = H;
+    e.ldv = Sp;
+    e.qn = b->norm_w[2];
+    e.kn = b->norm_w[3];
+    e.cos = cs;
+    e.sin = sn;
+    e.qk_eps = A.qk_eps;
+    {
+        Stage t(c, DIT_ST_QKV);
+        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], b->scale[0], w8, S, 3 * D, D, e, st, true), "qkv");
+    }
+    {
+        Stage t(c, DIT_ST_ATTN);
+        DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
+    }
+    DIT_TRY(gated(c->o, D, 1, D, 2 * D, DIT_ST_OUT));
+    DIT_TRY(norms(mod + 3 * D, DIT_ST_NORM2, c->h2, b->norm_w[1]));
+    GemmEpi u{};
+    u.kind = EPI_SWIGLU;
+    u.act = c->a;
+    {
+        Stage t(c, DIT_ST_UP);
+        DIT_LAUNCH(c, launch_gemm(c->h2, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st, true), "up");
+    }
+    DIT_TRY(gated(c->a, F, 3, F, 5 * D, DIT_ST_DOWN));
+    return DIT_OK;
+}
+
 dit_status time_vector(dit_ctx *c, const uint16_t *w1, const uint16_t *w2, float t, float *vec) {
     const dit_arch &A = c->arch;
     hipStream_t st = c->stream;
@@ -516,7 +606,7 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
     // stream block runs the image rows as a product starting at row L
     const size_t Sx = S + 256;
     const size_t sizes[] = {
-        12 * D * 4, D * 4, size_t(arch->time_dim) * 4, D * 4, 2 * D * 4,  // mod (2 x 6 rows) vec temb t1 fmod
+        kMaxModRows * 6 * D * 4, D * 4, size_t(arch->time_dim) * 4, D * 4, 2 * D * 4,  // mod vec temb t1 fmod
         Sx * D * 2, Sx * D * 2,                                        // h h2
         H * S * 128 * 2, H * S * 128 * 2, H * 128 * S * 2,             // q k vt
         Sx * D * 2, Sx * F * 2,                                        // o a
@@ -707,6 +797,27 @@ dit_status dit_parallel_block_forward(dit_ctx *ctx, const dit_block *b, float *x
     DIT_TRY(check_rows(ctx, L, N));
     DIT_TRY(check_ctx(ctx));
     return parallel_block_forward(ctx, b, x, vec, cos_t, sin_t, L + N);
+}
+
+dit_status dit_block_forward_runs(dit_ctx *ctx, const dit_block *b, float *x, const float *vecs, int R,
+                                  const int32_t *runs, int n_runs, const float *cos_t, const float *sin_t, int L,
+                                  int N) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !vecs || !runs || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vecs, runs, cos or sin is NULL");
+    DIT_TRY(check_block(ctx, b));
+    DIT_TRY(check_rows(ctx, L, N));
+    if (R < 1 || R > kMaxModRows) return fail(ctx, DIT_ERANGE, "R = %d outside 1..%d", R, kMaxModRows);
+    if (n_runs < 1 || n_runs > L + N) return fail(ctx, DIT_ERANGE, "n_runs = %d outside 1..%d", n_runs, L + N);
+    int end = 0;
+    for (int i = 0; i < n_runs; ++i) {
+        const int f = runs[3 * i], e = runs[3 * i + 1], m = runs[3 * i + 2];
+        if (f != end || e <= f) return fail(ctx, DIT_EINVAL, "run %d = (%d, %d) does not continue the runs at %d", i, f, e, end);
+        if (m < 0 || m >= R) return fail(ctx, DIT_ERANGE, "run %d uses modulation row %d outside 0..%d", i, m, R - 1);
+        end = e;
+    }
+    if (end != L + N) return fail(ctx, DIT_EINVAL, "runs end at %d, not at L + N = %d", end, L + N);
+    DIT_TRY(check_ctx(ctx));
+    return block_forward_runs(ctx, b, x, vecs, R, runs, n_runs, cos_t, sin_t, L + N);
 }
 
 dit_status dit_double_block_forward(dit_ctx *ctx, const dit_block *txt, const dit_block *img, float *x,

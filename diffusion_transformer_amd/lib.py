@@ -10,6 +10,8 @@ fallback: if libdit.so is missing, importing this module raises.
 from __future__ import annotations
 
 import ctypes as C
+
+import numpy as np
 import os
 import re
 
@@ -76,6 +78,8 @@ _SIGS = {
     "dit_parallel_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_double_block_forward": (C.c_int, [_P, C.POINTER(Block), C.POINTER(Block), _P, _P, _P, _P, C.c_int,
                                            C.c_int]),
+    "dit_block_forward_runs": (C.c_int, [_P, C.POINTER(Block), _P, _P, C.c_int, _P, C.c_int, _P, _P, C.c_int,
+                                         C.c_int]),
     "dit_prologue": (C.c_int, [_P, C.POINTER(Model), _P, C.c_int, _P]),
     "dit_denoise_step": (C.c_int, [_P, C.POINTER(Model), _P, _P, _P, _P, C.c_int, C.c_int,
                                    C.c_float, C.c_float, _P]),
@@ -219,6 +223,13 @@ class Context:
         self._call("dit_parallel_block_forward", C.byref(block.struct), _ptr(x, torch.float32, "x"),
                    _ptr(vec, torch.float32, "vec"), _ptr(cos, torch.float32, "cos"),
                    _ptr(sin, torch.float32, "sin"), L, N)
+
+    def block_forward_runs(self, block: "BlockWeights", x, vecs, runs, cos, sin, L, N):
+        """The block with modulation rows vecs [R, D] over runs [(first, end, row), ...]."""
+        r = np.ascontiguousarray(np.asarray(runs, dtype=np.int32).reshape(-1, 3))
+        self._call("dit_block_forward_runs", C.byref(block.struct), _ptr(x, torch.float32, "x"),
+                   _ptr(vecs, torch.float32, "vecs"), int(vecs.shape[0]), r.ctypes.data_as(C.c_void_p), len(r),
+                   _ptr(cos, torch.float32, "cos"), _ptr(sin, torch.float32, "sin"), L, N)
 
     def double_block_forward(self, txt: "BlockWeights", img: "BlockWeights", x, vec, cos, sin, L, N):
         """The double-stream block: rows [0, L) take `txt`, the rest `img`."""

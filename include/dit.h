@@ -11,7 +11,7 @@
  *        attention, s.4.4 fused qk-prep.
  *   [GZ] "gizai:dit" module reference: Arch, Block, Modulation, Sequence,
  *        Work, gluRows, gatedInto, normedInto, prepOf, sinusoids,
- *        Block.forward, Block.parallel, HEAD, CHUNK.
+ *        Block.forward, Block.parallel, runsOf, gatedInto, HEAD, CHUNK.
  *
  * Conventions (all entry points):
  *  - Every tensor argument is a DEVICE pointer to caller-owned memory on the
@@ -210,6 +210,23 @@ dit_status dit_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const f
  * concatenated [attention output | SwiGLU output] rows). */
 dit_status dit_parallel_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const float *vec,
                                       const float *cos, const float *sin, int L, int N);
+
+/* The block with several modulation rows ([GZ] Sequence: map gives each
+ * row its modulation row, runs are (first, end, row) triples of rows that
+ * share one; Modulation: [modulation rows, hidden] shift/scale/gate;
+ * gatedInto: one gated product per run).  vecs fp32 [R, D] on the device
+ * are the R conditioning vectors (1 <= R <= 8); runs int32 [n_runs][3] in
+ * HOST memory tile rows [0, L+N) in order (first of run i = end of run
+ * i-1, first of run 0 = 0, end of the last = L+N, first < end) and name a
+ * modulation row 0..R-1 each.  Every row gets dit_block_forward's
+ * arithmetic with its run's shifts, scales and gates; the products and the
+ * joint attention are shared.  A single run over all rows is
+ * dit_block_forward.  Errors as dit_block_forward, and DIT_ERANGE for R or
+ * a row outside range, DIT_EINVAL for runs that do not tile the rows.
+ * Debug buffer 0 holds the modulation rows [R, 6, D]. */
+dit_status dit_block_forward_runs(dit_ctx *ctx, const dit_block *b, float *x, const float *vecs, int R,
+                                  const int32_t *runs, int n_runs, const float *cos, const float *sin, int L,
+                                  int N);
 
 /* The double-stream block ([K4] Appendix B: the FLUX.2 double blocks, one
  * set of attention and MLP weights per stream, the q/k preparation run per

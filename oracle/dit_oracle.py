@@ -348,6 +348,22 @@ def block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, rows):
     return y, o, x1, a
 
 
+def _modulation_per_row(vecs, w_mod, runs, S: int):
+    """Per-row shift/scale/gate vectors [6, S, D] for (first, end, row) runs
+    that tile rows [0, S) in order ([GZ] Sequence runs)."""
+    mods = [modulation(v, w_mod, 6) for v in np.asarray(vecs, F64)]
+    per_row = np.empty((6, S, mods[0].shape[1]))
+    end = 0
+    for r0, r1, m in runs:                  # contiguous, in order, covering [0, S)
+        if r0 != end or r1 <= r0:
+            raise ValueError(f"runs must tile the rows in order: {runs}")
+        per_row[:, r0:r1] = mods[m][:, None, :]
+        end = r1
+    if end != S:
+        raise ValueError(f"runs end at {end}, not {S}")
+    return mods, per_row
+
+
 def block_forward_runs(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arch,
                        keep: bool = False):
     """The block with several modulation rows ([GZ] Sequence: map gives each
@@ -360,16 +376,7 @@ def block_forward_runs(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arch,
     x = np.asarray(x, F64)
     S, D = x.shape
     H, d = arch.heads, arch.head_dim
-    mods = [modulation(v, bw.w_mod, 6) for v in np.asarray(vecs, F64)]
-    per_row = np.empty((6, S, D))
-    end = 0
-    for r0, r1, m in runs:                  # contiguous, in order, covering [0, S)
-        if r0 != end or r1 <= r0:
-            raise ValueError(f"runs must tile the rows in order: {runs}")
-        per_row[:, r0:r1] = mods[m][:, None, :]
-        end = r1
-    if end != S:
-        raise ValueError(f"runs end at {end}, not {S}")
+    mods, per_row = _modulation_per_row(vecs, bw.w_mod, runs, S)
     shift_a, scale_a, gate_a, shift_m, scale_m, gate_m = per_row
     h = modulated_norm(x, shift_a, scale_a, arch, bw.norm1)
     qkv = linear(h, bw.w_qkv)
@@ -384,6 +391,31 @@ def block_forward_runs(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arch,
     if not keep:
         return y
     return y, dict(mods=np.array(mods), h=h, q=q, k=k, v=v, o=o, x1=x1, h2=h2, a=a)
+
+
+def block_forward_runs_rows(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arch, rows):
+    """block_forward_runs for the selected rows only (keys and values need
+    every row, everything after the attention is per row).  Returns
+    (y[rows], o[rows], a[rows])."""
+    x = np.asarray(x, F64)
+    S = x.shape[0]
+    rows = np.asarray(rows)
+    H, d = arch.heads, arch.head_dim
+    _, per_row = _modulation_per_row(vecs, bw.w_mod, runs, S)
+    shift_a, scale_a, gate_a, shift_m, scale_m, gate_m = per_row
+    h = modulated_norm(x, shift_a, scale_a, arch, bw.norm1)
+    wq = np.asarray(bw.w_qkv, F64)
+    q = heads_of(linear(h[rows], wq[0:H * d]), H, d)
+    k = heads_of(linear(h, wq[H * d:2 * H * d]), H, d)
+    v = heads_of(linear(h, wq[2 * H * d:]), H, d)
+    q = head_prep(q, bw.q_norm, arch.qk_eps, cos[rows], sin[rows])
+    k = head_prep(k, bw.k_norm, arch.qk_eps, cos, sin)
+    o = attention(q, k, v).transpose(1, 0, 2).reshape(len(rows), H * d)
+    x1 = x[rows] + gate_a[rows] * linear(o, bw.w_out)
+    h2 = modulated_norm(x1, shift_m[rows], scale_m[rows], arch, bw.norm2)
+    a = swiglu_interleaved(linear(h2, bw.w_up))
+    y = x1 + gate_m[rows] * linear(a, bw.w_down)
+    return y, o, a
 
 
 def parallel_block_forward(x, bw: BlockWeights, vec, cos, sin, arch: Arch,

@@ -435,6 +435,118 @@ def test_double_block_zero_modulation_is_identity(ctx_tiny):
     assert (np_of(_double_gpu(ctx_tiny, case)) == case["x"]).all()
 
 
+
+# --------------------------------------------------------------- modulation runs
+
+def _runs_case(name, R):
+    # R conditioning vectors drawn at the time vector's scale (its values
+    # have a standard deviation of about 0.13 at hidden 3072)
+    case = synth.block_case(name)
+    sh = case["shape"]
+    case["vecs"] = synth.normal((R, sh.hidden), seed=sh.seed + 200, std=0.13)
+    return case
+
+
+def _runs_gpu(ctx, case, runs, vecs=None):
+    sh = case["shape"]
+    seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    x = L.dev_f32(case["x"])
+    v = L.dev_f32(case["vecs"] if vecs is None else vecs)
+    ctx.block_forward_runs(bw, x, v, runs, seq.cos, seq.sin, sh.L, sh.N)
+    torch.cuda.synchronize()
+    return x
+
+
+def _runs_of(name, sh):
+    # text rows on one modulation row, the image rows split raggedly over
+    # two others (three runs: the OUT/DOWN launches pair two runs, then one)
+    if name == "s4608":
+        return [(0, sh.L, 1), (sh.L, sh.S, 0)]
+    cut = sh.L + (5 if name == "tiny" else 517)
+    return [(0, sh.L, 2), (sh.L, cut, 0), (cut, sh.S, 1)]
+
+
+@pytest.mark.parametrize("name", ["tiny", "s1088"])
+def test_block_runs_full_parity(ctx_tiny, name):
+    case = _runs_case(name, 3)
+    sh = case["shape"]
+    la, oa = arch_pair(sh)
+    ctx = ctx_tiny if name == "tiny" else L.Context(la, max_rows=sh.S)
+    runs = _runs_of(name, sh)
+    say("block runs", name, runs)
+    got = np_of(_runs_gpu(ctx, case, runs))
+    D, F, H = sh.hidden, sh.ffn, sh.heads
+    S, Sp = sh.S, (sh.S + 63) // 64 * 64
+    cs, sn, _ = _oracle_inputs(case, oa)
+    y, ref = O.block_forward_runs(case["x"], oracle_block(case["block"]), case["vecs"], runs, cs, sn, oa, keep=True)
+    mods = np_of(ctx.debug_copy(0, torch.float32, (3, 6, D)))
+    compare(f"{name}/mods", mods, ref["mods"], rel=1e-4, abs_=1e-4)
+    compare(f"{name}/h", np_of(ctx.debug_copy(1, torch.bfloat16, (S, D))), ref["h"], bf16_stored=True)
+    compare(f"{name}/q", np_of(ctx.debug_copy(2, torch.bfloat16, (H, S, 128))), ref["q"], bf16_stored=True)
+    compare(f"{name}/k", np_of(ctx.debug_copy(3, torch.bfloat16, (H, S, 128))), ref["k"], bf16_stored=True)
+    v = np_of(ctx.debug_copy(4, torch.bfloat16, (H, 128, Sp)))[:, :, :S].transpose(0, 2, 1)
+    compare(f"{name}/v", v, ref["v"], bf16_stored=True)
+    compare(f"{name}/o", np_of(ctx.debug_copy(5, torch.bfloat16, (S, D))), ref["o"], bf16_stored=True)
+    compare(f"{name}/h2", np_of(ctx.debug_copy(6, torch.bfloat16, (S, D))), ref["h2"], bf16_stored=True)
+    compare(f"{name}/a", np_of(ctx.debug_copy(7, torch.bfloat16, (S, F))), ref["a"], bf16_stored=True)
+    compare(f"{name}/y", got, y)
+    compare(f"{name}/delta", got - case["x"], y - case["x"])
+    if ctx is not ctx_tiny:
+        ctx.close()
+
+
+def test_block_runs_full_size_sampled_rows(ctx_big):
+    case = _runs_case("s4608", 2)
+    sh = case["shape"]
+    _, oa = arch_pair(sh)
+    D, F = sh.hidden, sh.ffn
+    runs = _runs_of("s4608", sh)
+    say("block runs s4608", runs)
+    got = np_of(_runs_gpu(ctx_big, case, runs))
+    o_got = np_of(ctx_big.debug_copy(5, torch.bfloat16, (sh.S, D)))
+    a_got = np_of(ctx_big.debug_copy(7, torch.bfloat16, (sh.S, F)))
+    cs, sn, _ = _oracle_inputs(case, oa)
+    rows = synth.rows_sample(sh.S, 48, L=sh.L)
+    y, o, a = O.block_forward_runs_rows(case["x"], oracle_block(case["block"]), case["vecs"], runs, cs, sn, oa, rows)
+    compare("s4608/o", o_got[rows], o, bf16_stored=True)
+    compare("s4608/a", a_got[rows], a, bf16_stored=True)
+    compare("s4608/y", got[rows], y)
+    compare("s4608/delta", got[rows] - case["x"][rows], y - case["x"][rows])
+
+
+@pytest.mark.parametrize("name", ["tiny", "s4608"])
+def test_block_runs_equal_vectors_are_the_block_bit_exact(ctx_tiny, ctx_big, name):
+    # every row's arithmetic is the single-vector block's, in the same
+    # kernels (the text and image runs of the 4608-row block share one
+    # launch of each gated product), so the rows agree to the bit
+    case = synth.block_case(name)
+    sh = case["shape"]
+    ctx = ctx_tiny if name == "tiny" else ctx_big
+    ref, seq, _ = _block_gpu(ctx, case)
+    vec = np_of(seq.vec).reshape(1, -1)
+    runs = [(0, sh.L, 1), (sh.L, sh.S, 0)] if name == "s4608" else [(0, 3, 1), (3, sh.S, 0)]
+    say("block runs equal vectors", name, runs)
+    got = _runs_gpu(ctx, case, runs, vecs=np.concatenate([vec, vec]))
+    assert torch.equal(got, ref)
+
+
+def test_block_runs_zero_gates_is_identity(ctx_tiny):
+    case = _runs_case("tiny", 3)
+    D = case["shape"].hidden
+    case["block"]["w_mod"][2 * D:3 * D] = 0.0
+    case["block"]["w_mod"][5 * D:] = 0.0
+    assert (np_of(_runs_gpu(ctx_tiny, case, _runs_of("tiny", case["shape"]))) == case["x"]).all()
+
+
+def test_block_runs_rejects_bad_runs(ctx_tiny):
+    case = _runs_case("tiny", 2)
+    sh = case["shape"]
+    for runs in ([(0, 3, 0), (4, sh.S, 1)], [(0, 3, 0), (3, sh.S, 2)], [(0, 3, 0)], [(1, sh.S, 0)],
+                 [(0, 0, 0), (0, sh.S, 1)]):
+        with pytest.raises(RuntimeError):
+            _runs_gpu(ctx_tiny, case, runs)
+
 # --------------------------------------------------------------- denoise
 
 def test_denoise_twin(ctx_tiny):

@@ -505,6 +505,21 @@ def test_runs_rows_take_their_own_modulation():
         _runs(W, pos, x, vecs, [(0, 2, 1), (3, S, 0)])
 
 
+
+def test_runs_sampled_rows_match_the_full_runs_block():
+    W, pos, x, vecc = _tiny_case(seed=44)
+    S, D = len(pos), TINY.hidden
+    vecs = np.stack([vecc, np.random.default_rng(45).standard_normal(D)])
+    runs = [(0, 3, 1), (3, S - 2, 0), (S - 2, S, 1)]
+    c, s = O.rope_tables(pos, TINY.axes)
+    bw = O.BlockWeights(**W)
+    y, ref = O.block_forward_runs(x, bw, vecs, runs, c, s, TINY, keep=True)
+    rows = np.array([0, 2, 3, S - 3, S - 1])
+    yr, o, a = O.block_forward_runs_rows(x, bw, vecs, runs, c, s, TINY, rows)
+    assert np.abs(yr - y[rows]).max() < 1e-12
+    assert np.abs(o - ref["o"][rows]).max() < 1e-12
+    assert np.abs(a - ref["a"][rows]).max() < 1e-12
+
 # ---------------------------------------------------------------- double-stream block
 
 def _double(Wt, Wi, pos, x, vecc, L, arch=TINY):
