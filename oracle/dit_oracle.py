@@ -23,7 +23,8 @@ Sources (web pages; cited by title and section):
         blocks' per-stream weight names).
   [GZ]  "gizai:dit" module reference: types Block, Sequence, Modulation;
         functions sinusoids, gluRows, gatedInto, normedInto, prepOf, silu,
-        Block.forward, Block.parallel; constants HEAD, QKV/OUT/UP/DOWN.
+        Block.forward, Block.parallel; constants HEAD, QKV/OUT/UP/DOWN,
+        POST_ATTN/POST_MLP (sandwich norms).
 
 Readings of points the pages leave open are listed in the repository's
 design notes; the ones that shape the arithmetic are restated where used.
@@ -39,6 +40,10 @@ the sum of the sequential block's attention-only and MLP-only updates (gate
 of the other half zero) under the same shift, scale and gate.
 `block_forward_runs` is pinned to it: one run, or equal vectors in every
 run, is the block; a run with zero gates keeps its rows.
+`post_norm` (a sandwich block's norms) is pinned by closed forms: with
+eps 0 each row of a half's update divided by its gate and norm weight has
+RMS 1 (RMSNorm) or mean 0 and variance 1 (LayerNorm), and the block is
+unchanged when the product's weight is scaled.
 `double_block_forward` is pinned to it as well: with the same weights in
 both streams it is the sequential block, and with no text rows it is the
 sequential block of the image weights.
@@ -280,7 +285,9 @@ class BlockWeights:
     w_qkv [3*H*d, D] (all queries, all keys, all values; [GZ] weightAt),
     w_out [D, H*d], w_up [2F, D] (gate/up interleaved, [GZ] gluRows),
     w_down [D, F], w_mod [6D, D]; q_norm, k_norm [d]; norm1, norm2 [D]
-    (RMS variant only)."""
+    (RMS variant only); post_attn, post_mlp [D]: a sandwich block's norm
+    weights after the attention and after the MLP ([GZ] POST_ATTN,
+    POST_MLP), None for a block without them."""
 
     w_qkv: np.ndarray
     w_out: np.ndarray
@@ -291,6 +298,29 @@ class BlockWeights:
     k_norm: np.ndarray
     norm1: np.ndarray = None
     norm2: np.ndarray = None
+    post_attn: np.ndarray = None
+    post_mlp: np.ndarray = None
+
+
+def post_norm(y, w, arch: Arch):
+    """A sandwich block's norm of a product's output rows, taken before the
+    gate ([GZ] POST_ATTN, POST_MLP: a sandwich block norms its attention and
+    MLP outputs before their gates; a block without the weights adds the
+    gated outputs as they are).  The norm is the block's own kind (the
+    arch's LayerNorm or RMSNorm, its eps) times the weight w; w None leaves
+    y as it is."""
+    if w is None:
+        return y
+    if arch.norm == "rms":
+        return rms_norm(y, w, arch.eps)
+    if arch.norm == "layer":
+        return layer_norm(y, arch.eps) * np.asarray(w, F64)
+    raise ValueError(arch.norm)
+
+
+def _no_sandwich(bw: BlockWeights, form: str):
+    if bw.post_attn is not None or bw.post_mlp is not None:
+        raise ValueError(f"sandwich norms belong to the sequential block, not the {form}")
 
 
 def block_forward(x, bw: BlockWeights, vec, cos, sin, arch: Arch,
@@ -313,11 +343,11 @@ def block_forward(x, bw: BlockWeights, vec, cos, sin, arch: Arch,
     q = head_prep(q, bw.q_norm, arch.qk_eps, cos, sin)
     k = head_prep(k, bw.k_norm, arch.qk_eps, cos, sin)
     o = attention(q, k, v).transpose(1, 0, 2).reshape(S, H * d)
-    x1 = x + gate_a * linear(o, bw.w_out)                    # [GZ] gatedInto
+    x1 = x + gate_a * post_norm(linear(o, bw.w_out), bw.post_attn, arch)   # [GZ] gatedInto
     # MLP half
     h2 = modulated_norm(x1, shift_m, scale_m, arch, bw.norm2)
     a = swiglu_interleaved(linear(h2, bw.w_up))
-    y = x1 + gate_m * linear(a, bw.w_down)
+    y = x1 + gate_m * post_norm(linear(a, bw.w_down), bw.post_mlp, arch)
     if not keep:
         return y
     return y, dict(mod=m, h=h, q=q, k=k, v=v, o=o, x1=x1, h2=h2, a=a)
@@ -341,10 +371,10 @@ def block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, rows):
     q = head_prep(q, bw.q_norm, arch.qk_eps, cos[rows], sin[rows])
     k = head_prep(k, bw.k_norm, arch.qk_eps, cos, sin)
     o = attention(q, k, v).transpose(1, 0, 2).reshape(len(rows), H * d)
-    x1 = x[rows] + gate_a * linear(o, bw.w_out)
+    x1 = x[rows] + gate_a * post_norm(linear(o, bw.w_out), bw.post_attn, arch)
     h2 = modulated_norm(x1, shift_m, scale_m, arch, bw.norm2)
     a = swiglu_interleaved(linear(h2, bw.w_up))
-    y = x1 + gate_m * linear(a, bw.w_down)
+    y = x1 + gate_m * post_norm(linear(a, bw.w_down), bw.post_mlp, arch)
     return y, o, x1, a
 
 
@@ -384,10 +414,10 @@ def block_forward_runs(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arch,
     k = head_prep(heads_of(qkv[:, H * d:2 * H * d], H, d), bw.k_norm, arch.qk_eps, cos, sin)
     v = heads_of(qkv[:, 2 * H * d:3 * H * d], H, d)
     o = attention(q, k, v).transpose(1, 0, 2).reshape(S, H * d)
-    x1 = x + gate_a * linear(o, bw.w_out)
+    x1 = x + gate_a * post_norm(linear(o, bw.w_out), bw.post_attn, arch)
     h2 = modulated_norm(x1, shift_m, scale_m, arch, bw.norm2)
     a = swiglu_interleaved(linear(h2, bw.w_up))
-    y = x1 + gate_m * linear(a, bw.w_down)
+    y = x1 + gate_m * post_norm(linear(a, bw.w_down), bw.post_mlp, arch)
     if not keep:
         return y
     return y, dict(mods=np.array(mods), h=h, q=q, k=k, v=v, o=o, x1=x1, h2=h2, a=a)
@@ -411,10 +441,10 @@ def block_forward_runs_rows(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arc
     q = head_prep(q, bw.q_norm, arch.qk_eps, cos[rows], sin[rows])
     k = head_prep(k, bw.k_norm, arch.qk_eps, cos, sin)
     o = attention(q, k, v).transpose(1, 0, 2).reshape(len(rows), H * d)
-    x1 = x[rows] + gate_a[rows] * linear(o, bw.w_out)
+    x1 = x[rows] + gate_a[rows] * post_norm(linear(o, bw.w_out), bw.post_attn, arch)
     h2 = modulated_norm(x1, shift_m[rows], scale_m[rows], arch, bw.norm2)
     a = swiglu_interleaved(linear(h2, bw.w_up))
-    y = x1 + gate_m[rows] * linear(a, bw.w_down)
+    y = x1 + gate_m[rows] * post_norm(linear(a, bw.w_down), bw.post_mlp, arch)
     return y, o, a
 
 
@@ -428,6 +458,7 @@ def parallel_block_forward(x, bw: BlockWeights, vec, cos, sin, arch: Arch,
     as in the sequential block.  Returns the new rows (float64) and, with
     keep=True, the intermediates (mod, h, q, k, v after prep, o, a)."""
     x = np.asarray(x, F64)
+    _no_sandwich(bw, "parallel block")
     S, D = x.shape
     H, d = arch.heads, arch.head_dim
     m = modulation(vec, bw.w_mod, 3)
@@ -450,6 +481,7 @@ def parallel_block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, 
     parallel_block_forward; keys and values need every row).  Returns
     (y[rows], o[rows], a[rows])."""
     x = np.asarray(x, F64)
+    _no_sandwich(bw, "parallel block")
     rows = np.asarray(rows)
     H, d = arch.heads, arch.head_dim
     shift, scale, gate = modulation(vec, bw.w_mod, 3)
@@ -479,6 +511,8 @@ def double_block_forward(x, bw_txt: BlockWeights, bw_img: BlockWeights, vec, cos
     shared).  Returns the new rows (float64) and, with keep=True, the
     intermediates (h, q, k, v after prep, o, x1, a) over all rows."""
     x = np.asarray(x, F64)
+    _no_sandwich(bw_txt, "double-stream block")
+    _no_sandwich(bw_img, "double-stream block")
     S, D = x.shape
     H, d = arch.heads, arch.head_dim
     streams = ((bw_txt, slice(0, L)), (bw_img, slice(L, S)))

@@ -9,6 +9,8 @@ that the pins notice.
 
 import math
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -519,6 +521,90 @@ def test_runs_sampled_rows_match_the_full_runs_block():
     assert np.abs(yr - y[rows]).max() < 1e-12
     assert np.abs(o - ref["o"][rows]).max() < 1e-12
     assert np.abs(a - ref["a"][rows]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- sandwich norms
+
+def _sandwich_case(seed, rms):
+    W, pos, x, vecc = _tiny_case(seed=seed, rms=rms)
+    rng = np.random.default_rng(seed + 1)
+    W["post_attn"] = 0.5 + rng.random(TINY.hidden)     # positive and distinct per column
+    W["post_mlp"] = 0.5 + rng.random(TINY.hidden)
+    arch = dataclasses.replace(TINY, eps=0.0, norm="rms" if rms else "layer")
+    return W, pos, x, vecc, arch
+
+
+def _sandwich_half(W, pos, x, vecc, arch, half):
+    # the update of one half with the other half's gate rows zeroed, divided
+    # by its gate and its post-norm weight, and that half's product output
+    D = arch.hidden
+    Wh = dict(W)
+    Wh["w_mod"] = W["w_mod"].copy()
+    other = slice(5 * D, 6 * D) if half == "attn" else slice(2 * D, 3 * D)
+    Wh["w_mod"][other] = 0.0
+    c, s = O.rope_tables(pos, arch.axes)
+    y, ref = O.block_forward(x, O.BlockWeights(**Wh), vecc, c, s, arch, keep=True)
+    gate = O.modulation(vecc, W["w_mod"], 6)[2 if half == "attn" else 5]
+    w = W["post_attn"] if half == "attn" else W["post_mlp"]
+    prod = ref["o"] @ W["w_out"].T if half == "attn" else ref["a"] @ W["w_down"].T
+    return (y - x) / (gate * w), prod
+
+
+@pytest.mark.parametrize("rms", [False, True])
+@pytest.mark.parametrize("half", ["attn", "mlp"])
+def test_sandwich_norm_comes_before_the_gate(rms, half):
+    W, pos, x, vecc, arch = _sandwich_case(50, rms)
+    u, prod = _sandwich_half(W, pos, x, vecc, arch, half)
+    # each row of the normed output: unit RMS (RMSNorm) or zero mean and unit
+    # variance (LayerNorm) -- before the gate and with this half's weight
+    assert np.abs((u * u).mean(axis=1) - 1).max() < 1e-10
+    if rms:
+        # RMSNorm keeps the direction of the product's output row
+        cosv = (u * prod).sum(1) / np.linalg.norm(u, axis=1) / np.linalg.norm(prod, axis=1)
+        assert np.abs(cosv - 1).max() < 1e-10
+    else:
+        assert np.abs(u.mean(axis=1)).max() < 1e-10
+        # the direction of the centred product output
+        pc = prod - prod.mean(axis=1, keepdims=True)
+        cosv = (u * pc).sum(1) / np.linalg.norm(u, axis=1) / np.linalg.norm(pc, axis=1)
+        assert np.abs(cosv - 1).max() < 1e-10
+
+
+@pytest.mark.parametrize("rms", [False, True])
+def test_sandwich_block_ignores_the_scale_of_its_products(rms):
+    W, pos, x, vecc, arch = _sandwich_case(51, rms)
+    ref = _oracle_block(W, pos, x, vecc, arch)
+    Ws = dict(W, w_out=W["w_out"] * 7.25, w_down=W["w_down"] * 0.375)
+    assert np.abs(_oracle_block(Ws, pos, x, vecc, arch) - ref).max() < 1e-10
+    # without the sandwich norms the scale shows
+    Wn = {k: v for k, v in W.items() if not k.startswith("post_")}
+    Wns = {k: v for k, v in Ws.items() if not k.startswith("post_")}
+    assert np.abs(_oracle_block(Wns, pos, x, vecc, arch) - _oracle_block(Wn, pos, x, vecc, arch)).max() > 1e-3
+    # zero gates: every row unchanged, with or without the norms
+    D = arch.hidden
+    Wz = dict(W, w_mod=W["w_mod"].copy())
+    Wz["w_mod"][2 * D:3 * D] = 0.0
+    Wz["w_mod"][5 * D:] = 0.0
+    assert (_oracle_block(Wz, pos, x, vecc, arch) == x).all()
+
+
+def test_sandwich_weights_belong_to_the_sequential_forms():
+    W, pos, x, vecc, arch = _sandwich_case(52, False)
+    c, s = O.rope_tables(pos, arch.axes)
+    bw = O.BlockWeights(**W)
+    # the runs form and the sampled-rows forms carry them too
+    y = O.block_forward(x, bw, vecc, c, s, arch)
+    S = len(pos)
+    assert np.abs(O.block_forward_runs(x, bw, vecc[None], [(0, S, 0)], c, s, arch) - y).max() < 1e-12
+    rows = np.array([0, S - 1])
+    assert np.abs(O.block_forward_rows(x, bw, vecc, c, s, arch, rows)[0] - y[rows]).max() < 1e-12
+    assert np.abs(O.block_forward_runs_rows(x, bw, vecc[None], [(0, S, 0)], c, s, arch, rows)[0]
+                  - y[rows]).max() < 1e-12
+    with pytest.raises(ValueError):
+        Wp = dict(W, w_mod=W["w_mod"][:3 * arch.hidden])
+        O.parallel_block_forward(x, O.BlockWeights(**Wp), vecc, c, s, arch)
+    with pytest.raises(ValueError):
+        O.double_block_forward(x, bw, bw, vecc, c, s, arch, 2)
 
 # ---------------------------------------------------------------- double-stream block
 
