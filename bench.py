@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--no-parallel", action="store_true", help="skip the parallel-block timing")
     p.add_argument("--no-double", action="store_true", help="skip the double-stream block timing")
     p.add_argument("--no-runs", action="store_true", help="skip the timing of the block with modulation runs")
+    p.add_argument("--no-sandwich", action="store_true", help="skip the sandwich block timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
                         "scale reference for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -340,6 +341,25 @@ def main():
                     "runs": runs, "stages_ms_per_step": stage_split(ctx, rfwd, args.steps)}
         log(f"block with modulation runs: {msr:.3f} ms  {runs_tf:.1f} TFLOP/s")
         del bwr, xr, vecs
+
+    # ---------------------------------------------------------------- sandwich block (bf16)
+    sw = None
+    if not args.no_sandwich:
+        log("sandwich block (attention and MLP outputs normed before their gates)")
+        sb = dict(case["block"])
+        sb["post_attn"] = synth.normal((D,), seed=sh.seed + 300, std=0.2, mean=1.0)
+        sb["post_mlp"] = synth.normal((D,), seed=sh.seed + 301, std=0.2, mean=1.0)
+        bws = L.BlockWeights.from_host(sb)
+        xs = L.dev_f32(case["x"])
+
+        def sfwd():
+            ctx.block_forward(bws, xs, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        mss = time_call(torch, sfwd, args.steps, args.warmup)
+        sw_tf = total_flops / (mss * 1e-3) / 1e12
+        sw = {"ms": round(mss, 4), "tflops": round(sw_tf, 2), "frac_bf16_peak": round(sw_tf / PEAK_BF16_TFLOPS, 4),
+              "flops_per_step": total_flops, "stages_ms_per_step": stage_split(ctx, sfwd, args.steps)}
+        log(f"sandwich block: {mss:.3f} ms  {sw_tf:.1f} TFLOP/s")
+        del bws, xs, sb
     del case
     torch.cuda.empty_cache()
 
@@ -389,6 +409,7 @@ def main():
         "parallel_block": par,
         "double_block": dbl,
         "runs_block": runs_res,
+        "sandwich_block": sw,
     }
     if img:
         out.update(img)

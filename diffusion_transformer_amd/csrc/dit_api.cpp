@@ -8,6 +8,7 @@
 // and Appendix B D2 (text rows and rotary tables hoisted out of the loop).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -35,6 +36,10 @@ struct dit_ctx {
     // parallel block: [attention output | SwiGLU output] per row, the one A
     // operand of its fused output product
     uint16_t *oa = nullptr;
+    // a sandwich block's fp32 product output [S, D]; it shares oa's memory
+    // (the sequential and the parallel block never run at once on one
+    // context: its calls are ordered on its stream)
+    float *yf = nullptr;
     float *seq = nullptr, *vel = nullptr;
     size_t bytes[9] = {};
     std::string err;
@@ -158,7 +163,9 @@ dit_status check_ctx(dit_ctx *c) {
     return DIT_OK;
 }
 
-dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false) {
+// `sandwich`: whether the form takes a sandwich block's post norms (the
+// sequential forms); the others reject them.
+dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bool sandwich = false) {
     if (!b) return fail(c, DIT_EINVAL, "block is NULL");
     if (b->wtype != DIT_W_BF16 && b->wtype != DIT_W_INT8_B32) return fail(c, DIT_EINVAL, "unknown wtype %d", b->wtype);
     for (int i = 0; i < 4; ++i) {
@@ -170,6 +177,10 @@ dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false) {
     if (!b->norm_w[2] || !b->norm_w[3]) return fail(c, DIT_EINVAL, "head-norm weights are NULL");
     if (c->arch.norm == DIT_NORM_RMS && (!b->norm_w[0] || (!parallel && !b->norm_w[1])))
         return fail(c, DIT_EINVAL, parallel ? "RMSNorm needs norm weight NORM1" : "RMSNorm needs norm weights NORM1 and NORM2");
+    if (!b->post_w[0] != !b->post_w[1])
+        return fail(c, DIT_EINVAL, "a sandwich block needs both post-norm weights (POST_ATTN and POST_MLP)");
+    if (b->post_w[0] && !sandwich)
+        return fail(c, DIT_EINVAL, "sandwich norms are taken by the sequential block forms only");
     return DIT_OK;
 }
 
@@ -177,77 +188,6 @@ dit_status check_rows(dit_ctx *c, int L, int N) {
     if (L < 0 || L > 512) return fail(c, DIT_ERANGE, "L = %d outside 0..512", L);
     if (N < 1 || N > 4096) return fail(c, DIT_ERANGE, "N = %d outside 1..4096", N);
     if (L + N > c->max_rows) return fail(c, DIT_ERANGE, "L + N = %d exceeds max_rows %d", L + N, c->max_rows);
-    return DIT_OK;
-}
-
-// The block forward's launch sequence (validated arguments).
-dit_status block_forward(dit_ctx *c, const dit_block *b, float *x, const float *vec, const float *cs,
-                         const float *sn, int S) {
-    const dit_arch &A = c->arch;
-    const int D = A.hidden, F = A.ffn, H = A.heads;
-    const int Sp = round_up(S, 64);
-    const bool w8 = b->wtype == DIT_W_INT8_B32;
-    const bool rms = A.norm == DIT_NORM_RMS;
-    hipStream_t st = c->stream;
-    float *mod = c->mod;
-
-    {
-        Stage t(c, DIT_ST_MOD);
-        DIT_LAUNCH(c, launch_gemv(b->w_mod, vec, 6 * D, D, true, mod, st), "modulation");
-    }
-    {
-        Stage t(c, DIT_ST_NORM1);
-        DIT_LAUNCH(c, launch_modnorm(x, S, D, mod, mod + D, b->norm_w[0], rms, A.eps, c->h, st), "norm1");
-    }
-
-    GemmEpi e{};
-    e.kind = EPI_QKV;
-    e.q = c->q;
-    e.k = c->k;
-    e.vt = c->vt;
-    e.heads = H;
-    e.ldv = Sp;
-    e.qn = b->norm_w[2];
-    e.kn = b->norm_w[3];
-    e.cos = cs;
-    e.sin = sn;
-    e.qk_eps = A.qk_eps;
-    {
-        Stage t(c, DIT_ST_QKV);
-        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], b->scale[0], w8, S, 3 * D, D, e, st, true), "qkv");
-    }
-    {
-        Stage t(c, DIT_ST_ATTN);
-        DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
-    }
-
-    GemmEpi g{};
-    g.kind = EPI_GATE_RES;
-    g.out = x;
-    g.ldo = D;
-    g.gate = mod + 2 * D;
-    {
-        Stage t(c, DIT_ST_OUT);
-        DIT_LAUNCH(c, launch_gemm(c->o, b->w[1], b->scale[1], w8, S, D, D, g, st, true), "out");
-    }
-    {
-        Stage t(c, DIT_ST_NORM2);
-        DIT_LAUNCH(c, launch_modnorm(x, S, D, mod + 3 * D, mod + 4 * D, b->norm_w[1], rms, A.eps, c->h2, st),
-                   "norm2");
-    }
-
-    GemmEpi u{};
-    u.kind = EPI_SWIGLU;
-    u.act = c->a;
-    {
-        Stage t(c, DIT_ST_UP);
-        DIT_LAUNCH(c, launch_gemm(c->h2, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st, true), "up");
-    }
-    g.gate = mod + 5 * D;
-    {
-        Stage t(c, DIT_ST_DOWN);
-        DIT_LAUNCH(c, launch_gemm(c->a, b->w[3], b->scale[3], w8, S, D, F, g, st, true), "down");
-    }
     return DIT_OK;
 }
 
@@ -492,8 +432,30 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
         }
         return DIT_OK;
     };
-    // OUT / DOWN: x[run] += gate(run) * (a_base[run] W^T), two runs per launch
-    auto gated = [&](const uint16_t *a_base, int lda, int w, int K, int gate_at, int stage) -> dit_status {
+    // OUT / DOWN: x[run] += gate(run) * (a_base[run] W^T), two runs per
+    // launch; a sandwich block's product writes its rows in fp32 and the
+    // post norm adds them, normed, with the run's gate
+    auto gated = [&](const uint16_t *a_base, int lda, int w, int K, int gate_at, int stage,
+                     const float *post) -> dit_status {
+        if (post) {
+            GemmEpi f{};
+            f.kind = EPI_F32;
+            f.out = c->yf;
+            f.ldo = D;
+            {
+                Stage t(c, stage);
+                DIT_LAUNCH(c, launch_gemm(a_base, b->w[w], b->scale[w], w8, S, D, K, f, st, true), "product");
+            }
+            for (int i = 0; i < n_runs; ++i) {
+                const int r0 = runs[3 * i], r1 = runs[3 * i + 1];
+                Stage t(c, DIT_ST_POST);
+                DIT_LAUNCH(c, launch_post_norm_gate(c->yf + int64_t(r0) * D, r1 - r0, D, post, rms, A.eps,
+                                                    mod + int64_t(runs[3 * i + 2]) * 6 * D + gate_at,
+                                                    x + int64_t(r0) * D, st),
+                           "post norm");
+            }
+            return DIT_OK;
+        }
         for (int i = 0; i < n_runs; i += 2) {
             GemmEpi g[2]{};
             int f[2] = {0, 0}, rows[2] = {0, 0};
@@ -533,7 +495,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
         Stage t(c, DIT_ST_ATTN);
         DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
     }
-    DIT_TRY(gated(c->o, D, 1, D, 2 * D, DIT_ST_OUT));
+    DIT_TRY(gated(c->o, D, 1, D, 2 * D, DIT_ST_OUT, b->post_w[0]));
     DIT_TRY(norms(mod + 3 * D, DIT_ST_NORM2, c->h2, b->norm_w[1]));
     GemmEpi u{};
     u.kind = EPI_SWIGLU;
@@ -542,8 +504,16 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
         Stage t(c, DIT_ST_UP);
         DIT_LAUNCH(c, launch_gemm(c->h2, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st, true), "up");
     }
-    DIT_TRY(gated(c->a, F, 3, F, 5 * D, DIT_ST_DOWN));
+    DIT_TRY(gated(c->a, F, 3, F, 5 * D, DIT_ST_DOWN, b->post_w[1]));
     return DIT_OK;
+}
+
+// The block forward ([GZ] Block.forward; validated arguments): one run of
+// all rows on the one modulation row.
+dit_status block_forward(dit_ctx *c, const dit_block *b, float *x, const float *vec, const float *cs,
+                         const float *sn, int S) {
+    const int32_t one[3] = {0, S, 0};
+    return block_forward_runs(c, b, x, vec, 1, one, 1, cs, sn, S);
 }
 
 dit_status time_vector(dit_ctx *c, const uint16_t *w1, const uint16_t *w2, float t, float *vec) {
@@ -562,7 +532,7 @@ dit_status check_model(dit_ctx *c, const dit_model *m) {
     if (m->n_blocks > 0 && !m->blocks) return fail(c, DIT_EINVAL, "model blocks array is NULL");
     if (!m->w_t1 || !m->w_t2 || !m->w_in || !m->w_txt || !m->w_fmod || !m->w_final)
         return fail(c, DIT_EINVAL, "a model weight pointer is NULL");
-    for (int i = 0; i < m->n_blocks; ++i) DIT_TRY(check_block(c, &m->blocks[i]));
+    for (int i = 0; i < m->n_blocks; ++i) DIT_TRY(check_block(c, &m->blocks[i], false, true));
     return DIT_OK;
 }
 
@@ -612,7 +582,7 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
         Sx * D * 2, Sx * F * 2,                                        // o a
         S * size_t(arch->latent) * 2, S * size_t(arch->text_dim) * 2,  // latb ctxb
         S * D * 4, S * size_t(arch->latent) * 4,                       // seq vel
-        S * (D + F) * 2,                                               // oa
+        S * std::max((D + F) * 2, D * 4),                              // oa (yf)
     };
     size_t off[sizeof sizes / sizeof sizes[0]];
     size_t total = 0;
@@ -643,6 +613,7 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
     c->seq = reinterpret_cast<float *>(p + off[14]);
     c->vel = reinterpret_cast<float *>(p + off[15]);
     c->oa = reinterpret_cast<uint16_t *>(p + off[16]);
+    c->yf = reinterpret_cast<float *>(p + off[16]);
     const size_t dbg[9] = {sizes[0], sizes[5], sizes[7], sizes[8], sizes[9], sizes[10], sizes[6], sizes[11], sizes[16]};
     for (int i = 0; i < 9; ++i) c->bytes[i] = dbg[i];
     *out = c;
@@ -783,7 +754,7 @@ dit_status dit_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const f
                              const float *sin_t, int L, int N) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
-    DIT_TRY(check_block(ctx, b));
+    DIT_TRY(check_block(ctx, b, false, true));
     DIT_TRY(check_rows(ctx, L, N));
     DIT_TRY(check_ctx(ctx));
     return block_forward(ctx, b, x, vec, cos_t, sin_t, L + N);
@@ -804,7 +775,7 @@ dit_status dit_block_forward_runs(dit_ctx *ctx, const dit_block *b, float *x, co
                                   int N) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (!x || !vecs || !runs || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vecs, runs, cos or sin is NULL");
-    DIT_TRY(check_block(ctx, b));
+    DIT_TRY(check_block(ctx, b, false, true));
     DIT_TRY(check_rows(ctx, L, N));
     if (R < 1 || R > kMaxModRows) return fail(ctx, DIT_ERANGE, "R = %d outside 1..%d", R, kMaxModRows);
     if (n_runs < 1 || n_runs > L + N) return fail(ctx, DIT_ERANGE, "n_runs = %d outside 1..%d", n_runs, L + N);

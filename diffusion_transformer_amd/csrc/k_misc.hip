@@ -246,6 +246,60 @@ k_modnorm(const float *__restrict__ x, int D, const float *__restrict__ shift,
     }
 }
 
+// One row per workgroup, as k_modnorm: the row of y stays in registers
+// between the statistics and the update.
+__global__ void __launch_bounds__(kNormThreads)
+k_post_norm_gate(const float *__restrict__ y, int D, const float *__restrict__ nw, int rms, float eps,
+                 const float *__restrict__ gate, float *__restrict__ x) {
+    __shared__ float red[kNormThreads / 64];
+    const int64_t r = blockIdx.x;
+    const float4 *yr = reinterpret_cast<const float4 *>(y + r * D);
+    const int n4 = D / 4;
+    float4 v[4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        v[i] = c < n4 ? yr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float invD = 1.0f / static_cast<float>(D);
+    float mu = 0.f;
+    if (!rms) mu = block_sum(s, red) * invD;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        if (c < n4) {
+            float a = v[i].x - mu, b = v[i].y - mu, cc = v[i].z - mu, d = v[i].w - mu;
+            q += (a * a + b * b) + (cc * cc + d * d);
+        }
+    }
+    const float rstd = rsqrtf(block_sum(q, red) * invD + eps);
+    float4 *xr = reinterpret_cast<float4 *>(x + r * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        if (c >= n4) continue;
+        const float4 w = reinterpret_cast<const float4 *>(nw)[c];
+        const float4 g = reinterpret_cast<const float4 *>(gate)[c];
+        float4 o = xr[c];
+        o.x += g.x * ((v[i].x - mu) * rstd * w.x);
+        o.y += g.y * ((v[i].y - mu) * rstd * w.y);
+        o.z += g.z * ((v[i].z - mu) * rstd * w.z);
+        o.w += g.w * ((v[i].w - mu) * rstd * w.w);
+        xr[c] = o;
+    }
+}
+
+hipError_t launch_post_norm_gate(const float *y, int rows, int D, const float *w, bool rms, float eps,
+                                 const float *gate, float *x, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (D % 4 != 0 || D > 16 * kNormThreads) return hipErrorInvalidValue;
+    k_post_norm_gate<<<rows, kNormThreads, 0, st>>>(y, D, w, rms ? 1 : 0, eps, gate, x);
+    return hipGetLastError();
+}
+
 hipError_t launch_modnorm(const float *x, int rows, int D, const float *shift, const float *scale,
                           const float *norm_w, bool rms, float eps, uint16_t *out, hipStream_t st) {
     if (rows <= 0) return hipSuccess;

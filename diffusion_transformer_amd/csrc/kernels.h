@@ -25,6 +25,12 @@ hipError_t launch_gemv(const uint16_t *W, const float *x, int O, int I, bool sil
 
 // out[r] = bf16(norm(x[r]) * (1 + scale) + shift), r < rows; D <= 4096,
 // D a multiple of 4.  rms: RMSNorm times norm_w; else LayerNorm.
+// x[r] += gate * (norm(y[r]) * w) for r < rows: a sandwich block's norm of
+// a product's output rows before the gate ([GZ] POST_ATTN / POST_MLP); the
+// norm is LayerNorm (rms false) or RMSNorm, eps as given; y, x fp32 [rows, D]
+hipError_t launch_post_norm_gate(const float *y, int rows, int D, const float *w, bool rms, float eps,
+                                 const float *gate, float *x, hipStream_t st);
+
 hipError_t launch_modnorm(const float *x, int rows, int D, const float *shift, const float *scale,
                           const float *norm_w, bool rms, float eps, uint16_t *out, hipStream_t st);
 

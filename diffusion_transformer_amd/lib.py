@@ -28,7 +28,7 @@ _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, ERANGE, ENOMEM, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 STAGES = ("mod", "norm1", "qkv", "attn", "out", "norm2", "up", "down", "time", "img_in", "final",
-          "euler", "txt_in", "par_in", "par_out")
+          "euler", "txt_in", "par_in", "par_out", "post")
 W_BF16, W_INT8_B32 = 0, 1
 NORM_LAYER, NORM_RMS = 0, 1
 _NAMES = {0: "DIT_OK", -1: "DIT_EINVAL", -2: "DIT_ERANGE", -3: "DIT_ENOMEM", -4: "DIT_EDEVICE",
@@ -51,7 +51,7 @@ class Arch(C.Structure):
 
 class Block(C.Structure):
     _fields_ = [("wtype", C.c_int32), ("w", C.c_void_p * 4), ("scale", C.c_void_p * 4),
-                ("norm_w", C.c_void_p * 4), ("w_mod", C.c_void_p)]
+                ("norm_w", C.c_void_p * 4), ("w_mod", C.c_void_p), ("post_w", C.c_void_p * 2)]
 
 
 class Model(C.Structure):
@@ -308,6 +308,8 @@ class BlockWeights:
         for i, n in enumerate(("norm1", "norm2", "q_norm", "k_norm")):
             b.norm_w[i] = _ptr(tensors.get(n), torch.float32, n)
         b.w_mod = _ptr(tensors["w_mod"], torch.bfloat16, "w_mod")
+        for i, n in enumerate(("post_attn", "post_mlp")):
+            b.post_w[i] = _ptr(tensors.get(n), torch.float32, n)
         self.struct = b
 
     @classmethod
@@ -318,7 +320,7 @@ class BlockWeights:
         for k, v in bw.items():
             if k.startswith("q_w"):
                 t[k] = torch.from_numpy(v).to(device)
-            elif k in ("q_norm", "k_norm", "norm1", "norm2"):
+            elif k in ("q_norm", "k_norm", "norm1", "norm2", "post_attn", "post_mlp"):
                 t[k] = dev_f32(v, device)
             else:
                 t[k] = dev_bf16(v, device)

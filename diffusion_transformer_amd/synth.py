@@ -134,12 +134,13 @@ def int8_weight(rng, out: int, inn: int):
     return q, s
 
 
-def block_weights(rng, sh: Shape, std=0.02, norm_std=0.0, int8=None, rms=False):
+def block_weights(rng, sh: Shape, std=0.02, norm_std=0.0, int8=None, rms=False, sandwich=False):
     """Weights of one block as a dict of float32 arrays (bf16 values).
     Keys: w_qkv [3D, D], w_out [D, D], w_up [2F, D], w_down [D, F],
     w_mod [6D, D], q_norm [hd], k_norm [hd] and, with rms=True, norm1/norm2
     [D].  With int8, the four linears are replaced by (codes, scales) pairs
-    under keys q_<name> and s_<name>."""
+    under keys q_<name> and s_<name>.  With sandwich=True, the post norms'
+    weights post_attn/post_mlp [D] ~ N(1, 0.2^2), drawn last."""
     D, F, hd = sh.hidden, sh.ffn, sh.head_dim
     int8 = sh.int8 if int8 is None else int8
     dims = {"w_qkv": (3 * D, D), "w_out": (D, D), "w_up": (2 * F, D), "w_down": (D, F)}
@@ -161,10 +162,13 @@ def block_weights(rng, sh: Shape, std=0.02, norm_std=0.0, int8=None, rms=False):
     if rms:
         out["norm1"] = normw(D)
         out["norm2"] = normw(D)
+    if sandwich:
+        for k in ("post_attn", "post_mlp"):
+            out[k] = bf16_round(1.0 + rng.standard_normal(D, dtype=np.float32) * np.float32(0.2))
     return out
 
 
-def block_case(name: str = "tiny", seed=None, norm_std=0.0, rms=False, t=None):
+def block_case(name: str = "tiny", seed=None, norm_std=0.0, rms=False, t=None, sandwich=False):
     """Inputs of one block forward: rows x [S, D] ~ N(0,1) (float32, fp32 on
     the GPU too), the time t (0.5 for `tiny`, else U(0,1)), the time MLP
     weights w_t1 [D, 256] and w_t2 [D, D], and the block's weights."""
@@ -175,7 +179,7 @@ def block_case(name: str = "tiny", seed=None, norm_std=0.0, rms=False, t=None):
         t = 0.5 if name == "tiny" else float(rng.uniform(0.0, 1.0))
     w_t1 = _normal(rng, (sh.hidden, sh.time_dim), 0.02)
     w_t2 = _normal(rng, (sh.hidden, sh.hidden), 0.02)
-    bw = block_weights(rng, sh, norm_std=norm_std, rms=rms)
+    bw = block_weights(rng, sh, norm_std=norm_std, rms=rms, sandwich=sandwich)
     return dict(shape=sh, x=x, t=np.float32(t), w_t1=w_t1, w_t2=w_t2, block=bw)
 
 

@@ -90,13 +90,20 @@ typedef struct {
  * norm_w: fp32.  [0] NORM1, [1] NORM2 ([D], required for DIT_NORM_RMS,
  *   ignored for DIT_NORM_LAYER), [2] Q_NORM, [3] K_NORM ([hd], required).
  * w_mod: bf16 [6D, D]; its output rows are shift, scale, gate of the
- *   attention, then of the MLP ([GZ] Modulation). */
+ *   attention, then of the MLP ([GZ] Modulation).
+ * post_w: fp32 [D] or NULL.  A sandwich block ([GZ] POST_ATTN, POST_MLP)
+ *   sets both: [0] after the attention, [1] after the MLP; each half's
+ *   product output row is normed (the arch's norm kind and eps, times the
+ *   weight) before its gate.  Both NULL: the gated outputs are added as
+ *   they are.  Only the sequential forms (dit_block_forward,
+ *   dit_block_forward_runs, the blocks of dit_denoise_step) take them. */
 typedef struct {
     int32_t wtype;
     const void *w[4];
     const uint16_t *scale[4];
     const float *norm_w[4];
     const uint16_t *w_mod;
+    const float *post_w[2];
 } dit_block;
 
 /* The whole DiT ([HC] s.1 DiT graph).  All bf16 [out, in]:
@@ -286,7 +293,8 @@ typedef enum {
     DIT_ST_TXT_IN = 12, /* prologue: text features -> bf16, text-in product */
     DIT_ST_PAR_IN = 13, /* parallel block: [QKV | UP] product, both epilogues */
     DIT_ST_PAR_OUT = 14,/* parallel block: [OUT | DOWN] product + gated residual */
-    DIT_NSTAGES = 15
+    DIT_ST_POST = 15,   /* sandwich block: norm of a product's output, gate, residual */
+    DIT_NSTAGES = 16
 } dit_stage;
 
 /* Per-stage timing, a measurement aid ([K4] s.3: every op of the busy time

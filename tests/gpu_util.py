@@ -72,7 +72,8 @@ def oracle_block(bw: dict) -> "O.BlockWeights":
         return bw[n]
     return O.BlockWeights(w_qkv=lin("w_qkv"), w_out=lin("w_out"), w_up=lin("w_up"),
                           w_down=lin("w_down"), w_mod=bw["w_mod"], q_norm=bw["q_norm"],
-                          k_norm=bw["k_norm"], norm1=bw.get("norm1"), norm2=bw.get("norm2"))
+                          k_norm=bw["k_norm"], norm1=bw.get("norm1"), norm2=bw.get("norm2"),
+                          post_attn=bw.get("post_attn"), post_mlp=bw.get("post_mlp"))
 
 
 class GpuSeq:

@@ -547,6 +547,95 @@ def test_block_runs_rejects_bad_runs(ctx_tiny):
         with pytest.raises(RuntimeError):
             _runs_gpu(ctx_tiny, case, runs)
 
+
+# --------------------------------------------------------------- sandwich norms
+
+@pytest.mark.parametrize("name,norm,norm_std", [("tiny", "layer", 0.0), ("tiny", "rms", 0.1),
+                                                 ("s1088", "layer", 0.0), ("s1088", "rms", 0.1)])
+def test_sandwich_block_full_parity(name, norm, norm_std):
+    case = synth.block_case(name, norm_std=norm_std, rms=(norm == "rms"), sandwich=True)
+    sh = case["shape"]
+    la, oa = arch_pair(sh, norm)
+    ctx = L.Context(la, max_rows=sh.S)
+    say("sandwich block", name, norm, "S =", sh.S)
+    x, _, _ = _block_gpu(ctx, case, norm)
+    got = np_of(x)
+    inter = _intermediates(ctx, sh, sh.S)
+    cs, sn, vec = _oracle_inputs(case, oa)
+    y, ref = O.block_forward(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, keep=True)
+    for k in ("h", "o", "h2", "a"):   # h2 follows the attention half's post norm
+        compare(f"{name}/{k}", inter[k], ref[k], bf16_stored=True)
+    compare(f"{name}/y", got, y)
+    compare(f"{name}/delta", got - case["x"], y - case["x"])
+    ctx.close()
+
+
+@pytest.mark.parametrize("name", ["s4608", "s4608_int8"])
+def test_sandwich_block_full_size_sampled_rows(ctx_big, name):
+    case = synth.block_case(name, sandwich=True)
+    sh = case["shape"]
+    _, oa = arch_pair(sh)
+    say("sandwich block", name, "S =", sh.S)
+    x, _, _ = _block_gpu(ctx_big, case)
+    got = np_of(x)
+    inter = _intermediates(ctx_big, sh, sh.S)
+    cs, sn, vec = _oracle_inputs(case, oa)
+    rows = synth.rows_sample(sh.S, 48, L=sh.L)
+    y, o, x1, a = O.block_forward_rows(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, rows)
+    # int8 weights: tolerance relative to the reference's largest magnitude
+    sc = (lambda r: max(1.0, REL * float(np.abs(r).max()) / ABS)) if sh.int8 else (lambda r: 1.0)
+    compare(f"{name}/o", inter["o"][rows], o, abs_=ABS * sc(o), bf16_stored=True)
+    compare(f"{name}/a", inter["a"][rows], a, abs_=ABS * sc(a), bf16_stored=True)
+    compare(f"{name}/y", got[rows], y, abs_=ABS * sc(y))
+    d = y - case["x"][rows]
+    compare(f"{name}/delta", got[rows] - case["x"][rows], d, abs_=ABS * sc(d))
+
+
+def test_sandwich_block_runs_parity(ctx_tiny):
+    case = synth.block_case("tiny", sandwich=True)
+    sh = case["shape"]
+    case["vecs"] = synth.normal((3, sh.hidden), seed=sh.seed + 200, std=0.13)
+    _, oa = arch_pair(sh)
+    runs = _runs_of("tiny", sh)
+    say("sandwich block runs", runs)
+    got = np_of(_runs_gpu(ctx_tiny, case, runs))
+    cs, sn, _ = _oracle_inputs(case, oa)
+    y = O.block_forward_runs(case["x"], oracle_block(case["block"]), case["vecs"], runs, cs, sn, oa)
+    compare("tiny/y", got, y)
+    compare("tiny/delta", got - case["x"], y - case["x"])
+
+
+def test_sandwich_block_zero_gates_is_identity(ctx_tiny):
+    case = synth.block_case("tiny", sandwich=True)
+    D = case["shape"].hidden
+    case["block"]["w_mod"][2 * D:3 * D] = 0.0
+    case["block"]["w_mod"][5 * D:] = 0.0
+    x, _, _ = _block_gpu(ctx_tiny, case)
+    assert (np_of(x) == case["x"]).all()
+
+
+def test_sandwich_weights_rejected_where_not_taken(ctx_tiny):
+    case = synth.block_case("tiny", sandwich=True)
+    sh = case["shape"]
+    seq = GpuSeq(ctx_tiny, sh, case["t"], case["w_t1"], case["w_t2"])
+    x = L.dev_f32(case["x"])
+    one = dict(case["block"])
+    del one["post_mlp"]
+    with pytest.raises(L.DitError) as e:
+        ctx_tiny.block_forward(L.BlockWeights.from_host(one), x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    assert e.value.status == L.EINVAL
+    bw = L.BlockWeights.from_host(case["block"])
+    with pytest.raises(L.DitError) as e:
+        ctx_tiny.double_block_forward(bw, bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    assert e.value.status == L.EINVAL
+    pb = dict(case["block"])
+    pb["w_mod"] = np.ascontiguousarray(pb["w_mod"][:3 * sh.hidden])
+    with pytest.raises(L.DitError) as e:
+        ctx_tiny.parallel_block_forward(L.BlockWeights.from_host(pb), x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    assert e.value.status == L.EINVAL
+    torch.cuda.synchronize()
+    assert (np_of(x) == case["x"]).all()
+
 # --------------------------------------------------------------- denoise
 
 def test_denoise_twin(ctx_tiny):
