@@ -26,6 +26,11 @@ Sources (web pages; cited by title and section):
         Block.forward, Block.parallel; constants HEAD, QKV/OUT/UP/DOWN,
         POST_ATTN/POST_MLP (sandwich norms).
 
+`quantize_rows_int8` is pinned by a worked example (ties to even, the
+largest magnitude to 127, zero rows), the half-step error bound, and
+`linear_w8a8` by brute-force integer sums and the error bound of the
+activations' rounding.
+
 Readings of points the pages leave open are listed in the repository's
 design notes; the ones that shape the arithmetic are restated where used.
 
@@ -173,9 +178,54 @@ def timestep_embedding(t: float, dim: int = 256) -> np.ndarray:
     return sinusoids([1000.0 * float(t)], dim)[0]
 
 
-def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """x W^T with W stored [out, in] ([GZ] Block: linears [out, in])."""
+def linear(x: np.ndarray, w) -> np.ndarray:
+    """x W^T with W stored [out, in] ([GZ] Block: linears [out, in]).  An
+    Int8Rows weight takes x's rows through INT8 too (linear_w8a8)."""
+    if isinstance(w, Int8Rows):
+        return linear_w8a8(x, w)
     return np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+
+
+# ---------------------------------------------------------------------------
+# W8A8 linears ([GZ] linear and quantizedOf: a linear with INT8 weights takes
+# x's rows as INT8 with one scale a row, and the product is the integer dot
+# product times x's scale and W's; [K4] Appendix B, D4: symmetric weights
+# with one absmax/127 scale per output row, activations quantized per token
+# at each call, int8 x int8 -> int32, then an fp32 dequantisation)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Int8Rows:
+    """A linear's weights as INT8 rows q [out, in] and one float32 scale per
+    row s [out]: W = q * s[:, None]."""
+
+    q: np.ndarray
+    s: np.ndarray
+
+
+def quantize_rows_int8(x):
+    """Symmetric INT8 codes of each row of x over one scale a row:
+    s = max|x| / 127 and q = x / s rounded to nearest, ties to even, so
+    |q| <= 127 and the largest magnitude maps to +-127; an all-zero row has
+    s = 0 and q = 0.  Where floating point decides an integer both sides
+    decide in one precision; the pages fix none, so it is the kernels'
+    float32: x is taken to float32, inv = 127 / amax and q = rint(x * inv),
+    s = amax / 127, each a correctly rounded float32 operation.  Returns
+    (q int8 [..., K], s float32 [...])."""
+    x = np.asarray(x, dtype=F32)
+    amax = np.abs(x).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        inv = np.where(amax > 0, F32(127) / amax, F32(0)).astype(F32)
+    q = np.clip(np.rint(x * inv[..., None]), -127, 127).astype(np.int8)
+    return q, (amax / F32(127)).astype(F32)
+
+
+def linear_w8a8(x, w: Int8Rows) -> np.ndarray:
+    """x W^T with x's rows quantized by quantize_rows_int8: the exact integer
+    dot products (int64) times x's row scale and W's row scale, in float64."""
+    q, s = quantize_rows_int8(x)
+    acc = q.astype(np.int64) @ np.asarray(w.q).astype(np.int64).T
+    return acc * np.asarray(s, F64)[..., None] * np.asarray(w.s, F64)[None, :]
 
 
 def time_vector(t: float, w_t1: np.ndarray, w_t2: np.ndarray, dim: int = 256):

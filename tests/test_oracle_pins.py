@@ -606,6 +606,73 @@ def test_sandwich_weights_belong_to_the_sequential_forms():
     with pytest.raises(ValueError):
         O.double_block_forward(x, bw, bw, vecc, c, s, arch, 2)
 
+
+# ---------------------------------------------------------------- W8A8 linears
+
+def test_quantize_rows_worked_example():
+    # max |x| = 127 gives inv = s = 1: the codes are x rounded to nearest,
+    # ties to even (63.5 -> 64, 62.5 -> 62, -0.5 -> 0, 1.5 -> 2)
+    q, s = O.quantize_rows_int8([[127.0, 63.5, 62.5, -0.5, 1.5, -126.4, 0.0],
+                                 [0.0] * 7,
+                                 [-2.0, 1.0, 0.0, 0.0, 0.0, 0.0, 0.0]])
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert q[0].tolist() == [127, 64, 62, 0, 2, -126, 0] and s[0] == 1.0
+    assert q[1].tolist() == [0] * 7 and s[1] == 0.0                       # zero row
+    assert q[2].tolist()[:2] == [-127, 64] and s[2] == np.float32(2.0) / np.float32(127)   # 63.5 -> 64
+
+
+def test_quantize_rows_error_bound():
+    rng = np.random.default_rng(60)
+    x = rng.standard_normal((50, 96)) * rng.uniform(0.01, 100, (50, 1))
+    q, s = O.quantize_rows_int8(x)
+    amax = np.abs(x).max(axis=1)
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    assert np.all(np.abs(q.astype(int)).max(axis=1) == 127)               # the largest magnitude
+    assert np.allclose(s, amax / 127, rtol=1e-6)
+    err = np.abs(x - q * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5) + amax[:, None] * 1e-6)
+
+
+def test_w8a8_linear_brute_force():
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((3, 5))
+    w = O.Int8Rows(q=rng.integers(-127, 128, (4, 5)).astype(np.int8), s=rng.uniform(0.001, 0.01, 4).astype(np.float32))
+    qx, sx = O.quantize_rows_int8(x)
+    y = O.linear(x, w)
+    for i in range(3):
+        for j in range(4):
+            acc = sum(int(qx[i, k]) * int(w.q[j, k]) for k in range(5))
+            assert abs(y[i, j] - acc * float(sx[i]) * float(w.s[j])) <= 1e-12 * max(1.0, abs(y[i, j]))
+
+
+def test_w8a8_linear_error_bound():
+    # with the weights exact (q * s), only x's rounding errs: each output is
+    # off the exact product by at most sum_k |W[j, k]| * s_x / 2
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal((20, 64))
+    w = O.Int8Rows(q=rng.integers(-127, 128, (8, 64)).astype(np.int8), s=rng.uniform(0.001, 0.01, 8).astype(np.float32))
+    wd = w.q.astype(np.float64) * w.s[:, None]
+    _, sx = O.quantize_rows_int8(x)
+    bound = (sx[:, None].astype(np.float64) * (0.5 + 1e-5) + np.abs(x).max(1, keepdims=True) * 1e-6) @ np.abs(wd).sum(1)[None, :]
+    err = np.abs(O.linear(x, w) - x @ wd.T)
+    assert np.all(err <= bound)
+    assert err.max() > 0                                                     # the rounding is there
+
+
+def test_w8a8_block_is_close_to_the_float_block():
+    # the same block with INT8 weights, its products' inputs taken to INT8:
+    # close to the float block of the dequantized weights, not equal
+    W, pos, x, vecc = _tiny_case(seed=63)
+    Wq = dict(W)
+    for n in ("w_qkv", "w_out", "w_up", "w_down"):
+        q, s = O.quantize_rows_int8(W[n])
+        Wq[n] = O.Int8Rows(q=q, s=s)
+        W[n] = q.astype(np.float64) * s[:, None]
+    ref = _oracle_block(W, pos, x, vecc, TINY)
+    got = _oracle_block(Wq, pos, x, vecc, TINY)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref - x)
+    assert 0 < rel < 2e-2
+
 # ---------------------------------------------------------------- double-stream block
 
 def _double(Wt, Wi, pos, x, vecc, L, arch=TINY):
