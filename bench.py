@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--no-double", action="store_true", help="skip the double-stream block timing")
     p.add_argument("--no-runs", action="store_true", help="skip the timing of the block with modulation runs")
     p.add_argument("--no-sandwich", action="store_true", help="skip the sandwich block timing")
+    p.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 block timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
                         "scale reference for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -375,6 +376,24 @@ def main():
         log(f"int8 block: {ms8:.3f} ms  {int8_tf:.1f} TFLOP/s")
         del bw8, x8, c8
         torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- W8A8 block
+    w8 = None
+    if not args.no_w8a8:
+        log("W8A8 block (INT8 weight rows, INT8 activation rows, int8 matrix cores)")
+        cw = synth.block_case("s4608_w8a8")
+        bww = L.BlockWeights.from_host(cw["block"])
+        xw = L.dev_f32(cw["x"])
+
+        def wfwd():
+            ctx.block_forward(bww, xw, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        msw = time_call(torch, wfwd, args.steps, args.warmup)
+        w_tf = total_flops / (msw * 1e-3) / 1e12
+        w8 = {"ms": round(msw, 4), "tflops": round(w_tf, 2), "flops_per_step": total_flops,
+              "stages_ms_per_step": stage_split(ctx, wfwd, args.steps)}
+        log(f"W8A8 block: {msw:.3f} ms  {w_tf:.1f} TFLOP/s (int8 ops)")
+        del bww, xw, cw
+        torch.cuda.empty_cache()
     ctx.close()
 
     # ---------------------------------------------------------------- whole image
@@ -410,6 +429,7 @@ def main():
         "double_block": dbl,
         "runs_block": runs_res,
         "sandwich_block": sw,
+        "w8a8_block": w8,
     }
     if img:
         out.update(img)

@@ -40,6 +40,10 @@ struct dit_ctx {
     // (the sequential and the parallel block never run at once on one
     // context: its calls are ordered on its stream)
     float *yf = nullptr;
+    // W8A8 blocks: a product's A rows as INT8 codes [Sx, max(D, F)] and
+    // their scales [Sx]
+    int8_t *aq = nullptr;
+    float *as = nullptr;
     float *seq = nullptr, *vel = nullptr;
     size_t bytes[9] = {};
     std::string err;
@@ -61,6 +65,9 @@ namespace {
 constexpr int kMaxModRows = 8;
 
 thread_local std::string g_err;
+
+// a block's bf16 block-32 weight scales (DIT_W_INT8_B32)
+inline const uint16_t *bscale(const dit_block *b, int i) { return static_cast<const uint16_t *>(b->scale[i]); }
 
 dit_status fail(dit_ctx *c, dit_status s, const char *fmt, ...) {
     char buf[512];
@@ -163,14 +170,17 @@ dit_status check_ctx(dit_ctx *c) {
     return DIT_OK;
 }
 
-// `sandwich`: whether the form takes a sandwich block's post norms (the
-// sequential forms); the others reject them.
-dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bool sandwich = false) {
+// `sequential`: whether the form is a sequential one, which alone takes a
+// sandwich block's post norms and W8A8 weights; the others reject them.
+dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bool sequential = false) {
     if (!b) return fail(c, DIT_EINVAL, "block is NULL");
-    if (b->wtype != DIT_W_BF16 && b->wtype != DIT_W_INT8_B32) return fail(c, DIT_EINVAL, "unknown wtype %d", b->wtype);
+    if (b->wtype != DIT_W_BF16 && b->wtype != DIT_W_INT8_B32 && b->wtype != DIT_W_INT8_ROW)
+        return fail(c, DIT_EINVAL, "unknown wtype %d", b->wtype);
+    if (b->wtype == DIT_W_INT8_ROW && !sequential)
+        return fail(c, DIT_EINVAL, "W8A8 weights are taken by the sequential block forms only");
     for (int i = 0; i < 4; ++i) {
         if (!b->w[i]) return fail(c, DIT_EINVAL, "block weight w[%d] is NULL", i);
-        if (b->wtype == DIT_W_INT8_B32 && !b->scale[i]) return fail(c, DIT_EINVAL, "int8 weight %d has no scales", i);
+        if (b->wtype != DIT_W_BF16 && !b->scale[i]) return fail(c, DIT_EINVAL, "int8 weight %d has no scales", i);
         if (b->wtype == DIT_W_BF16 && b->scale[i]) return fail(c, DIT_EINVAL, "bf16 weight %d given scales", i);
     }
     if (!b->w_mod) return fail(c, DIT_EINVAL, "block w_mod is NULL");
@@ -179,7 +189,7 @@ dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bo
         return fail(c, DIT_EINVAL, parallel ? "RMSNorm needs norm weight NORM1" : "RMSNorm needs norm weights NORM1 and NORM2");
     if (!b->post_w[0] != !b->post_w[1])
         return fail(c, DIT_EINVAL, "a sandwich block needs both post-norm weights (POST_ATTN and POST_MLP)");
-    if (b->post_w[0] && !sandwich)
+    if (b->post_w[0] && !sequential)
         return fail(c, DIT_EINVAL, "sandwich norms are taken by the sequential block forms only");
     return DIT_OK;
 }
@@ -261,14 +271,14 @@ dit_status parallel_block_forward(dit_ctx *c, const dit_block *b, float *x, cons
     }
     {
         Stage t(c, DIT_ST_QKV);
-        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], b->scale[0], w8, S, 3 * D, D, e, st, true), "qkv");
+        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], bscale(b, 0), w8, S, 3 * D, D, e, st, true), "qkv");
     }
     GemmEpi u{};
     u.kind = EPI_SWIGLU;
     u.act = c->a;
     {
         Stage t(c, DIT_ST_UP);
-        DIT_LAUNCH(c, launch_gemm(c->h, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st, true), "up");
+        DIT_LAUNCH(c, launch_gemm(c->h, b->w[2], bscale(b, 2), w8, S, 2 * F, D, u, st, true), "up");
     }
     {
         Stage t(c, DIT_ST_ATTN);
@@ -276,11 +286,11 @@ dit_status parallel_block_forward(dit_ctx *c, const dit_block *b, float *x, cons
     }
     {
         Stage t(c, DIT_ST_OUT);
-        DIT_LAUNCH(c, launch_gemm(c->o, b->w[1], b->scale[1], w8, S, D, D, g, st, true), "out");
+        DIT_LAUNCH(c, launch_gemm(c->o, b->w[1], bscale(b, 1), w8, S, D, D, g, st, true), "out");
     }
     {
         Stage t(c, DIT_ST_DOWN);
-        DIT_LAUNCH(c, launch_gemm(c->a, b->w[3], b->scale[3], w8, S, D, F, g, st, true), "down");
+        DIT_LAUNCH(c, launch_gemm(c->a, b->w[3], bscale(b, 3), w8, S, D, F, g, st, true), "down");
     }
     return DIT_OK;
 }
@@ -326,7 +336,7 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
             for (int i = 1; i >= 0 && e == hipSuccess; --i) {
                 const Stream &t = sts[i];
                 if (t.rows)
-                    e = launch_gemm(a_base + int64_t(t.r0) * a_ld, t.b->w[w], t.b->scale[w], t.b->wtype == DIT_W_INT8_B32,
+                    e = launch_gemm(a_base + int64_t(t.r0) * a_ld, t.b->w[w], bscale(t.b, w), t.b->wtype == DIT_W_INT8_B32,
                                     t.rows, n, k, ep[i], st, true);
             }
             return e;
@@ -421,22 +431,43 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
         DIT_LAUNCH(c, launch_gemv(b->w_mod, vecs + int64_t(r) * D, 6 * D, D, true, mod + int64_t(r) * 6 * D, st),
                    "modulation");
     }
+    // W8A8 (DIT_W_INT8_ROW): every product takes its A rows as INT8 codes
+    // and a scale a row in aq / as -- from the norms directly, from a
+    // quantization pass over o and a
+    const bool q8 = b->wtype == DIT_W_INT8_ROW;
     auto norms = [&](const float *shift_of, int which, uint16_t *out, const float *nw) -> dit_status {
         for (int i = 0; i < n_runs; ++i) {
             const int f = runs[3 * i], e = runs[3 * i + 1], m = runs[3 * i + 2];
             const float *mr = mod + int64_t(m) * 6 * D;
+            const float *sh = mr + (shift_of - mod), *sc = sh + D;
             Stage t(c, which);
-            DIT_LAUNCH(c, launch_modnorm(x + int64_t(f) * D, e - f, D, mr + (shift_of - mod), mr + (shift_of - mod) + D,
-                                         nw, rms, A.eps, out + int64_t(f) * D, st),
-                       "norm");
+            if (q8)
+                DIT_LAUNCH(c, launch_modnorm_i8(x + int64_t(f) * D, e - f, D, sh, sc, nw, rms, A.eps,
+                                                c->aq + int64_t(f) * D, c->as + f, st),
+                           "norm");
+            else
+                DIT_LAUNCH(c, launch_modnorm(x + int64_t(f) * D, e - f, D, sh, sc, nw, rms, A.eps, out + int64_t(f) * D, st),
+                           "norm");
         }
         return DIT_OK;
+    };
+    // the product of weight w over rows [r0, r0 + M) of A (bf16 a with row
+    // stride K, or the INT8 rows in aq / as)
+    auto product = [&](const uint16_t *a, int r0, int M, int w, int N, int K, const GemmEpi &ep) -> hipError_t {
+        if (q8)
+            return launch_gemm_w8a8(c->aq + int64_t(r0) * K, c->as + r0, static_cast<const int8_t *>(b->w[w]),
+                                    static_cast<const float *>(b->scale[w]), M, N, K, ep, st);
+        return launch_gemm(a + int64_t(r0) * K, b->w[w], bscale(b, w), w8, M, N, K, ep, st, true);
     };
     // OUT / DOWN: x[run] += gate(run) * (a_base[run] W^T), two runs per
     // launch; a sandwich block's product writes its rows in fp32 and the
     // post norm adds them, normed, with the run's gate
     auto gated = [&](const uint16_t *a_base, int lda, int w, int K, int gate_at, int stage,
                      const float *post) -> dit_status {
+        if (q8) {
+            Stage t(c, DIT_ST_QUANT);
+            DIT_LAUNCH(c, launch_quant_rows(a_base, S, K, c->aq, c->as, st), "quantize rows");
+        }
         if (post) {
             GemmEpi f{};
             f.kind = EPI_F32;
@@ -444,7 +475,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
             f.ldo = D;
             {
                 Stage t(c, stage);
-                DIT_LAUNCH(c, launch_gemm(a_base, b->w[w], b->scale[w], w8, S, D, K, f, st, true), "product");
+                DIT_LAUNCH(c, product(a_base, 0, S, w, D, K, f), "product");
             }
             for (int i = 0; i < n_runs; ++i) {
                 const int r0 = runs[3 * i], r1 = runs[3 * i + 1];
@@ -453,6 +484,19 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
                                                     mod + int64_t(runs[3 * i + 2]) * 6 * D + gate_at,
                                                     x + int64_t(r0) * D, st),
                            "post norm");
+            }
+            return DIT_OK;
+        }
+        if (q8) {
+            for (int i = 0; i < n_runs; ++i) {
+                const int r0 = runs[3 * i], r1 = runs[3 * i + 1];
+                GemmEpi g{};
+                g.kind = EPI_GATE_RES;
+                g.out = x + int64_t(r0) * D;
+                g.ldo = D;
+                g.gate = mod + int64_t(runs[3 * i + 2]) * 6 * D + gate_at;
+                Stage t(c, stage);
+                DIT_LAUNCH(c, product(a_base, r0, r1 - r0, w, D, K, g), "gated product");
             }
             return DIT_OK;
         }
@@ -468,8 +512,8 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
                 g[j].gate = mod + int64_t(runs[3 * (i + j) + 2]) * 6 * D + gate_at;
             }
             Stage t(c, stage);
-            DIT_LAUNCH(c, launch_gemm2(a_base + int64_t(f[0]) * lda, b->w[w], b->scale[w], rows[0], g[0],
-                                       a_base + int64_t(f[1]) * lda, b->w[w], b->scale[w], rows[1], g[1], w8, D, K, st),
+            DIT_LAUNCH(c, launch_gemm2(a_base + int64_t(f[0]) * lda, b->w[w], bscale(b, w), rows[0], g[0],
+                                       a_base + int64_t(f[1]) * lda, b->w[w], bscale(b, w), rows[1], g[1], w8, D, K, st),
                        "gated product");
         }
         return DIT_OK;
@@ -489,7 +533,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
     e.qk_eps = A.qk_eps;
     {
         Stage t(c, DIT_ST_QKV);
-        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], b->scale[0], w8, S, 3 * D, D, e, st, true), "qkv");
+        DIT_LAUNCH(c, product(c->h, 0, S, 0, 3 * D, D, e), "qkv");
     }
     {
         Stage t(c, DIT_ST_ATTN);
@@ -502,7 +546,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
     u.act = c->a;
     {
         Stage t(c, DIT_ST_UP);
-        DIT_LAUNCH(c, launch_gemm(c->h2, b->w[2], b->scale[2], w8, S, 2 * F, D, u, st, true), "up");
+        DIT_LAUNCH(c, product(c->h2, 0, S, 2, 2 * F, D, u), "up");
     }
     DIT_TRY(gated(c->a, F, 3, F, 5 * D, DIT_ST_DOWN, b->post_w[1]));
     return DIT_OK;
@@ -583,6 +627,7 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
         S * size_t(arch->latent) * 2, S * size_t(arch->text_dim) * 2,  // latb ctxb
         S * D * 4, S * size_t(arch->latent) * 4,                       // seq vel
         S * std::max((D + F) * 2, D * 4),                              // oa (yf)
+        Sx * std::max(D, F), Sx * 4,                                   // aq as
     };
     size_t off[sizeof sizes / sizeof sizes[0]];
     size_t total = 0;
@@ -614,6 +659,8 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
     c->vel = reinterpret_cast<float *>(p + off[15]);
     c->oa = reinterpret_cast<uint16_t *>(p + off[16]);
     c->yf = reinterpret_cast<float *>(p + off[16]);
+    c->aq = reinterpret_cast<int8_t *>(p + off[17]);
+    c->as = reinterpret_cast<float *>(p + off[18]);
     const size_t dbg[9] = {sizes[0], sizes[5], sizes[7], sizes[8], sizes[9], sizes[10], sizes[6], sizes[11], sizes[16]};
     for (int i = 0; i < 9; ++i) c->bytes[i] = dbg[i];
     *out = c;
@@ -736,6 +783,51 @@ dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint
     e.out = out;
     e.ldo = N;
     DIT_LAUNCH(ctx, launch_gemm(a, w, scale, wtype == DIT_W_INT8_B32, M, N, K, e, ctx->stream, false), "linear");
+    return DIT_OK;
+}
+
+dit_status dit_quantize_rows(dit_ctx *ctx, const uint16_t *x, int rows, int K, int8_t *q, float *s) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !q || !s) return fail(ctx, DIT_EINVAL, "x, q or s is NULL");
+    if (rows < 1) return fail(ctx, DIT_ERANGE, "rows %d < 1", rows);
+    if (K < 8 || K % 8 || K > 16384) return fail(ctx, DIT_EINVAL, "K %d: must be a multiple of 8 in 8..16384", K);
+    DIT_TRY(check_ctx(ctx));
+    DIT_LAUNCH(ctx, launch_quant_rows(x, rows, K, q, s, ctx->stream), "quantize rows");
+    return DIT_OK;
+}
+
+dit_status dit_modulated_norm_int8(dit_ctx *ctx, const float *x, int rows, const float *shift, const float *scale,
+                                   const float *norm_w, float eps, int8_t *q, float *s) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !shift || !scale || !q || !s) return fail(ctx, DIT_EINVAL, "x, shift, scale, q or s is NULL");
+    const bool rms = ctx->arch.norm == DIT_NORM_RMS;
+    if (rms && !norm_w) return fail(ctx, DIT_EINVAL, "RMSNorm needs norm_w");
+    if (rows < 1 || rows > ctx->max_rows) return fail(ctx, DIT_ERANGE, "rows %d outside 1..%d", rows, ctx->max_rows);
+    if (!(eps > 0)) return fail(ctx, DIT_EINVAL, "eps must be positive");
+    DIT_TRY(check_ctx(ctx));
+    DIT_LAUNCH(ctx, launch_modnorm_i8(x, rows, ctx->arch.hidden, shift, scale, norm_w, rms, eps, q, s, ctx->stream),
+               "modulated norm int8");
+    return DIT_OK;
+}
+
+dit_status dit_linear_w8a8(dit_ctx *ctx, const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
+                           int M, int N, int K, float *out) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!a || !a_scale || !w || !w_scale || !out) return fail(ctx, DIT_EINVAL, "a, a_scale, w, w_scale or out is NULL");
+    if (M < 1 || M > ctx->max_rows) return fail(ctx, DIT_ERANGE, "M %d outside 1..%d", M, ctx->max_rows);
+    if (N < 256 || N % 256 || N > 65536) return fail(ctx, DIT_EINVAL, "N %d: must be a multiple of 256 in 256..65536", N);
+    const int Kmax = std::max(ctx->arch.hidden, ctx->arch.ffn);
+    if (K < 128 || K % 128 || K > Kmax) return fail(ctx, DIT_EINVAL, "K %d: must be a multiple of 128 in 128..%d", K, Kmax);
+    DIT_TRY(check_ctx(ctx));
+    // the kernel reads A in whole 256-row tiles: the rows go to the
+    // context's INT8 workspace, which has them
+    if (hipMemcpyAsync(ctx->aq, a, static_cast<size_t>(M) * K, hipMemcpyDeviceToDevice, ctx->stream) != hipSuccess)
+        return fail(ctx, DIT_EDEVICE, "copy of the INT8 rows failed");
+    GemmEpi e{};
+    e.kind = EPI_F32;
+    e.out = out;
+    e.ldo = N;
+    DIT_LAUNCH(ctx, launch_gemm_w8a8(ctx->aq, a_scale, w, w_scale, M, N, K, e, ctx->stream), "linear w8a8");
     return DIT_OK;
 }
 

@@ -29,6 +29,8 @@
 //    int8 weights are dequantised (code * scale, rounded to bf16) on the way
 //    into LDS, once per block.
 #include "common.h"
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace dit {
@@ -588,11 +590,22 @@ __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 }
 }  // namespace
 
-template <int EPI, bool KS>
+// I8: the W8A8 form.  A and W are INT8 rows; a 128-byte LDS row then holds
+// 128 codes of K instead of 64 bf16, a lane's 16-byte fragment feeds
+// v_mfma_i32_16x16x64_i8 where it fed v_mfma_f32_16x16x32_bf16 (A and W
+// fragments take K in the same order, so the dot products are those of the
+// rows), and the int32 sums are scaled by ep.a_scale[row] * ep.w_scale[col]
+// before the epilogue.  Everything else is the bf16 kernel's.
+template <int EPI, bool KS, bool I8 = false>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
           GemmEpi ep, const uint16_t *__restrict__ A2, const uint16_t *__restrict__ W2, int M2, GemmEpi ep2) {
+    static_assert(!(KS && I8), "the k-split form is bf16 only");
     constexpr int BM = PP_BM, BN = PP_BN;
+    constexpr uint32_t ESZ = I8 ? 1 : 2;          // bytes per element
+    constexpr int BKE = 128 / ESZ;                // elements per 128-byte k-tile row
+    using FragT = std::conditional_t<I8, i32x4, bf16x8>;
+    using AccT = std::conditional_t<I8, i32x4, f32x4>;
     __shared__ u32x4 lds[(P3_NA + P3_NW) * P3_BUF];   // 160 KB
     u32x4 *const Abuf = lds;
     u32x4 *const Wbuf = lds + P3_NA * P3_BUF;
@@ -627,7 +640,7 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     const int tile_m = first + (bid % (GM * ntn)) % gsz;
     const int tile_n = (bid % (GM * ntn)) / gsz;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
-    const int T = K / BK;
+    const int T = K / BKE;
 
     // Loads: a wave's instruction i (0..3) within a 128-row half writes the
     // half's LDS slots 8(4wg + i) .. +7: lane -> slot 8(4wg + i) + (lane>>3),
@@ -640,30 +653,32 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     // scalar offset.
     const int lrow = lane >> 3;
     const int cE = (lane & 7) ^ (lane >> 4), cO = cE ^ 4;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + static_cast<int64_t>(m0) * K);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(reinterpret_cast<const char *>(A) + static_cast<int64_t>(m0) * K * ESZ);
     // The weight rows of this tile.  Two-weight products: the SwiGLU columns
     // of EPI_QKV_SWIGLU read the second weight; with KS the k-tiles past
     // k_split read the second weight's rows (row length K - k_split).
     bool swi = false;
-    const uint16_t *Wt = W + static_cast<int64_t>(n0) * K;
+    const char *Wt = reinterpret_cast<const char *>(W) + static_cast<int64_t>(n0) * K * ESZ;
     if constexpr (EPI == EPI_QKV_SWIGLU) {
         swi = n0 >= ep.n_split;
-        if (swi) Wt = ep.w2 + static_cast<int64_t>(n0 - ep.n_split) * K;
+        if (swi) Wt = reinterpret_cast<const char *>(ep.w2) + static_cast<int64_t>(n0 - ep.n_split) * K * ESZ;
     }
-    const int K1 = KS ? ep.k_split : K, K2 = K - K1, T1 = K1 / BK;
-    if constexpr (KS) Wt = W + static_cast<int64_t>(n0) * K1;
+    const int K1 = KS ? ep.k_split : K, K2 = K - K1, T1 = K1 / BKE;
+    if constexpr (KS) Wt = reinterpret_cast<const char *>(W + static_cast<int64_t>(n0) * K1);
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wt);
-    const __amdgpu_buffer_rsrc_t rW2 = make_rsrc(KS ? ep.w2 + static_cast<int64_t>(n0) * K2 : Wt);
+    const __amdgpu_buffer_rsrc_t rW2 =
+        make_rsrc(KS ? reinterpret_cast<const char *>(ep.w2 + static_cast<int64_t>(n0) * K2) : Wt);
     const int ah = grp ^ 1;                        // the A and W halves this group loads
     // instruction i reads rows 8i (A) or 16i (W, de-interleaved) further
     // down than instruction 0
     const int wrow0 = 128 * ah + (wg < 2 ? 2 * (32 * wg + lrow) : 2 * (32 * wg - 64 + lrow) + 1);
-    const uint32_t a_offE = 2u * static_cast<uint32_t>((128 * ah + 32 * wg + lrow) * K + cE * 8);
-    const uint32_t a_offO = 2u * static_cast<uint32_t>((128 * ah + 32 * wg + lrow) * K + cO * 8);
-    const uint32_t w_offE = 2u * static_cast<uint32_t>(wrow0 * K1 + cE * 8);
-    const uint32_t w_offO = 2u * static_cast<uint32_t>(wrow0 * K1 + cO * 8);
-    const uint32_t w2_offE = 2u * static_cast<uint32_t>(wrow0 * K2 + cE * 8);
-    const uint32_t w2_offO = 2u * static_cast<uint32_t>(wrow0 * K2 + cO * 8);
+    // byte offsets: a row is K * ESZ bytes, a 16-byte chunk c starts at 16c
+    const uint32_t a_offE = ESZ * static_cast<uint32_t>((128 * ah + 32 * wg + lrow) * K) + 16u * cE;
+    const uint32_t a_offO = ESZ * static_cast<uint32_t>((128 * ah + 32 * wg + lrow) * K) + 16u * cO;
+    const uint32_t w_offE = ESZ * static_cast<uint32_t>(wrow0 * K1) + 16u * cE;
+    const uint32_t w_offO = ESZ * static_cast<uint32_t>(wrow0 * K1) + 16u * cO;
+    const uint32_t w2_offE = ESZ * static_cast<uint32_t>(wrow0 * K2) + 16u * cE;
+    const uint32_t w2_offO = ESZ * static_cast<uint32_t>(wrow0 * K2) + 16u * cO;
     // load i (0..3) of the W half or the A half this group loads (half
     // grp ^ 1 of both), of k-tile kt.  Past the last k-tile the source is
     // clamped to it: those loads land in a buffer nobody reads any more, and
@@ -672,13 +687,13 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
         const int ks = min(kt, T - 1);
         u32x4 *dst = Wbuf + (kt & 1) * P3_BUF + (128 * ah + 8 * (4 * wg + i)) * 8;
         if (KS && ks >= T1)
-            bdma16(rW2, (i & 1) ? w2_offO : w2_offE, 2u * static_cast<uint32_t>((ks - T1) * BK + i * 16 * K2), dst);
+            bdma16(rW2, (i & 1) ? w2_offO : w2_offE, 128u * (ks - T1) + ESZ * static_cast<uint32_t>(i * 16 * K2), dst);
         else
-            bdma16(rW, (i & 1) ? w_offO : w_offE, 2u * static_cast<uint32_t>(ks * BK + i * 16 * K1), dst);
+            bdma16(rW, (i & 1) ? w_offO : w_offE, 128u * ks + ESZ * static_cast<uint32_t>(i * 16 * K1), dst);
     };
     auto issue_a = [&](int kt, int i) {
         const int ks = min(kt, T - 1);
-        bdma16(rA, (i & 1) ? a_offO : a_offE, 2u * static_cast<uint32_t>(ks * BK + i * 8 * K),
+        bdma16(rA, (i & 1) ? a_offO : a_offE, 128u * ks + ESZ * static_cast<uint32_t>(i * 8 * K),
                Abuf + (kt % 3) * P3_BUF + (128 * ah + 8 * (4 * wg + i)) * 8);
     };
 
@@ -689,15 +704,15 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     const int offA0 = (wm * WM + l16) * 8 + c0, offA1 = offA0 ^ 4;
     const int offB0 = (128 * wn + l16) * 8 + c0, offB1 = offB0 ^ 4;
 
-    bf16x8 af[2][TM], bfr[2][TN];
+    FragT af[2][TM], bfr[2][TN];
     auto frag = [&](const u32x4 *La, const u32x4 *Lw, int f) {   // fragment read f of 24
         if (f < 2 * TM) {
             const int ks = f & 1, tm = f >> 1;
-            af[ks][tm] = __builtin_bit_cast(bf16x8, La[(ks ? offA1 : offA0) + tm * 128]);
+            af[ks][tm] = __builtin_bit_cast(FragT, La[(ks ? offA1 : offA0) + tm * 128]);
         } else {
             const int ks = (f - 2 * TM) & 1, tn = (f - 2 * TM) >> 1;
             const int o = ((tn < TN / 2 ? 0 : 64) + (tn % (TN / 2)) * 16) * 8;
-            bfr[ks][tn] = __builtin_bit_cast(bf16x8, Lw[(ks ? offB1 : offB0) + o]);
+            bfr[ks][tn] = __builtin_bit_cast(FragT, Lw[(ks ? offB1 : offB0) + o]);
         }
     };
     // fragments of k-tile kt only (prologue)
@@ -721,19 +736,23 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
         }
     };
 
-    f32x4 acc[TM][TN];
+    AccT acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j) acc[i][j] = AccT{0, 0, 0, 0};
     auto compute = [&]() {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
+                for (int tn = 0; tn < TN; ++tn) {
+                    if constexpr (I8)
+                        acc[tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
+                    else
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][tm], bfr[ks][tn], acc[tm][tn], 0, 0, 0);
+                }
     };
 
     // prologue: k-tiles 0 and 1 whole, and A rows 128-255 of k-tile 2 (group
@@ -793,7 +812,27 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     wait_vm0();   // no load into LDS may be in flight when the block ends
     pp_barrier();
 
-    if constexpr (EPI == EPI_QKV_SWIGLU) {
+    if constexpr (I8) {
+        // acc[tm][tn][r] is the int32 sum of row m0 + wm*64 + tm*16 +
+        // 4*(lane>>4) + r and column 2P (tn < TN/2) or 2P + 1 (tn >= TN/2),
+        // P = (n0 + wn*128)/2 + (tn % (TN/2))*16 + (lane & 15)
+        f32x4 accf[TM][TN];
+        float sw[TN];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+            sw[tn] = ep.w_scale[n0 + 128 * wn + 2 * ((tn % (TN / 2)) * 16 + l16) + (tn >= TN / 2 ? 1 : 0)];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm * WM + tm * 16 + 4 * (lane >> 4) + r;
+                const float sa = row < M ? ep.a_scale[row] : 0.f;
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) accf[tm][tn][r] = static_cast<float>(acc[tm][tn][r]) * sa * sw[tn];
+            }
+        }
+        pp_epilogue<EPI>(accf, lds, m0, n0, wm, wn, lane, tid, M, N, ep);
+    } else if constexpr (EPI == EPI_QKV_SWIGLU) {
         if (swi) pp_epilogue<EPI_SWIGLU>(acc, lds, m0, n0 - ep.n_split, wm, wn, lane, tid, M, N - ep.n_split, ep);
         else pp_epilogue<EPI_QKV>(acc, lds, m0, n0, wm, wn, lane, tid, M, ep.n_split, ep);
     } else {
@@ -825,11 +864,11 @@ static hipError_t launch_cfg(const uint16_t *A, const void *W, const uint16_t *W
     return hipGetLastError();
 }
 
-template <int EPI, bool KS = false>
+template <int EPI, bool KS = false, bool I8 = false>
 static hipError_t launch_pp(const uint16_t *A, const uint16_t *W, int M, int N, int K, const GemmEpi &ep,
                             hipStream_t st) {
     const int grid = static_cast<int>(cdiv(M, PP_BM) * cdiv(N, PP_BN));
-    k_gemm_p3<EPI, KS><<<grid, 512, 0, st>>>(A, W, M, N, K, ep, nullptr, nullptr, 0, ep);
+    k_gemm_p3<EPI, KS, I8><<<grid, 512, 0, st>>>(A, W, M, N, K, ep, nullptr, nullptr, 0, ep);
     return hipGetLastError();
 }
 
@@ -886,6 +925,24 @@ hipError_t launch_gemm2(const uint16_t *A, const void *W, const uint16_t *Ws, in
         case EPI_GATE_RES: return launch_pp2<EPI_GATE_RES>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
         case EPI_SWIGLU: return launch_pp2<EPI_SWIGLU>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
         case EPI_QKV: return launch_pp2<EPI_QKV>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemm_w8a8(const int8_t *A, const float *a_scale, const int8_t *W, const float *w_scale, int M,
+                            int N, int K, const GemmEpi &ep_in, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    if (N % PP_BN || K % 128 || K < 128 || !a_scale || !w_scale) return hipErrorInvalidValue;
+    GemmEpi ep = ep_in;
+    ep.a_scale = a_scale;
+    ep.w_scale = w_scale;
+    const auto *a = reinterpret_cast<const uint16_t *>(A);
+    const auto *w = reinterpret_cast<const uint16_t *>(W);
+    switch (ep.kind) {
+        case EPI_F32: return launch_pp<EPI_F32, false, true>(a, w, M, N, K, ep, st);
+        case EPI_GATE_RES: return launch_pp<EPI_GATE_RES, false, true>(a, w, M, N, K, ep, st);
+        case EPI_SWIGLU: return launch_pp<EPI_SWIGLU, false, true>(a, w, M, N, K, ep, st);
+        case EPI_QKV: return launch_pp<EPI_QKV, false, true>(a, w, M, N, K, ep, st);
         default: return hipErrorInvalidValue;
     }
 }

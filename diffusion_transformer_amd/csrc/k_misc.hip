@@ -300,6 +300,134 @@ hipError_t launch_post_norm_gate(const float *y, int rows, int D, const float *w
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ INT8 rows
+// Symmetric INT8 codes of a row over one scale (W8A8 products' inputs):
+// inv = 127 / amax and q = rint(v * inv) clamped to +-127, s = amax / 127,
+// each a correctly rounded fp32 operation (the division is IEEE-exact by
+// default in HIP); an all-zero row gets s = 0 and q = 0.
+__device__ __forceinline__ float block_max(float v, float *red) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wv] = v;
+    __syncthreads();
+    float t = red[0];
+#pragma unroll
+    for (int i = 1; i < kNormThreads / 64; ++i) t = fmaxf(t, red[i]);
+    return t;
+}
+
+__device__ __forceinline__ uint32_t q8x4(float a, float b, float c, float d, float inv) {
+    auto q = [inv](float v) -> uint32_t {
+        const float r = fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
+        return static_cast<uint32_t>(static_cast<int>(r)) & 0xffu;
+    };
+    return q(a) | (q(b) << 8) | (q(c) << 16) | (q(d) << 24);
+}
+
+// The modulated norm of k_modnorm with its row taken to INT8 codes (out)
+// and one fp32 scale (s[r]) in the same pass.
+__global__ void __launch_bounds__(kNormThreads)
+k_modnorm_i8(const float *__restrict__ x, int D, const float *__restrict__ shift,
+             const float *__restrict__ scale, const float *__restrict__ nw, int rms, float eps,
+             int8_t *__restrict__ out, float *__restrict__ s_out) {
+    __shared__ float red[kNormThreads / 64];
+    const int64_t r = blockIdx.x;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + r * D);
+    const int n4 = D / 4;
+    float4 v[4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        v[i] = c < n4 ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float invD = 1.0f / static_cast<float>(D);
+    float mu = 0.f;
+    if (!rms) mu = block_sum(s, red) * invD;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        if (c < n4) {
+            float a = v[i].x - mu, b = v[i].y - mu, cc = v[i].z - mu, d = v[i].w - mu;
+            q += (a * a + b * b) + (cc * cc + d * d);
+        }
+    }
+    const float rstd = rsqrtf(block_sum(q, red) * invD + eps);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        if (c >= n4) continue;
+        float4 sh = reinterpret_cast<const float4 *>(shift)[c];
+        float4 sc = reinterpret_cast<const float4 *>(scale)[c];
+        float4 w = rms ? reinterpret_cast<const float4 *>(nw)[c] : make_float4(1.f, 1.f, 1.f, 1.f);
+        v[i].x = (v[i].x - mu) * rstd * w.x * (1.f + sc.x) + sh.x;
+        v[i].y = (v[i].y - mu) * rstd * w.y * (1.f + sc.y) + sh.y;
+        v[i].z = (v[i].z - mu) * rstd * w.z * (1.f + sc.z) + sh.z;
+        v[i].w = (v[i].w - mu) * rstd * w.w * (1.f + sc.w) + sh.w;
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    }
+    amax = block_max(amax, red);
+    const float inv = amax > 0.f ? 127.f / amax : 0.f;
+    uint32_t *orow = reinterpret_cast<uint32_t *>(out + r * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = threadIdx.x + i * kNormThreads;
+        if (c < n4) orow[c] = q8x4(v[i].x, v[i].y, v[i].z, v[i].w, inv);
+    }
+    if (threadIdx.x == 0) s_out[r] = amax / 127.f;
+}
+
+// bf16 rows [rows, K] to INT8 codes and a scale a row; K % 8 == 0, K <= 16384.
+__global__ void __launch_bounds__(kNormThreads)
+k_quant_rows(const uint16_t *__restrict__ x, int K, int8_t *__restrict__ out, float *__restrict__ s_out) {
+    __shared__ float red[kNormThreads / 64];
+    const int64_t r = blockIdx.x;
+    const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + r * K);
+    const int n8 = K / 8;
+    u32x4 v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = threadIdx.x + i * kNormThreads;
+        v[i] = c < n8 ? xr[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16lo_to_f32(v[i][j])), fabsf(bf16hi_to_f32(v[i][j]))));
+    }
+    amax = block_max(amax, red);
+    const float inv = amax > 0.f ? 127.f / amax : 0.f;
+    u32x2 *orow = reinterpret_cast<u32x2 *>(out + r * K);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = threadIdx.x + i * kNormThreads;
+        if (c >= n8) continue;
+        const u32x4 w = v[i];
+        orow[c] = u32x2{q8x4(bf16lo_to_f32(w[0]), bf16hi_to_f32(w[0]), bf16lo_to_f32(w[1]), bf16hi_to_f32(w[1]), inv),
+                        q8x4(bf16lo_to_f32(w[2]), bf16hi_to_f32(w[2]), bf16lo_to_f32(w[3]), bf16hi_to_f32(w[3]), inv)};
+    }
+    if (threadIdx.x == 0) s_out[r] = amax / 127.f;
+}
+
+hipError_t launch_modnorm_i8(const float *x, int rows, int D, const float *shift, const float *scale,
+                             const float *norm_w, bool rms, float eps, int8_t *out, float *s, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (D % 4 != 0 || D > 16 * kNormThreads) return hipErrorInvalidValue;
+    k_modnorm_i8<<<rows, kNormThreads, 0, st>>>(x, D, shift, scale, norm_w, rms ? 1 : 0, eps, out, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const uint16_t *x, int rows, int K, int8_t *out, float *s, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (K % 8 != 0 || K > 64 * kNormThreads) return hipErrorInvalidValue;
+    k_quant_rows<<<rows, kNormThreads, 0, st>>>(x, K, out, s);
+    return hipGetLastError();
+}
+
 hipError_t launch_modnorm(const float *x, int rows, int D, const float *shift, const float *scale,
                           const float *norm_w, bool rms, float eps, uint16_t *out, hipStream_t st) {
     if (rows <= 0) return hipSuccess;

@@ -25,6 +25,15 @@ hipError_t launch_gemv(const uint16_t *W, const float *x, int O, int I, bool sil
 
 // out[r] = bf16(norm(x[r]) * (1 + scale) + shift), r < rows; D <= 4096,
 // D a multiple of 4.  rms: RMSNorm times norm_w; else LayerNorm.
+// The modulated norm's rows as INT8 codes out [rows, D] and a scale a row
+// s [rows] (symmetric: s = amax / 127, q = rint(v * 127 / amax)).
+hipError_t launch_modnorm_i8(const float *x, int rows, int D, const float *shift, const float *scale,
+                             const float *norm_w, bool rms, float eps, int8_t *out, float *s, hipStream_t st);
+
+// bf16 rows x [rows, K] as INT8 codes and a scale a row (as above);
+// K % 8 == 0, K <= 16384.
+hipError_t launch_quant_rows(const uint16_t *x, int rows, int K, int8_t *out, float *s, hipStream_t st);
+
 // x[r] += gate * (norm(y[r]) * w) for r < rows: a sandwich block's norm of
 // a product's output rows before the gate ([GZ] POST_ATTN / POST_MLP); the
 // norm is LayerNorm (rms false) or RMSNorm, eps as given; y, x fp32 [rows, D]
@@ -65,6 +74,10 @@ struct GemmEpi {
     // cos and sin are passed already offset to row_base.
     int row_base;
     int rows_total;
+    // W8A8 products (launch_gemm_w8a8 sets them): fp32 scale per A row and
+    // per output column
+    const float *a_scale;
+    const float *w_scale;
 };
 
 // C = A[M,K] * W[N,K]^T, A bf16; W bf16 (w8 = false) or int8 with bf16
@@ -80,6 +93,12 @@ hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Wscale,
 hipError_t launch_gemm2(const uint16_t *A, const void *W, const uint16_t *Ws, int M, const GemmEpi &ep,
                         const uint16_t *A2, const void *W2, const uint16_t *Ws2, int M2, const GemmEpi &ep2,
                         bool w8, int N, int K, hipStream_t st);
+// W8A8: C = (A_q W_q^T) * a_scale[row] * w_scale[col], A_q int8 [M, K] (rows
+// allocated to a whole 256-row tile), W_q int8 [N, K]; N % 256 == 0,
+// K % 128 == 0; epilogues EPI_F32, EPI_GATE_RES, EPI_SWIGLU, EPI_QKV.
+hipError_t launch_gemm_w8a8(const int8_t *A, const float *a_scale, const int8_t *W, const float *w_scale, int M,
+                            int N, int K, const GemmEpi &ep, hipStream_t st);
+
 // Whether launch_gemm runs this product as the 256x256 ping-pong kernel (the
 // only one that takes EPI_QKV_SWIGLU and k_split > 0; asked before using them).
 bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &epi, bool a_rows_padded);

@@ -28,8 +28,8 @@ _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, ERANGE, ENOMEM, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 STAGES = ("mod", "norm1", "qkv", "attn", "out", "norm2", "up", "down", "time", "img_in", "final",
-          "euler", "txt_in", "par_in", "par_out", "post")
-W_BF16, W_INT8_B32 = 0, 1
+          "euler", "txt_in", "par_in", "par_out", "post", "quant")
+W_BF16, W_INT8_B32, W_INT8_ROW = 0, 1, 2
 NORM_LAYER, NORM_RMS = 0, 1
 _NAMES = {0: "DIT_OK", -1: "DIT_EINVAL", -2: "DIT_ERANGE", -3: "DIT_ENOMEM", -4: "DIT_EDEVICE",
           -5: "DIT_EUNSUPPORTED"}
@@ -73,6 +73,9 @@ _SIGS = {
     "dit_modulation": (C.c_int, [_P, _P, C.c_int, _P, _P]),
     "dit_modulated_norm": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_float, _P]),
     "dit_linear": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, _P]),
+    "dit_quantize_rows": (C.c_int, [_P, _P, C.c_int, C.c_int, _P, _P]),
+    "dit_modulated_norm_int8": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_float, _P, _P]),
+    "dit_linear_w8a8": (C.c_int, [_P, _P, _P, _P, _P, C.c_int, C.c_int, C.c_int, _P]),
     "dit_attention": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, _P]),
     "dit_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_parallel_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
@@ -209,6 +212,21 @@ class Context:
                    _ptr(scale, torch.bfloat16, "scale"), wtype, M, N, K,
                    _ptr(out, torch.float32, "out"))
 
+    def quantize_rows(self, x, rows, K, q, s):
+        self._call("dit_quantize_rows", _ptr(x, torch.bfloat16, "x"), rows, K, _ptr(q, torch.int8, "q"),
+                   _ptr(s, torch.float32, "s"))
+
+    def modulated_norm_int8(self, x, rows, shift, scale, norm_w, eps, q, s):
+        self._call("dit_modulated_norm_int8", _ptr(x, torch.float32, "x"), rows,
+                   _ptr(shift, torch.float32, "shift"), _ptr(scale, torch.float32, "scale"),
+                   _ptr(norm_w, torch.float32, "norm_w"), float(eps), _ptr(q, torch.int8, "q"),
+                   _ptr(s, torch.float32, "s"))
+
+    def linear_w8a8(self, a, a_scale, w, w_scale, M, N, K, out):
+        self._call("dit_linear_w8a8", _ptr(a, torch.int8, "a"), _ptr(a_scale, torch.float32, "a_scale"),
+                   _ptr(w, torch.int8, "w"), _ptr(w_scale, torch.float32, "w_scale"), M, N, K,
+                   _ptr(out, torch.float32, "out"))
+
     def attention(self, q, k, vt, heads, S, o):
         self._call("dit_attention", _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"),
                    _ptr(vt, torch.bfloat16, "vt"), heads, S, _ptr(o, torch.bfloat16, "o"))
@@ -296,10 +314,14 @@ class BlockWeights:
     def __init__(self, tensors: dict, int8: bool = False):
         self.t = tensors
         self.int8 = int8
+        w8a8 = "q8_w_qkv" in tensors
         b = Block()
-        b.wtype = W_INT8_B32 if int8 else W_BF16
+        b.wtype = W_INT8_ROW if w8a8 else W_INT8_B32 if int8 else W_BF16
         for i, n in enumerate(self.LIN):
-            if int8:
+            if w8a8:
+                b.w[i] = _ptr(tensors["q8_" + n], torch.int8, "q8_" + n)
+                b.scale[i] = _ptr(tensors["s8_" + n], torch.float32, "s8_" + n)
+            elif int8:
                 b.w[i] = _ptr(tensors["q_" + n], torch.int8, "q_" + n)
                 b.scale[i] = _ptr(tensors["s_" + n], torch.bfloat16, "s_" + n)
             else:
@@ -318,9 +340,9 @@ class BlockWeights:
         t = {}
         int8 = "q_w_qkv" in bw
         for k, v in bw.items():
-            if k.startswith("q_w"):
+            if k.startswith("q_w") or k.startswith("q8_w"):
                 t[k] = torch.from_numpy(v).to(device)
-            elif k in ("q_norm", "k_norm", "norm1", "norm2", "post_attn", "post_mlp"):
+            elif k in ("q_norm", "k_norm", "norm1", "norm2", "post_attn", "post_mlp") or k.startswith("s8_w"):
                 t[k] = dev_f32(v, device)
             else:
                 t[k] = dev_bf16(v, device)

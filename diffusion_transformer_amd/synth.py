@@ -66,6 +66,7 @@ class Shape:
     seed: int
     int8: bool = False
     blocks: int = 1
+    w8a8: bool = False
     latent: int = 64
     text_dim: int = 4096
     time_dim: int = 256
@@ -85,6 +86,7 @@ SHAPES = {
     "s1088": Shape("s1088", 3072, 24, 128, 12288, 64, 32, 32, seed=2),
     "s4608": Shape("s4608", 3072, 24, 128, 12288, 512, 64, 64, seed=3),
     "s4608_int8": Shape("s4608_int8", 3072, 24, 128, 12288, 512, 64, 64, seed=4, int8=True),
+    "s4608_w8a8": Shape("s4608_w8a8", 3072, 24, 128, 12288, 512, 64, 64, seed=6, w8a8=True),
     "dit32": Shape("dit32", 3072, 24, 128, 12288, 512, 64, 64, seed=5, blocks=32),
 }
 
@@ -134,19 +136,32 @@ def int8_weight(rng, out: int, inn: int):
     return q, s
 
 
-def block_weights(rng, sh: Shape, std=0.02, norm_std=0.0, int8=None, rms=False, sandwich=False):
+def w8a8_weight(rng, out: int, inn: int, std=0.02):
+    """INT8 rows q ~ U{-127..127} [out, in] and one fp32 scale a row [out],
+    std * sqrt(3) / 127 * (1 + N(0, 0.1^2)), so the weights' spread is about
+    std."""
+    q = rng.integers(-127, 128, (out, inn), dtype=np.int8)
+    s = (np.float32(std * np.sqrt(3.0) / 127.0) * (1.0 + 0.1 * rng.standard_normal(out, dtype=np.float32)))
+    return q, s.astype(np.float32)
+
+
+def block_weights(rng, sh: Shape, std=0.02, norm_std=0.0, int8=None, rms=False, sandwich=False, w8a8=None):
     """Weights of one block as a dict of float32 arrays (bf16 values).
     Keys: w_qkv [3D, D], w_out [D, D], w_up [2F, D], w_down [D, F],
     w_mod [6D, D], q_norm [hd], k_norm [hd] and, with rms=True, norm1/norm2
     [D].  With int8, the four linears are replaced by (codes, scales) pairs
-    under keys q_<name> and s_<name>.  With sandwich=True, the post norms'
+    under keys q_<name> and s_<name>; with w8a8, by INT8 rows and fp32 row
+    scales (w8a8_weight) under q8_<name> and s8_<name>.  With sandwich=True, the post norms'
     weights post_attn/post_mlp [D] ~ N(1, 0.2^2), drawn last."""
     D, F, hd = sh.hidden, sh.ffn, sh.head_dim
     int8 = sh.int8 if int8 is None else int8
+    w8a8 = sh.w8a8 if w8a8 is None else w8a8
     dims = {"w_qkv": (3 * D, D), "w_out": (D, D), "w_up": (2 * F, D), "w_down": (D, F)}
     out = {}
     for k, (o, i) in dims.items():
-        if int8:
+        if w8a8:
+            out["q8_" + k], out["s8_" + k] = w8a8_weight(rng, o, i, std)
+        elif int8:
             out["q_" + k], out["s_" + k] = int8_weight(rng, o, i)
         else:
             out[k] = _normal(rng, (o, i), std)
@@ -168,7 +183,7 @@ def block_weights(rng, sh: Shape, std=0.02, norm_std=0.0, int8=None, rms=False, 
     return out
 
 
-def block_case(name: str = "tiny", seed=None, norm_std=0.0, rms=False, t=None, sandwich=False):
+def block_case(name: str = "tiny", seed=None, norm_std=0.0, rms=False, t=None, sandwich=False, w8a8=None):
     """Inputs of one block forward: rows x [S, D] ~ N(0,1) (float32, fp32 on
     the GPU too), the time t (0.5 for `tiny`, else U(0,1)), the time MLP
     weights w_t1 [D, 256] and w_t2 [D, D], and the block's weights."""
@@ -179,7 +194,7 @@ def block_case(name: str = "tiny", seed=None, norm_std=0.0, rms=False, t=None, s
         t = 0.5 if name == "tiny" else float(rng.uniform(0.0, 1.0))
     w_t1 = _normal(rng, (sh.hidden, sh.time_dim), 0.02)
     w_t2 = _normal(rng, (sh.hidden, sh.hidden), 0.02)
-    bw = block_weights(rng, sh, norm_std=norm_std, rms=rms, sandwich=sandwich)
+    bw = block_weights(rng, sh, norm_std=norm_std, rms=rms, sandwich=sandwich, w8a8=w8a8)
     return dict(shape=sh, x=x, t=np.float32(t), w_t1=w_t1, w_t2=w_t2, block=bw)
 
 

@@ -52,7 +52,7 @@ typedef enum {
 
 /* Weight storage of the four block linears ([HC] s.1: bf16, or int8 with
  * one bf16 scale per block of 32 along the input axis). */
-typedef enum { DIT_W_BF16 = 0, DIT_W_INT8_B32 = 1 } dit_wtype;
+typedef enum { DIT_W_BF16 = 0, DIT_W_INT8_B32 = 1, DIT_W_INT8_ROW = 2 } dit_wtype;
 
 /* Norm before attention and MLP: LayerNorm without affine, or RMSNorm times
  * a per-feature weight ([GZ] normedInto; Block.parallel's modulated LayerNorm). */
@@ -87,6 +87,12 @@ typedef struct {
  * wtype DIT_W_BF16: w[i] are bf16; scale[i] must be NULL.
  * wtype DIT_W_INT8_B32: w[i] are int8 [out, in]; scale[i] are bf16
  *   [out, in/32]; weight = code * scale[o][k/32].
+ * wtype DIT_W_INT8_ROW (W8A8; [GZ] linear, quantizedOf): w[i] are int8
+ *   [out, in], scale[i] fp32 [out]; weight = code * scale[o].  Each
+ *   product's input rows are taken to INT8 with one scale a row
+ *   (s = max|row| / 127, codes rint(v * 127 / max|row|)), fused into the
+ *   modulated norm for QKV and UP; the int32 sums times both scales.  Only
+ *   the sequential forms take it.
  * norm_w: fp32.  [0] NORM1, [1] NORM2 ([D], required for DIT_NORM_RMS,
  *   ignored for DIT_NORM_LAYER), [2] Q_NORM, [3] K_NORM ([hd], required).
  * w_mod: bf16 [6D, D]; its output rows are shift, scale, gate of the
@@ -100,7 +106,7 @@ typedef struct {
 typedef struct {
     int32_t wtype;
     const void *w[4];
-    const uint16_t *scale[4];
+    const void *scale[4];
     const float *norm_w[4];
     const uint16_t *w_mod;
     const float *post_w[2];
@@ -181,6 +187,27 @@ dit_status dit_modulated_norm(dit_ctx *ctx, const float *x, int rows, const floa
  * N a multiple of 64, 1 <= M <= max_rows. */
 dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint16_t *scale,
                       int wtype, int M, int N, int K, float *out);
+
+/* INT8 rows ([GZ] quantizedOf; [K4] Appendix B D4 per-token quantization):
+ * x bf16 [rows, K] -> q int8 [rows, K] and s fp32 [rows] with, per row,
+ * amax = max|x|, s = amax / 127 and q = clamp(rint(x * (127 / amax)),
+ * -127, 127), each step one correctly rounded fp32 operation (an all-zero
+ * row: s = 0, q = 0).  K a multiple of 8, at most 16384. */
+dit_status dit_quantize_rows(dit_ctx *ctx, const uint16_t *x, int rows, int K, int8_t *q, float *s);
+
+/* dit_modulated_norm with its output rows as INT8 codes q [rows, D] and a
+ * scale a row s [rows], quantized as dit_quantize_rows quantizes (from the
+ * fp32 norm output, in the same pass: [GZ] normedInto, INT8 rows). */
+dit_status dit_modulated_norm_int8(dit_ctx *ctx, const float *x, int rows, const float *shift,
+                                   const float *scale, const float *norm_w, float eps, int8_t *q, float *s);
+
+/* W8A8 product ([GZ] linear): out[m][n] = (sum_k a[m][k] w[n][k]) *
+ * a_scale[m] * w_scale[n] in fp32, int32 sums on the INT8 matrix cores.
+ * a int8 [M, K], a_scale fp32 [M], w int8 [N, K], w_scale fp32 [N], out
+ * fp32 [M, N]; 1 <= M <= max_rows, N a multiple of 256, K a multiple of
+ * 128 up to max(hidden, ffn). */
+dit_status dit_linear_w8a8(dit_ctx *ctx, const int8_t *a, const float *a_scale, const int8_t *w,
+                           const float *w_scale, int M, int N, int K, float *out);
 
 /* Joint attention ([K4] s.4.3): for each head h, o[:, h*128:(h+1)*128] =
  * bf16(softmax(q_h k_h^T / sqrt(128)) v_h), no mask.  q, k bf16
@@ -294,7 +321,8 @@ typedef enum {
     DIT_ST_PAR_IN = 13, /* parallel block: [QKV | UP] product, both epilogues */
     DIT_ST_PAR_OUT = 14,/* parallel block: [OUT | DOWN] product + gated residual */
     DIT_ST_POST = 15,   /* sandwich block: norm of a product's output, gate, residual */
-    DIT_NSTAGES = 16
+    DIT_ST_QUANT = 16,  /* W8A8 block: attention / SwiGLU rows to INT8 */
+    DIT_NSTAGES = 17
 } dit_stage;
 
 /* Per-stage timing, a measurement aid ([K4] s.3: every op of the busy time

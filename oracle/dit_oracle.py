@@ -220,6 +220,18 @@ def quantize_rows_int8(x):
     return q, (amax / F32(127)).astype(F32)
 
 
+class _RowSlicer:
+    """Row ranges of a weight, float or Int8Rows (its scales go along)."""
+
+    def __init__(self, w):
+        self.w = w
+
+    def __getitem__(self, sl):
+        if isinstance(self.w, Int8Rows):
+            return Int8Rows(q=np.asarray(self.w.q)[sl], s=np.asarray(self.w.s)[sl])
+        return np.asarray(self.w, F64)[sl]
+
+
 def linear_w8a8(x, w: Int8Rows) -> np.ndarray:
     """x W^T with x's rows quantized by quantize_rows_int8: the exact integer
     dot products (int64) times x's row scale and W's row scale, in float64."""
@@ -414,7 +426,7 @@ def block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, rows):
     m = modulation(vec, bw.w_mod, 6)
     shift_a, scale_a, gate_a, shift_m, scale_m, gate_m = m
     h = modulated_norm(x, shift_a, scale_a, arch, bw.norm1)
-    wq = np.asarray(bw.w_qkv, F64)
+    wq = _RowSlicer(bw.w_qkv)
     q = heads_of(linear(h[rows], wq[0:H * d]), H, d)
     k = heads_of(linear(h, wq[H * d:2 * H * d]), H, d)
     v = heads_of(linear(h, wq[2 * H * d:]), H, d)
@@ -484,7 +496,7 @@ def block_forward_runs_rows(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arc
     _, per_row = _modulation_per_row(vecs, bw.w_mod, runs, S)
     shift_a, scale_a, gate_a, shift_m, scale_m, gate_m = per_row
     h = modulated_norm(x, shift_a, scale_a, arch, bw.norm1)
-    wq = np.asarray(bw.w_qkv, F64)
+    wq = _RowSlicer(bw.w_qkv)
     q = heads_of(linear(h[rows], wq[0:H * d]), H, d)
     k = heads_of(linear(h, wq[H * d:2 * H * d]), H, d)
     v = heads_of(linear(h, wq[2 * H * d:]), H, d)
@@ -536,7 +548,7 @@ def parallel_block_forward_rows(x, bw: BlockWeights, vec, cos, sin, arch: Arch, 
     H, d = arch.heads, arch.head_dim
     shift, scale, gate = modulation(vec, bw.w_mod, 3)
     h = modulated_norm(x, shift, scale, arch, bw.norm1)
-    wq = np.asarray(bw.w_qkv, F64)
+    wq = _RowSlicer(bw.w_qkv)
     q = heads_of(linear(h[rows], wq[0:H * d]), H, d)
     k = heads_of(linear(h, wq[H * d:2 * H * d]), H, d)
     v = heads_of(linear(h, wq[2 * H * d:]), H, d)

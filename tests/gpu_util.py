@@ -69,6 +69,8 @@ def oracle_block(bw: dict) -> "O.BlockWeights":
     def lin(n):
         if "q_" + n in bw:
             return O.dequant_int8_b32(bw["q_" + n], bw["s_" + n])
+        if "q8_" + n in bw:
+            return O.Int8Rows(q=bw["q8_" + n], s=bw["s8_" + n])
         return bw[n]
     return O.BlockWeights(w_qkv=lin("w_qkv"), w_out=lin("w_out"), w_up=lin("w_up"),
                           w_down=lin("w_down"), w_mod=bw["w_mod"], q_norm=bw["q_norm"],

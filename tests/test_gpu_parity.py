@@ -636,6 +636,163 @@ def test_sandwich_weights_rejected_where_not_taken(ctx_tiny):
     torch.cuda.synchronize()
     assert (np_of(x) == case["x"]).all()
 
+
+# --------------------------------------------------------------- W8A8
+
+def _bf16_rows(rows, K, seed):
+    # rows at spreads from 1e-3 to 1e3, a zero row and a row of one value
+    x = synth.normal((rows, K), seed=seed) * np.float32(10.0) ** np.linspace(-3, 3, rows, dtype=np.float32)[:, None]
+    x[1] = 0.0
+    x[2] = 0.75
+    return synth.bf16_round(x)
+
+
+@pytest.mark.parametrize("rows,K", [(5, 8), (72, 256), (300, 3072), (4608, 12288), (3, 16384)])
+def test_quantize_rows_bit_exact(ctx_tiny, rows, K):
+    x = _bf16_rows(rows, K, seed=rows + K)
+    q = torch.empty((rows, K), dtype=torch.int8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    say("quantize rows", rows, K)
+    ctx_tiny.quantize_rows(L.dev_bf16(x), rows, K, q, s)
+    torch.cuda.synchronize()
+    qr, sr = O.quantize_rows_int8(x)
+    assert (np_of(s) == sr).all()
+    assert (np_of(q) == qr).all()
+
+
+@pytest.mark.parametrize("norm", ["layer", "rms"])
+@pytest.mark.parametrize("rows", [72, 4608])
+def test_modulated_norm_int8(norm, rows):
+    # the codes are taken from the fp32 norm output, which the oracle holds
+    # in float64: the integer decisions agree except where the two values
+    # straddle a rounding boundary, and there by one step
+    D = 3072
+    sh = synth.Shape("n", D, D // 128, 128, 1024, 0, 1, rows, seed=0)
+    la, oa = arch_pair(sh, norm)
+    ctx = L.Context(la, max_rows=rows)
+    x = synth.normal((rows, D), seed=rows + 7, std=2.0, mean=0.5)
+    shift = synth.normal((D,), seed=1, std=0.3)
+    scale = synth.normal((D,), seed=2, std=0.3)
+    nw = synth.normal((D,), seed=3, std=0.1, mean=1.0)
+    q = torch.empty((rows, D), dtype=torch.int8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    say("modulated norm int8", norm, rows)
+    ctx.modulated_norm_int8(L.dev_f32(x), rows, L.dev_f32(shift), L.dev_f32(scale), L.dev_f32(nw), 1e-6, q, s)
+    torch.cuda.synchronize()
+    ref = O.modulated_norm(x, shift, scale, oa, nw)
+    qr, sr = O.quantize_rows_int8(ref)
+    d = np_of(q).astype(int) - qr.astype(int)
+    say(f"codes off by one: {np.count_nonzero(d)} of {d.size}")
+    assert np.abs(d).max() <= 1 and np.count_nonzero(d) <= d.size * 1e-3
+    assert np.allclose(np_of(s), sr, rtol=1e-5, atol=0)
+    ctx.close()
+
+
+@pytest.mark.parametrize("M,N,K", [(72, 256, 128), (300, 768, 256), (4608, 3072, 3072), (4608, 24576, 3072),
+                                   (4608, 3072, 12288), (1, 256, 12288)])
+def test_linear_w8a8(ctx_big, M, N, K):
+    # exact int32 sums times two fp32 scales: three fp32 roundings
+    rng = np.random.default_rng(M + N + K)
+    a = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    sa = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    say("linear w8a8", M, N, K)
+    ctx_big.linear_w8a8(torch.from_numpy(a).cuda(), L.dev_f32(sa), torch.from_numpy(w).cuda(), L.dev_f32(sw),
+                        M, N, K, out)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if M <= 300 else synth.rows_sample(M, 48)
+    # int8 products summed over K <= 12288 stay below 2^53: float64 is exact
+    ref = (a[rows].astype(np.float64) @ w.astype(np.float64).T) * sa[rows, None].astype(np.float64) * sw[None, :]
+    got = np_of(out)[rows].astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 3e-7 * np.abs(ref) + 1e-30)
+
+
+def _w8a8_gpu(ctx, case, runs=None):
+    sh = case["shape"]
+    seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    x = L.dev_f32(case["x"])
+    if runs is None:
+        ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    else:
+        ctx.block_forward_runs(bw, x, L.dev_f32(case["vecs"]), runs, seq.cos, seq.sin, sh.L, sh.N)
+    torch.cuda.synchronize()
+    return x
+
+
+@pytest.mark.parametrize("name,norm,norm_std,sandwich", [("tiny", "layer", 0.0, False), ("tiny", "rms", 0.1, False),
+                                                          ("tiny", "layer", 0.0, True), ("s1088", "layer", 0.0, False)])
+def test_w8a8_block_full_parity(name, norm, norm_std, sandwich):
+    case = synth.block_case(name, norm_std=norm_std, rms=(norm == "rms"), sandwich=sandwich, w8a8=True)
+    sh = case["shape"]
+    la, oa = arch_pair(sh, norm)
+    ctx = L.Context(la, max_rows=sh.S)
+    say("w8a8 block", name, norm, "sandwich" if sandwich else "", "S =", sh.S)
+    got = np_of(_w8a8_gpu(ctx, case))
+    D, F, H = sh.hidden, sh.ffn, sh.heads
+    S, Sp = sh.S, (sh.S + 63) // 64 * 64
+    cs, sn, vec = _oracle_inputs(case, oa)
+    y, ref = O.block_forward(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, keep=True)
+    compare(f"{name}/q", np_of(ctx.debug_copy(2, torch.bfloat16, (H, S, 128))), ref["q"], bf16_stored=True)
+    compare(f"{name}/k", np_of(ctx.debug_copy(3, torch.bfloat16, (H, S, 128))), ref["k"], bf16_stored=True)
+    v = np_of(ctx.debug_copy(4, torch.bfloat16, (H, 128, Sp)))[:, :, :S].transpose(0, 2, 1)
+    compare(f"{name}/v", v, ref["v"], bf16_stored=True)
+    compare(f"{name}/o", np_of(ctx.debug_copy(5, torch.bfloat16, (S, D))), ref["o"], bf16_stored=True)
+    compare(f"{name}/a", np_of(ctx.debug_copy(7, torch.bfloat16, (S, F))), ref["a"], bf16_stored=True)
+    compare(f"{name}/y", got, y)
+    compare(f"{name}/delta", got - case["x"], y - case["x"])
+    ctx.close()
+
+
+def test_w8a8_block_full_size_sampled_rows(ctx_big):
+    case = synth.block_case("s4608_w8a8")
+    sh = case["shape"]
+    _, oa = arch_pair(sh)
+    D, F = sh.hidden, sh.ffn
+    say("w8a8 block s4608")
+    got = np_of(_w8a8_gpu(ctx_big, case))
+    o_got = np_of(ctx_big.debug_copy(5, torch.bfloat16, (sh.S, D)))
+    a_got = np_of(ctx_big.debug_copy(7, torch.bfloat16, (sh.S, F)))
+    cs, sn, vec = _oracle_inputs(case, oa)
+    rows = synth.rows_sample(sh.S, 48, L=sh.L)
+    y, o, x1, a = O.block_forward_rows(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, rows)
+    compare("s4608_w8a8/o", o_got[rows], o, bf16_stored=True)
+    compare("s4608_w8a8/a", a_got[rows], a, bf16_stored=True)
+    compare("s4608_w8a8/y", got[rows], y)
+    compare("s4608_w8a8/delta", got[rows] - case["x"][rows], y - case["x"][rows])
+
+
+def test_w8a8_block_runs_parity(ctx_tiny):
+    case = synth.block_case("tiny", w8a8=True)
+    sh = case["shape"]
+    case["vecs"] = synth.normal((3, sh.hidden), seed=sh.seed + 200, std=0.13)
+    _, oa = arch_pair(sh)
+    runs = _runs_of("tiny", sh)
+    say("w8a8 block runs", runs)
+    got = np_of(_w8a8_gpu(ctx_tiny, case, runs))
+    cs, sn, _ = _oracle_inputs(case, oa)
+    y = O.block_forward_runs(case["x"], oracle_block(case["block"]), case["vecs"], runs, cs, sn, oa)
+    compare("tiny/y", got, y)
+    compare("tiny/delta", got - case["x"], y - case["x"])
+
+
+def test_w8a8_weights_rejected_where_not_taken(ctx_tiny):
+    case = synth.block_case("tiny", w8a8=True)
+    sh = case["shape"]
+    seq = GpuSeq(ctx_tiny, sh, case["t"], case["w_t1"], case["w_t2"])
+    x = L.dev_f32(case["x"])
+    bw = L.BlockWeights.from_host(case["block"])
+    with pytest.raises(L.DitError) as e:
+        ctx_tiny.double_block_forward(bw, bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    assert e.value.status == L.EINVAL
+    pb = dict(case["block"])
+    pb["w_mod"] = np.ascontiguousarray(pb["w_mod"][:3 * sh.hidden])
+    with pytest.raises(L.DitError) as e:
+        ctx_tiny.parallel_block_forward(L.BlockWeights.from_host(pb), x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    assert e.value.status == L.EINVAL
+
 # --------------------------------------------------------------- denoise
 
 def test_denoise_twin(ctx_tiny):

@@ -672,6 +672,11 @@ def test_w8a8_block_is_close_to_the_float_block():
     got = _oracle_block(Wq, pos, x, vecc, TINY)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref - x)
     assert 0 < rel < 2e-2
+    # the sampled-rows form slices the INT8 weights with their scales
+    c, s = O.rope_tables(pos, TINY.axes)
+    rows = np.array([0, 3, len(pos) - 1])
+    yr = O.block_forward_rows(x, O.BlockWeights(**Wq), vecc, c, s, TINY, rows)[0]
+    assert np.abs(yr - got[rows]).max() < 1e-12
 
 # ---------------------------------------------------------------- double-stream block
 
