@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -783,6 +784,26 @@ dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint
     e.out = out;
     e.ldo = N;
     DIT_LAUNCH(ctx, launch_gemm(a, w, scale, wtype == DIT_W_INT8_B32, M, N, K, e, ctx->stream, false), "linear");
+    return DIT_OK;
+}
+
+dit_status dit_sigma_schedule(const float *sample_sigmas, int n, float shift, float *sigmas, float *t) {
+#pragma clang fp contract(off)
+    if (!sample_sigmas || !sigmas || !t) return fail(nullptr, DIT_EINVAL, "sample_sigmas, sigmas or t is NULL");
+    if (n < 1 || n > 10000) return fail(nullptr, DIT_ERANGE, "n = %d outside 1..10000", n);
+    if (!(shift > 0.f) || !std::isfinite(shift)) return fail(nullptr, DIT_EINVAL, "shift must be positive and finite");
+    for (int i = 0; i < n; ++i) {
+        const float s0 = sample_sigmas[i];
+        if (!(s0 >= 0.f && s0 <= 1.f)) return fail(nullptr, DIT_EINVAL, "sigma %d = %g outside [0, 1]", i, s0);
+        // one float operation at a time, each rounded (no contraction)
+        const float num = shift * s0;
+        const float den = 1.f + (shift - 1.f) * s0;
+        const float s = num / den;
+        sigmas[i] = s;
+        const float ts = s * 1000.f;
+        t[i] = ts / 1000.f;
+    }
+    sigmas[n] = 0.f;
     return DIT_OK;
 }
 

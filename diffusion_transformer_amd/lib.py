@@ -74,6 +74,7 @@ _SIGS = {
     "dit_modulated_norm": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_float, _P]),
     "dit_linear": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, _P]),
     "dit_quantize_rows": (C.c_int, [_P, _P, C.c_int, C.c_int, _P, _P]),
+    "dit_sigma_schedule": (C.c_int, [_P, C.c_int, C.c_float, _P, _P]),
     "dit_modulated_norm_int8": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_float, _P, _P]),
     "dit_linear_w8a8": (C.c_int, [_P, _P, _P, _P, _P, C.c_int, C.c_int, C.c_int, _P]),
     "dit_attention": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, _P]),
@@ -115,6 +116,19 @@ def version() -> str:
 
 def last_error(ctx_ptr=None) -> str:
     return _lib.dit_last_error(ctx_ptr).decode()
+
+
+def sigma_schedule(sample_sigmas, shift: float = 1.0):
+    """The sampler's grid from dit_sigma_schedule: (sigmas [n + 1], t [n]) float32."""
+    g = np.ascontiguousarray(np.asarray(sample_sigmas, dtype=np.float32))
+    n = len(g)
+    sig = np.empty(n + 1, np.float32)
+    t = np.empty(n, np.float32)
+    st = _lib.dit_sigma_schedule(g.ctypes.data_as(C.c_void_p), n, float(shift), sig.ctypes.data_as(C.c_void_p),
+                                 t.ctypes.data_as(C.c_void_p))
+    if st != OK:
+        raise DitError(st, last_error(None))
+    return sig, t
 
 
 def make_arch(hidden=3072, heads=24, head_dim=128, ffn=12288, axes=(16, 56, 56), eps=1e-6,

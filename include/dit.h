@@ -188,6 +188,19 @@ dit_status dit_modulated_norm(dit_ctx *ctx, const float *x, int rows, const floa
 dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint16_t *scale,
                       int wtype, int M, int N, int K, float *out);
 
+/* The sampler's grid ([HC] s.6, FlowMatch Euler with a fixed grid), host
+ * memory, no context: for the n given sigmas s in [0, 1], sigmas[i] =
+ * shift*s / (1 + (shift - 1)*s) and the DiT time input t[i] = (sigmas[i] *
+ * 1000) / 1000, every step one rounded fp32 operation; sigmas[n] = 0 (the
+ * grid holds n + 1 values, t n).  Step i runs dit_denoise_step with
+ * sigma = sigmas[i] and sigma_next = sigmas[i+1]; that step's time input is
+ * sigma, which on an unshifted grid equals t[i] bit for bit ([HC] s.6
+ * states it for the 8-step grid); after a shift the two can differ in the
+ * last bit.  DIT_EINVAL for NULL pointers, a shift
+ * that is not positive and finite or a sigma outside [0, 1]; DIT_ERANGE
+ * for n outside 1..10000.  dit_last_error(NULL) holds the message. */
+dit_status dit_sigma_schedule(const float *sample_sigmas, int n, float shift, float *sigmas, float *t);
+
 /* INT8 rows ([GZ] quantizedOf; [K4] Appendix B D4 per-token quantization):
  * x bf16 [rows, K] -> q int8 [rows, K] and s fp32 [rows] with, per row,
  * amax = max|x|, s = amax / 127 and q = clamp(rint(x * (127 / amax)),

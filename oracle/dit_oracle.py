@@ -644,6 +644,19 @@ def sigma_grid(steps: int) -> np.ndarray:
     return np.linspace(1.0, 0.0, steps + 1).astype(F32)
 
 
+def sigma_schedule(sample_sigmas, shift: float = 1.0):
+    """The sampler's grid ([HC] s.6, FlowMatch Euler with a fixed grid): the
+    given sigmas in fp32, shifted as shift*s / (1 + (shift - 1)*s), the
+    timesteps s*1000 and the DiT time input t = timesteps/1000, every step a
+    float32 operation; the grid closed by a terminal 0.  Returns
+    (sigmas [n + 1], t [n]), float32."""
+    s = np.asarray(sample_sigmas, F32)
+    sh = F32(shift)
+    s = (sh * s) / (F32(1) + (sh - F32(1)) * s)
+    t = (s * F32(1000)) / F32(1000)
+    return np.append(s, F32(0)).astype(F32), t.astype(F32)
+
+
 # ---------------------------------------------------------------------------
 # The whole DiT ([HC] s.1 DiT graph: img_tokens, txt_feats, timestep -> vel)
 # ---------------------------------------------------------------------------

@@ -793,6 +793,24 @@ def test_w8a8_weights_rejected_where_not_taken(ctx_tiny):
         ctx_tiny.parallel_block_forward(L.BlockWeights.from_host(pb), x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
     assert e.value.status == L.EINVAL
 
+
+# --------------------------------------------------------------- sampler grid
+
+@pytest.mark.parametrize("shift", [1.0, 3.0, 0.37])
+def test_sigma_schedule_bit_exact(shift):
+    # host code of the library: every step one rounded fp32 operation, as
+    # the oracle's float32 NumPy steps
+    given = [1.0, 0.978453, 0.95418, 0.926626, 0.89508, 0.845148, 0.704534, 0.414568]
+    grid = np.concatenate([np.array(given, np.float32), np.linspace(0.9, 0.01, 37, dtype=np.float32)])
+    sig, t = L.sigma_schedule(grid, shift)
+    rs, rt = O.sigma_schedule(grid, shift)
+    assert (sig.view(np.uint32) == rs.view(np.uint32)).all()
+    assert (t.view(np.uint32) == rt.view(np.uint32)).all()
+    with pytest.raises(L.DitError):
+        L.sigma_schedule([1.0, 1.5], shift)
+    with pytest.raises(L.DitError):
+        L.sigma_schedule(grid, 0.0)
+
 # --------------------------------------------------------------- denoise
 
 def test_denoise_twin(ctx_tiny):

@@ -678,6 +678,31 @@ def test_w8a8_block_is_close_to_the_float_block():
     yr = O.block_forward_rows(x, O.BlockWeights(**Wq), vecc, c, s, TINY, rows)[0]
     assert np.abs(yr - got[rows]).max() < 1e-12
 
+
+# ---------------------------------------------------------------- sampler grid
+
+def test_sigma_schedule_golden_fixture():
+    g = _golden("sampler_sigmas_8step.txt")
+    given = np.array(g["sample_sigmas"], np.float32)
+    sig, t = O.sigma_schedule(given, float(g["shift"]))
+    assert len(t) == int(g["steps"]) and len(sig) == int(g["steps"]) + 1
+    # shift 1.0 leaves the grid unchanged bit for bit, closed by 0; t equals
+    # sigma bit for bit at every step
+    assert (sig[:-1].view(np.uint32) == given.view(np.uint32)).all() and sig[-1] == 0
+    assert (t.view(np.uint32) == sig[:-1].view(np.uint32)).all()
+
+
+def test_sigma_schedule_shift_closed_forms():
+    sig, t = O.sigma_schedule([1.0, 0.5, 0.25, 0.0], 3.0)
+    # 3s / (1 + 2s): 1 -> 1, 1/2 -> 3/4, 1/4 -> 1/2, 0 -> 0 (all exact in fp32)
+    assert sig.tolist() == [1.0, 0.75, 0.5, 0.0, 0.0]
+    assert t.tolist() == [1.0, 0.75, 0.5, 0.0]
+    grid = np.linspace(1, 0.05, 20)
+    for shift in (0.5, 1.7, 6.0):
+        s_, _ = O.sigma_schedule(grid, shift)
+        assert np.all(np.diff(s_[:-1]) < 0)                 # still decreasing
+        assert (s_[1:-1] > grid[1:]).all() == (shift > 1)    # shift > 1 raises every sigma below 1
+
 # ---------------------------------------------------------------- double-stream block
 
 def _double(Wt, Wi, pos, x, vecc, L, arch=TINY):
