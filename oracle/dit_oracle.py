@@ -49,6 +49,9 @@ run, is the block; a run with zero gates keeps its rows.
 eps 0 each row of a half's update divided by its gate and norm weight has
 RMS 1 (RMSNorm) or mean 0 and variance 1 (LayerNorm), and the block is
 unchanged when the product's weight is scaled.
+`block_forward_cached` is pinned to it: with the cache recorded from the
+same rows its updated rows are the block's, the read-only rows stay, and
+the read-only rows' own values no longer matter once cached.
 `double_block_forward` is pinned to it as well: with the same weights in
 both streams it is the sequential block, and with no text rows it is the
 sequential block of the image weights.
@@ -508,6 +511,44 @@ def block_forward_runs_rows(x, bw: BlockWeights, vecs, runs, cos, sin, arch: Arc
     a = swiglu_interleaved(linear(h2, bw.w_up))
     y = x1 + gate_m[rows] * post_norm(linear(a, bw.w_down), bw.post_mlp, arch)
     return y, o, a
+
+
+def reference_kv(x, bw: BlockWeights, vec, cos, sin, arch: Arch, first: int):
+    """The keys and values (after the head norm and rotary) of rows
+    [first, S) as the block computes them over x ([GZ] RefSlot: a recording
+    step keeps the reference rows' keys and values).  Returns (k, v), each
+    [H, S - first, d]."""
+    _, ref = block_forward(x, bw, vec, cos, sin, arch, keep=True)
+    return ref["k"][:, first:], ref["v"][:, first:]
+
+
+def block_forward_cached(x, bw: BlockWeights, vec, cos, sin, arch: Arch, first: int, k_ref, v_ref):
+    """The block over the first rows only ([GZ] Sequence.active: rows
+    [0, first) are updated, rows [first, S) are read only, with the same
+    positions and modulation; RefSlot: the read-only rows' keys and values
+    come from a recording step, k_ref and v_ref [H, S - first, d]).  The
+    queries are rows [0, first); the keys and values are the first rows'
+    own followed by the cached ones.  Rows [first, S) are returned as they
+    are."""
+    x = np.asarray(x, F64)
+    S, D = x.shape
+    H, d = arch.heads, arch.head_dim
+    shift_a, scale_a, gate_a, shift_m, scale_m, gate_m = modulation(vec, bw.w_mod, 6)
+    xa = x[:first]
+    h = modulated_norm(xa, shift_a, scale_a, arch, bw.norm1)
+    qkv = linear(h, bw.w_qkv)
+    q = head_prep(heads_of(qkv[:, 0:H * d], H, d), bw.q_norm, arch.qk_eps, cos[:first], sin[:first])
+    k = head_prep(heads_of(qkv[:, H * d:2 * H * d], H, d), bw.k_norm, arch.qk_eps, cos[:first], sin[:first])
+    v = heads_of(qkv[:, 2 * H * d:3 * H * d], H, d)
+    k = np.concatenate([k, np.asarray(k_ref, F64)], axis=1)
+    v = np.concatenate([v, np.asarray(v_ref, F64)], axis=1)
+    o = attention(q, k, v).transpose(1, 0, 2).reshape(first, H * d)
+    x1 = xa + gate_a * post_norm(linear(o, bw.w_out), bw.post_attn, arch)
+    h2 = modulated_norm(x1, shift_m, scale_m, arch, bw.norm2)
+    a = swiglu_interleaved(linear(h2, bw.w_up))
+    y = x.copy()
+    y[:first] = x1 + gate_m * post_norm(linear(a, bw.w_down), bw.post_mlp, arch)
+    return y
 
 
 def parallel_block_forward(x, bw: BlockWeights, vec, cos, sin, arch: Arch,

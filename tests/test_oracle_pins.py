@@ -703,6 +703,39 @@ def test_sigma_schedule_shift_closed_forms():
         assert np.all(np.diff(s_[:-1]) < 0)                 # still decreasing
         assert (s_[1:-1] > grid[1:]).all() == (shift > 1)    # shift > 1 raises every sigma below 1
 
+
+# ---------------------------------------------------------------- reference rows (RefSlot)
+
+def test_cached_block_with_a_fresh_cache_is_the_block():
+    W, pos, x, vecc = _tiny_case(seed=80, S_L=2, h=3, w=3)
+    c, s = O.rope_tables(pos, TINY.axes)
+    bw = O.BlockWeights(**W)
+    S = len(pos)
+    ref = O.block_forward(x, bw, vecc, c, s, TINY)
+    for first in (1, 4, S - 1, S):
+        k, v = O.reference_kv(x, bw, vecc, c, s, TINY, first)
+        y = O.block_forward_cached(x, bw, vecc, c, s, TINY, first, k, v)
+        assert np.abs(y[:first] - ref[:first]).max() < 1e-12
+        assert (y[first:] == x[first:]).all()
+
+
+def test_cached_block_reads_the_cache_not_the_rows():
+    W, pos, x, vecc = _tiny_case(seed=81, S_L=2, h=3, w=3)
+    c, s = O.rope_tables(pos, TINY.axes)
+    bw = O.BlockWeights(**W)
+    first = 5
+    k, v = O.reference_kv(x, bw, vecc, c, s, TINY, first)
+    y = O.block_forward_cached(x, bw, vecc, c, s, TINY, first, k, v)
+    x2 = x.copy()
+    # the read-only rows move (not by a shift or a scale, which the norm
+    # removes), the cache does not
+    x2[first:] += np.random.default_rng(82).standard_normal(x2[first:].shape)
+    y2 = O.block_forward_cached(x2, bw, vecc, c, s, TINY, first, k, v)
+    assert (y2[:first] == y[:first]).all() and (y2[first:] == x2[first:]).all()
+    k2, v2 = O.reference_kv(x2, bw, vecc, c, s, TINY, first)
+    y3 = O.block_forward_cached(x, bw, vecc, c, s, TINY, first, k2, v2)
+    assert np.abs(y3[:first] - y[:first]).max() > 1e-6     # another cache, other rows
+
 # ---------------------------------------------------------------- double-stream block
 
 def _double(Wt, Wi, pos, x, vecc, L, arch=TINY):
