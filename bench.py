@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--no-double", action="store_true", help="skip the double-stream block timing")
     p.add_argument("--no-runs", action="store_true", help="skip the timing of the block with modulation runs")
     p.add_argument("--no-sandwich", action="store_true", help="skip the sandwich block timing")
+    p.add_argument("--no-cached", action="store_true", help="skip the timing of the step with cached reference rows")
     p.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 block timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
@@ -343,6 +344,28 @@ def main():
         log(f"block with modulation runs: {msr:.3f} ms  {runs_tf:.1f} TFLOP/s")
         del bwr, xr, vecs
 
+    # ---------------------------------------------------------------- cached reference rows (bf16)
+    cached = None
+    if not args.no_cached:
+        first = S - 1024
+        log(f"block step with 1024 cached reference rows (rows {first}..{S - 1} read only)")
+        bwc = L.BlockWeights.from_host(case["block"])
+        xc = L.dev_f32(case["x"])
+        slot = torch.empty(2 * H * (S - first) * 128, dtype=torch.bfloat16, device="cuda")
+        ctx.block_forward_cached(bwc, xc, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, True)
+
+        def cfwd():
+            ctx.block_forward_cached(bwc, xc, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, False)
+        msc = time_call(torch, cfwd, args.steps, args.warmup)
+        # algorithmic work of the step: the products over `first` rows, the
+        # attention of `first` queries against all S keys, the GEMV
+        c_flops = (2 * first * D * (3 * D + D + 2 * F + F) + 4 * H * first * S * 128 + 2 * 6 * D * D)
+        c_tf = c_flops / (msc * 1e-3) / 1e12
+        cached = {"ms": round(msc, 4), "tflops": round(c_tf, 2), "first": first, "flops_per_step": c_flops,
+                  "stages_ms_per_step": stage_split(ctx, cfwd, args.steps)}
+        log(f"cached step: {msc:.3f} ms  {c_tf:.1f} TFLOP/s")
+        del bwc, xc, slot
+
     # ---------------------------------------------------------------- sandwich block (bf16)
     sw = None
     if not args.no_sandwich:
@@ -429,6 +452,7 @@ def main():
         "double_block": dbl,
         "runs_block": runs_res,
         "sandwich_block": sw,
+        "cached_step": cached,
         "w8a8_block": w8,
     }
     if img:

@@ -418,11 +418,38 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
 // norms run per run with the run's shift and scale; QKV, the attention and
 // UP once over all rows; OUT and DOWN per run with the run's gate, two runs
 // per launch.
+// Keys and values of rows [first, Sk) between the block's q/k/vt buffers
+// (head stride Sk, V^T row stride round_up(Sk, 64)) and a RefSlot's rows:
+// K [H, count, 128] then V^T [H, 128, count], count = Sk - first; out:
+// buffers -> slot (a recording step), else slot -> buffers.
+dit_status ref_copy(dit_ctx *c, uint16_t *slot_mut, const uint16_t *slot, int first, int Sk, bool out) {
+    const int H = c->arch.heads, count = Sk - first, ldv = round_up(Sk, 64);
+    if (count <= 0) return DIT_OK;
+    uint16_t *sk = const_cast<uint16_t *>(out ? slot_mut : slot);
+    uint16_t *sv = sk + static_cast<size_t>(H) * count * 128;
+    uint16_t *bk = c->k + static_cast<size_t>(first) * 128, *bv = c->vt + first;
+    const size_t kw = static_cast<size_t>(count) * 256, kp = static_cast<size_t>(Sk) * 256;
+    const size_t vw = static_cast<size_t>(count) * 2, vp = static_cast<size_t>(ldv) * 2;
+    hipError_t e = out ? hipMemcpy2DAsync(sk, kw, bk, kp, kw, H, hipMemcpyDeviceToDevice, c->stream)
+                       : hipMemcpy2DAsync(bk, kp, sk, kw, kw, H, hipMemcpyDeviceToDevice, c->stream);
+    if (e == hipSuccess)
+        e = out ? hipMemcpy2DAsync(sv, vw, bv, vp, vw, static_cast<size_t>(H) * 128, hipMemcpyDeviceToDevice, c->stream)
+                : hipMemcpy2DAsync(bv, vp, sv, vw, vw, static_cast<size_t>(H) * 128, hipMemcpyDeviceToDevice, c->stream);
+    if (e != hipSuccess) return fail(c, DIT_EDEVICE, "reference key/value copy: %s", hipGetErrorString(e));
+    return DIT_OK;
+}
+
+// With Sk > S the rows [S, Sk) are read-only context ([GZ] Sequence.active,
+// RefSlot): their keys and values come from `slot` (K [H, Sk - S, 128] then
+// V^T [H, 128, Sk - S]), copied in after the QKV product of rows [0, S), and
+// the attention's queries are rows [0, S) against all Sk keys.
 dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const float *vecs, int R, const int32_t *runs,
-                              int n_runs, const float *cs, const float *sn, int S) {
+                              int n_runs, const float *cs, const float *sn, int S, int Sk = 0,
+                              const uint16_t *slot = nullptr) {
     const dit_arch &A = c->arch;
     const int D = A.hidden, F = A.ffn, H = A.heads;
-    const int Sp = round_up(S, 64);
+    if (Sk < S) Sk = S;
+    const int Sp = round_up(Sk, 64);
     const bool w8 = b->wtype == DIT_W_INT8_B32;
     const bool rms = A.norm == DIT_NORM_RMS;
     hipStream_t st = c->stream;
@@ -532,13 +559,15 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
     e.cos = cs;
     e.sin = sn;
     e.qk_eps = A.qk_eps;
+    e.rows_total = Sk;
     {
         Stage t(c, DIT_ST_QKV);
         DIT_LAUNCH(c, product(c->h, 0, S, 0, 3 * D, D, e), "qkv");
     }
+    if (Sk > S) DIT_TRY(ref_copy(c, nullptr, slot, S, Sk, false));
     {
         Stage t(c, DIT_ST_ATTN);
-        DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
+        DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, Sk, Sp, c->o, D, st, S), "attention");
     }
     DIT_TRY(gated(c->o, D, 1, D, 2 * D, DIT_ST_OUT, b->post_w[0]));
     DIT_TRY(norms(mod + 3 * D, DIT_ST_NORM2, c->h2, b->norm_w[1]));
@@ -902,6 +931,25 @@ dit_status dit_block_forward_runs(dit_ctx *ctx, const dit_block *b, float *x, co
     if (end != L + N) return fail(ctx, DIT_EINVAL, "runs end at %d, not at L + N = %d", end, L + N);
     DIT_TRY(check_ctx(ctx));
     return block_forward_runs(ctx, b, x, vecs, R, runs, n_runs, cos_t, sin_t, L + N);
+}
+
+dit_status dit_block_forward_cached(dit_ctx *ctx, const dit_block *b, float *x, const float *vec, const float *cos_t,
+                                   const float *sin_t, int L, int N, int first, uint16_t *slot, int record) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
+    DIT_TRY(check_block(ctx, b, false, true));
+    DIT_TRY(check_rows(ctx, L, N));
+    const int S = L + N;
+    if (first < 1 || first > S) return fail(ctx, DIT_ERANGE, "first = %d outside 1..%d", first, S);
+    if (first < S && !slot) return fail(ctx, DIT_EINVAL, "slot is NULL with %d reference rows", S - first);
+    if (record != 0 && record != 1) return fail(ctx, DIT_EINVAL, "record = %d is not 0 or 1", record);
+    DIT_TRY(check_ctx(ctx));
+    if (record) {
+        DIT_TRY(block_forward(ctx, b, x, vec, cos_t, sin_t, S));
+        return ref_copy(ctx, slot, nullptr, first, S, true);
+    }
+    const int32_t one[3] = {0, first, 0};
+    return block_forward_runs(ctx, b, x, vec, 1, one, 1, cos_t, sin_t, first, S, slot);
 }
 
 dit_status dit_double_block_forward(dit_ctx *ctx, const dit_block *txt, const dit_block *img, float *x,

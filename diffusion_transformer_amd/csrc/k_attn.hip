@@ -89,7 +89,7 @@ __device__ __forceinline__ void att_lgkm_done() { __builtin_amdgcn_s_waitcnt(0xc
 __global__ void __launch_bounds__(NT, 1)
 k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
             const uint16_t *__restrict__ Vt, int S, int ldv, int heads, uint16_t *__restrict__ O,
-            int ldo) {
+            int ldo, int Sq) {
     __shared__ u32x4 lds[NKB * K_U4 + NVB * V_U4];   // 112 KB
     u32x4 *const Kb = lds;
     u32x4 *const Vb = lds + NKB * K_U4;
@@ -97,8 +97,10 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     const int grp = wave >> 2, wg = wave & 3;
     const int g = lane >> 4, l16 = lane & 15;
 
-    // XCD-compact order: consecutive work ids on one XCD share a head
-    const int nqb = (S + QB - 1) / QB;
+    // XCD-compact order: consecutive work ids on one XCD share a head.
+    // Queries are rows [0, Sq) (Sq <= S; q keeps the head stride S), keys
+    // and values all S rows.
+    const int nqb = (Sq + QB - 1) / QB;
     const int total = nqb * heads;
     int bid = blockIdx.x;
     {
@@ -119,7 +121,7 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     bf16x8 qf[2][4];
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
-        const int qr = min(q0 + tq * 16 + l16, S - 1);
+        const int qr = min(q0 + tq * 16 + l16, Sq - 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const u32x4 w = *reinterpret_cast<const u32x4 *>(Qh + static_cast<int64_t>(qr) * HD + ks * 32 + g * 8);
@@ -377,7 +379,7 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     for (int tq = 0; tq < 2; ++tq) {
         const float inv = 1.0f / rsum[tq][0];
         const int q = q0 + tq * 16 + l16;
-        if (q >= S) continue;
+        if (q >= Sq) continue;
         uint16_t *orow = O + static_cast<int64_t>(q) * ldo + h * HD;
 #pragma unroll
         for (int dd = 0; dd < 8; ++dd) {
@@ -389,10 +391,12 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 }
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int heads,
-                            int S, int ldv, uint16_t *o, int ldo, hipStream_t st) {
-    if (S <= 0 || heads <= 0) return hipSuccess;
-    const int grid = ((S + QB - 1) / QB) * heads;
-    k_attention<<<grid, NT, 0, st>>>(q, k, vt, S, ldv, heads, o, ldo);
+                            int S, int ldv, uint16_t *o, int ldo, hipStream_t st, int Sq) {
+    if (Sq < 0) Sq = S;
+    if (S <= 0 || heads <= 0 || Sq == 0) return hipSuccess;
+    if (Sq > S) return hipErrorInvalidValue;
+    const int grid = ((Sq + QB - 1) / QB) * heads;
+    k_attention<<<grid, NT, 0, st>>>(q, k, vt, S, ldv, heads, o, ldo, Sq);
     return hipGetLastError();
 }
 

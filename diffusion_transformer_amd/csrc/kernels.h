@@ -104,7 +104,9 @@ hipError_t launch_gemm_w8a8(const int8_t *A, const float *a_scale, const int8_t 
 bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &epi, bool a_rows_padded);
 
 // ---- attention (k_attn.hip) ------------------------------------------------
+// o = softmax(q k^T / sqrt(128)) v per head over S keys; the queries are
+// rows [0, Sq) (Sq < 0: all S), q keeping the head stride S.
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, int heads,
-                            int S, int ldv, uint16_t *o, int ldo, hipStream_t st);
+                            int S, int ldv, uint16_t *o, int ldo, hipStream_t st, int Sq = -1);
 
 }  // namespace dit

@@ -82,6 +82,8 @@ _SIGS = {
     "dit_parallel_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_double_block_forward": (C.c_int, [_P, C.POINTER(Block), C.POINTER(Block), _P, _P, _P, _P, C.c_int,
                                            C.c_int]),
+    "dit_block_forward_cached": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int, C.c_int, _P,
+                                           C.c_int]),
     "dit_block_forward_runs": (C.c_int, [_P, C.POINTER(Block), _P, _P, C.c_int, _P, C.c_int, _P, _P, C.c_int,
                                          C.c_int]),
     "dit_prologue": (C.c_int, [_P, C.POINTER(Model), _P, C.c_int, _P]),
@@ -262,6 +264,12 @@ class Context:
         self._call("dit_block_forward_runs", C.byref(block.struct), _ptr(x, torch.float32, "x"),
                    _ptr(vecs, torch.float32, "vecs"), int(vecs.shape[0]), r.ctypes.data_as(C.c_void_p), len(r),
                    _ptr(cos, torch.float32, "cos"), _ptr(sin, torch.float32, "sin"), L, N)
+
+    def block_forward_cached(self, block: "BlockWeights", x, vec, cos, sin, L, N, first, slot, record):
+        """The block with reference rows [first, L+N) whose keys and values live in slot (bf16)."""
+        self._call("dit_block_forward_cached", C.byref(block.struct), _ptr(x, torch.float32, "x"),
+                   _ptr(vec, torch.float32, "vec"), _ptr(cos, torch.float32, "cos"), _ptr(sin, torch.float32, "sin"),
+                   L, N, int(first), _ptr(slot, torch.bfloat16, "slot"), 1 if record else 0)
 
     def double_block_forward(self, txt: "BlockWeights", img: "BlockWeights", x, vec, cos, sin, L, N):
         """The double-stream block: rows [0, L) take `txt`, the rest `img`."""

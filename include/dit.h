@@ -11,7 +11,8 @@
  *        attention, s.4.4 fused qk-prep.
  *   [GZ] "gizai:dit" module reference: Arch, Block, Modulation, Sequence,
  *        Work, gluRows, gatedInto, normedInto, prepOf, sinusoids,
- *        Block.forward, Block.parallel, runsOf, gatedInto, HEAD, CHUNK.
+ *        Block.forward, Block.parallel, runsOf, gatedInto, RefSlot,
+ *        Sequence.active, HEAD, CHUNK.
  *
  * Conventions (all entry points):
  *  - Every tensor argument is a DEVICE pointer to caller-owned memory on the
@@ -274,6 +275,23 @@ dit_status dit_parallel_block_forward(dit_ctx *ctx, const dit_block *b, float *x
 dit_status dit_block_forward_runs(dit_ctx *ctx, const dit_block *b, float *x, const float *vecs, int R,
                                   const int32_t *runs, int n_runs, const float *cos, const float *sin, int L,
                                   int N);
+
+/* The block with cached reference rows ([GZ] RefSlot, Sequence.active):
+ * rows [first, L+N) are a reference whose keys and values are kept across
+ * steps in `slot` (device bf16: K [H, count, 128] then V^T [H, 128, count],
+ * count = L + N - first; the caller owns it, 2 * H * count * 128 values).
+ * record = 1: the whole block over all rows (dit_block_forward), then the
+ * reference rows' keys and values (after the head norm and rotary) are
+ * copied into the slot.  record = 0: only rows [0, first) are updated -- their
+ * norm, QKV, attention against the first rows' keys and the slot's, the
+ * output product and the MLP -- and rows [first, L+N) of x stay as they
+ * are.  first in 1..L+N (first = L+N: no reference rows, slot may be NULL).
+ * Takes the weights the sequential block takes.  Errors as
+ * dit_block_forward, DIT_ERANGE for first, DIT_EINVAL for a NULL slot with
+ * reference rows or a record flag other than 0 or 1. */
+dit_status dit_block_forward_cached(dit_ctx *ctx, const dit_block *b, float *x, const float *vec,
+                                    const float *cos, const float *sin, int L, int N, int first,
+                                    uint16_t *slot, int record);
 
 /* The double-stream block ([K4] Appendix B: the FLUX.2 double blocks, one
  * set of attention and MLP weights per stream, the q/k preparation run per

@@ -794,6 +794,92 @@ def test_w8a8_weights_rejected_where_not_taken(ctx_tiny):
     assert e.value.status == L.EINVAL
 
 
+
+# --------------------------------------------------------------- reference rows (RefSlot)
+
+def _ref_first(name, sh):
+    # the reference: the last rows of the image (24, 300 or 1024 of them)
+    return sh.S - {"tiny": 24, "s1088": 300, "s4608": 1024}[name]
+
+
+@pytest.mark.parametrize("name", ["tiny", "s1088"])
+def test_cached_block_parity(ctx_tiny, name):
+    case = synth.block_case(name)
+    sh = case["shape"]
+    la, oa = arch_pair(sh)
+    ctx = ctx_tiny if name == "tiny" else L.Context(la, max_rows=sh.S)
+    first, H, D = _ref_first(name, sh), sh.heads, sh.hidden
+    count = sh.S - first
+    say("cached block", name, "first =", first)
+    seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    slot = torch.empty(2 * H * count * 128, dtype=torch.bfloat16, device="cuda")
+    # recording step: the whole block, then the reference rows' k and v
+    x0 = L.dev_f32(case["x"])
+    ctx.block_forward_cached(bw, x0, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, True)
+    torch.cuda.synchronize()
+    cs, sn, vec = _oracle_inputs(case, oa)
+    ob = oracle_block(case["block"])
+    compare(f"{name}/record y", np_of(x0), O.block_forward(case["x"], ob, vec, cs, sn, oa))
+    k_ref, v_ref = O.reference_kv(case["x"], ob, vec, cs, sn, oa, first)
+    sl = np_of(slot)
+    compare(f"{name}/slot k", sl[:H * count * 128].reshape(H, count, 128), k_ref, bf16_stored=True)
+    compare(f"{name}/slot v", sl[H * count * 128:].reshape(H, 128, count).transpose(0, 2, 1), v_ref, bf16_stored=True)
+    # a later step: new values in the updated rows, the reference rows as they were
+    x1h = case["x"].copy()
+    x1h[:first] = synth.normal((first, D), seed=sh.seed + 400)
+    x1 = L.dev_f32(x1h)
+    ctx.block_forward_cached(bw, x1, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, False)
+    torch.cuda.synchronize()
+    got = np_of(x1)
+    y = O.block_forward_cached(x1h, ob, vec, cs, sn, oa, first, k_ref, v_ref)
+    assert (got[first:] == x1h[first:]).all()
+    compare(f"{name}/step y", got[:first], y[:first])
+    compare(f"{name}/step delta", got[:first] - x1h[:first], y[:first] - x1h[:first])
+    if ctx is not ctx_tiny:
+        ctx.close()
+
+
+def test_cached_block_step_on_the_recorded_rows_is_the_block_bit_exact(ctx_big):
+    # the same rows after the recording step: the first rows' arithmetic is
+    # the whole block's in the same kernels, with the keys and values of the
+    # reference rows put back bit for bit
+    case = synth.block_case("s4608")
+    sh = case["shape"]
+    first, H = _ref_first("s4608", sh), sh.heads
+    count = sh.S - first
+    say("cached block s4608 first =", first)
+    seq = GpuSeq(ctx_big, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    slot = torch.empty(2 * H * count * 128, dtype=torch.bfloat16, device="cuda")
+    x0 = L.dev_f32(case["x"])
+    ctx_big.block_forward_cached(bw, x0, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, True)
+    x1 = L.dev_f32(case["x"])
+    ctx_big.block_forward_cached(bw, x1, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, False)
+    ref = L.dev_f32(case["x"])
+    ctx_big.block_forward(bw, ref, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    torch.cuda.synchronize()
+    assert torch.equal(x0, ref)
+    assert torch.equal(x1[:first], ref[:first])
+    assert torch.equal(x1[first:], L.dev_f32(case["x"])[first:])
+
+
+def test_cached_block_rejects_bad_arguments(ctx_tiny):
+    case = synth.block_case("tiny")
+    sh = case["shape"]
+    seq = GpuSeq(ctx_tiny, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    x = L.dev_f32(case["x"])
+    for first, slot in ((0, None), (sh.S + 1, None), (sh.S - 4, None)):
+        with pytest.raises(L.DitError):
+            ctx_tiny.block_forward_cached(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, False)
+    # no reference rows: no slot needed, and the step is the block
+    ref = L.dev_f32(case["x"])
+    ctx_tiny.block_forward(bw, ref, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    ctx_tiny.block_forward_cached(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N, sh.S, None, False)
+    torch.cuda.synchronize()
+    assert torch.equal(x, ref)
+
 # --------------------------------------------------------------- sampler grid
 
 @pytest.mark.parametrize("shift", [1.0, 3.0, 0.37])
