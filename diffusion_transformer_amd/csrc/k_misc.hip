@@ -135,7 +135,9 @@ hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *y, hipStream_t st
 // ---------------------------------------------------------------------- GEMV
 // One wave per output row, 16-byte loads of W (8 bf16 per lane per step),
 // the input vector staged once per block in LDS (with silu applied).  The
-// weight is read exactly once: the kernel is HBM-bound.
+// weight is read exactly once: the kernel is HBM-bound, so a lane issues all
+// its loads of a row (at most 8) before the first multiply, keeping several
+// in flight per wave; the sum runs in the same order as a one-load loop.
 constexpr int kGemvThreads = 256;
 constexpr int kGemvMaxI = 4096;
 
@@ -152,9 +154,19 @@ k_gemv(const uint16_t *__restrict__ W, const float *__restrict__ x, int O, int I
     const int nchunk = I / 8;
     for (int o = blockIdx.x * 4 + wv; o < O; o += gridDim.x * 4) {
         const u32x4 *row = reinterpret_cast<const u32x4 *>(W + static_cast<int64_t>(o) * I);
+        constexpr int J = kGemvMaxI / 8 / 64;
+        u32x4 wr[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int c = lane + 64 * j;
+            wr[j] = c < nchunk ? __builtin_nontemporal_load(row + c) : u32x4{0u, 0u, 0u, 0u};
+        }
         float acc = 0.f;
-        for (int c = lane; c < nchunk; c += 64) {
-            u32x4 w = __builtin_nontemporal_load(row + c);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int c = lane + 64 * j;
+            if (c >= nchunk) break;
+            const u32x4 w = wr[j];
             const float *xp = xs + c * 8;
             acc += bf16lo_to_f32(w.x) * xp[0] + bf16hi_to_f32(w.x) * xp[1];
             acc += bf16lo_to_f32(w.y) * xp[2] + bf16hi_to_f32(w.y) * xp[3];
@@ -168,6 +180,8 @@ k_gemv(const uint16_t *__restrict__ W, const float *__restrict__ x, int O, int I
 
 hipError_t launch_gemv(const uint16_t *W, const float *x, int O, int I, bool silu_in, float *y,
                        hipStream_t st) {
+    if (O <= 0) return hipSuccess;
+    if (I <= 0 || I > kGemvMaxI || I % 8) return hipErrorInvalidValue;
     int blocks = (O + 3) / 4;
     if (blocks > 2048) blocks = 2048;
     k_gemv<<<blocks, kGemvThreads, 0, st>>>(W, x, O, I, silu_in ? 1 : 0, y);
