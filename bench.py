@@ -132,7 +132,7 @@ def summarize_counters(fetch_csv, write_csv, out_json):
         pending = None
         for d in order:
             n = names[d]
-            pp = re.search(r"k_gemm_p3<(\d), (true|false)>", n)
+            pp = re.search(r"k_gemm_p3<(\d), (true|false), false>", n)   # the bf16 form
             epi = pp or re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
             epi = int(epi.group(1)) if epi else None
             if pp and pp.group(2) == "true":
