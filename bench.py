@@ -420,9 +420,11 @@ def main():
     ctx.close()
 
     # ---------------------------------------------------------------- whole image
-    img = None
+    img = img8 = None
     if not args.no_denoise:
         img = bench_images(torch, L, synth, args.images)
+        if not args.no_w8a8:
+            img8 = bench_images(torch, L, synth, args.images, w8a8=True)
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None if args.no_cpu else cpu_baseline()
@@ -457,17 +459,20 @@ def main():
     }
     if img:
         out.update(img)
+    if img8:
+        out["w8a8_image"] = {k: img8[k] for k in ("images_per_s", "ms_per_image", "image_finite", "image_workload")}
     out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
-def bench_images(torch, L, synth, images):
-    """Whole path per image at the 1024-px DiT: 32 blocks, 4 Euler steps."""
+def bench_images(torch, L, synth, images, w8a8=False):
+    """Whole path per image at the 1024-px DiT: 32 blocks, 4 Euler steps;
+    with w8a8, blocks of INT8 weight rows (W8A8 products)."""
     sh = synth.SHAPES["dit32"]
     S, D, H, F, lat = sh.S, sh.hidden, sh.heads, sh.ffn, sh.latent
     arch = L.make_arch(hidden=D, heads=H, ffn=F, latent=lat, text_dim=sh.text_dim)
     ctx = L.Context(arch, max_rows=S)
-    log("generating 32 blocks of random bf16 weights on the GPU")
+    log(f"generating 32 blocks of random {'W8A8' if w8a8 else 'bf16'} weights on the GPU")
     g = torch.Generator(device="cuda")
     g.manual_seed(sh.seed)
 
@@ -475,11 +480,23 @@ def bench_images(torch, L, synth, images):
         t = torch.randn((o, i), generator=g, device="cuda", dtype=torch.float32).mul_(0.02)
         return t.to(torch.bfloat16)
 
+    def q8(o, i):
+        return torch.randint(-127, 128, (o, i), generator=g, device="cuda", dtype=torch.int8)
+
+    def s8(o):
+        return torch.full((o,), 0.02 * 3 ** 0.5 / 127, device="cuda", dtype=torch.float32)
+
     blocks = []
+    dims = {"w_qkv": (3 * D, D), "w_out": (D, D), "w_up": (2 * F, D), "w_down": (D, F)}
     for _ in range(sh.blocks):
-        t = {"w_qkv": w(3 * D, D), "w_out": w(D, D), "w_up": w(2 * F, D), "w_down": w(D, F),
-             "w_mod": w(6 * D, D),
-             "q_norm": torch.ones(128, device="cuda"), "k_norm": torch.ones(128, device="cuda")}
+        if w8a8:
+            t = {}
+            for n, (o, i) in dims.items():
+                t["q8_" + n], t["s8_" + n] = q8(o, i), s8(o)
+        else:
+            t = {n: w(o, i) for n, (o, i) in dims.items()}
+        t.update({"w_mod": w(6 * D, D), "q_norm": torch.ones(128, device="cuda"),
+                  "k_norm": torch.ones(128, device="cuda")})
         blocks.append(L.BlockWeights(t))
     top = {"w_t1": w(D, sh.time_dim), "w_t2": w(D, D), "w_in": w(D, lat), "w_txt": w(D, sh.text_dim),
            "w_fmod": w(2 * D, D), "w_final": w(lat, D)}
@@ -515,14 +532,16 @@ def bench_images(torch, L, synth, images):
     blk = sum(stage_flops(S, D, H, F).values())
     img_flops = 4 * (sh.blocks * blk + 2 * sh.N * lat * D + 2 * sh.N * D * lat + 2 * D * 256
                      + 2 * D * D + 2 * 2 * D * D) + 2 * sh.L * sh.text_dim * D
-    log(f"image: {ms:.1f} ms  {1000 / ms:.3f} img/s  {img_flops / ms / 1e9:.1f} TFLOP/s  finite={finite}")
+    log(f"image{' (W8A8)' if w8a8 else ''}: {ms:.1f} ms  {1000 / ms:.3f} img/s  {img_flops / ms / 1e9:.1f} TFLOP/s  "
+        f"finite={finite}")
     ctx.close()
     del model, blocks, top
     torch.cuda.empty_cache()
     return {"images_per_s": round(1000.0 / ms, 4), "ms_per_image": round(ms, 2),
             "image_tflops": round(img_flops / ms / 1e9, 2), "image_flops": img_flops,
             "image_workload": "32-block DiT, 4 Euler steps (sigmas 1, .75, .5, .25, 0), L=512 + N=4096, "
-                              "latent 64, text features 4096-d, batch 1, random-init bf16 weights",
+                              f"latent 64, text features 4096-d, batch 1, random-init {'W8A8' if w8a8 else 'bf16'} "
+                              "block weights",
             "image_finite": finite}
 
 

@@ -199,7 +199,7 @@ def block_case(name: str = "tiny", seed=None, norm_std=0.0, rms=False, t=None, s
 
 
 def model_case(name: str = "dit32", blocks=None, seed=None, hidden=None, heads=None,
-               ffn=None, L=None, h=None, w=None, text_dim=None):
+               ffn=None, L=None, h=None, w=None, text_dim=None, w8a8=False):
     """Inputs of a whole DiT: latent x_lat [N, 64] ~ N(0,1), text features
     ctx [L, text_dim] ~ N(0,1), and all weights (time MLP, in/out linears,
     final modulation, `blocks` blocks).  Overrides make reduced-size twins."""
@@ -222,7 +222,7 @@ def model_case(name: str = "dit32", blocks=None, seed=None, hidden=None, heads=N
         w_fmod=_normal(rng, (2 * D, D), 0.02),
         w_final=_normal(rng, (sh.latent, D), 0.02),
     )
-    blocks = [block_weights(rng, sh, int8=False) for _ in range(sh.blocks)]
+    blocks = [block_weights(rng, sh, int8=False, w8a8=w8a8) for _ in range(sh.blocks)]
     return dict(shape=sh, x_lat=x_lat, ctx=ctx, top=top, blocks=blocks)
 
 

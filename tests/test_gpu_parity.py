@@ -899,10 +899,12 @@ def test_sigma_schedule_bit_exact(shift):
 
 # --------------------------------------------------------------- denoise
 
-def test_denoise_twin(ctx_tiny):
+@pytest.mark.parametrize("w8a8", [False, True])
+def test_denoise_twin(ctx_tiny, w8a8):
     """A reduced-width DiT (hidden 256, 2 heads, 3 blocks, 8 text + 8x8 image
-    rows, text features 256-d) through the full 4-step loop."""
-    m = synth.model_case("dit32", blocks=3, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8, text_dim=256)
+    rows, text features 256-d) through the full 4-step loop; bf16 or W8A8
+    block weights."""
+    m = synth.model_case("dit32", blocks=3, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8, text_dim=256, w8a8=w8a8)
     sh = m["shape"]
     la, oa = arch_pair(sh)
     ctx = L.Context(la, max_rows=sh.S)
