@@ -881,12 +881,9 @@ static hipError_t launch_pp2(const uint16_t *A, const uint16_t *W, int M, const 
     return hipGetLastError();
 }
 
-bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &ep, bool a_rows_padded) {
-    // Large problems: 256x256 tiles (8 waves; ping-pong for bf16 weights when
-    // A's allocation covers whole 256-row tiles and N is a multiple of 256).
-    const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
-    // the ping-pong kernel's staged epilogue moves 16-byte pieces and keeps
-    // the two heads of a QKV tile in one region
+// Whether the ping-pong kernel's staged epilogue can serve ep: it moves
+// 16-byte pieces and keeps the two heads of a QKV tile in one region.
+static bool pp_epilogue_ok(const GemmEpi &ep, int N) {
     auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const bool qkv_ok = ep.heads % 2 == 0 && al16(ep.q) && al16(ep.k) && al16(ep.cos) && al16(ep.sin);
     const bool act_ok = al16(ep.act) && ep.ld_act % 8 == 0;
@@ -901,6 +898,14 @@ bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &ep, bool a_ro
             break;
         default: break;
     }
+    return epi_ok;
+}
+
+bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &ep, bool a_rows_padded) {
+    // Large problems: 256x256 tiles (8 waves; ping-pong for bf16 weights when
+    // A's allocation covers whole 256-row tiles and N is a multiple of 256).
+    const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
+    bool epi_ok = pp_epilogue_ok(ep, N);
     if (ep.k_split > 0)
         epi_ok = epi_ok && ep.kind == EPI_GATE_RES && ep.w2 && ep.k_split % BK == 0 && ep.k_split >= 128 &&
                  K - ep.k_split >= 128;
@@ -933,6 +938,7 @@ hipError_t launch_gemm_w8a8(const int8_t *A, const float *a_scale, const int8_t 
                             int N, int K, const GemmEpi &ep_in, hipStream_t st) {
     if (M <= 0) return hipSuccess;
     if (N % PP_BN || K % 128 || K < 128 || !a_scale || !w_scale) return hipErrorInvalidValue;
+    if (ep_in.k_split > 0 || !pp_epilogue_ok(ep_in, N)) return hipErrorInvalidValue;
     GemmEpi ep = ep_in;
     ep.a_scale = a_scale;
     ep.w_scale = w_scale;

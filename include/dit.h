@@ -93,7 +93,8 @@ typedef struct {
  *   product's input rows are taken to INT8 with one scale a row
  *   (s = max|row| / 127, codes rint(v * 127 / max|row|)), fused into the
  *   modulated norm for QKV and UP; the int32 sums times both scales.  Only
- *   the sequential forms take it.
+ *   the sequential forms take it; x, cos and sin must then be 16-byte
+ *   aligned (the INT8 products have no unaligned fallback: DIT_EDEVICE).
  * norm_w: fp32.  [0] NORM1, [1] NORM2 ([D], required for DIT_NORM_RMS,
  *   ignored for DIT_NORM_LAYER), [2] Q_NORM, [3] K_NORM ([hd], required).
  * w_mod: bf16 [6D, D]; its output rows are shift, scale, gate of the
