@@ -215,8 +215,8 @@ def main():
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.traffic_json)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is "
-              "described in DESIGN.md and not run here.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path is sized for one "
+              "GPU's share and no multi-GPU run is made.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

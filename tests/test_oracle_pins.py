@@ -864,7 +864,7 @@ def test_denoise_composes_velocity_and_euler():
     assert (x == O.euler_step(x1, v1, 0.5, 0.0)).all()
 
 
-def test_block_flops_config_north_star():
+def test_block_flops_of_the_1024px_block():
     arch = O.Arch(3072, 24, 128, 12288)
     f = O.block_flops(4608, arch)
     assert abs(f / 1e9 - 1652.6) < 0.1
