@@ -880,6 +880,47 @@ def test_cached_block_rejects_bad_arguments(ctx_tiny):
     torch.cuda.synchronize()
     assert torch.equal(x, ref)
 
+
+def test_block_runs_single_row_runs(ctx_tiny):
+    # runs of one row at the start, in the middle and at the end
+    case = _runs_case("tiny", 3)
+    sh = case["shape"]
+    _, oa = arch_pair(sh)
+    runs = [(0, 1, 1), (1, 2, 0), (2, 40, 2), (40, 41, 1), (41, sh.S - 1, 0), (sh.S - 1, sh.S, 2)]
+    say("block runs", runs)
+    got = np_of(_runs_gpu(ctx_tiny, case, runs))
+    cs, sn, _ = _oracle_inputs(case, oa)
+    y = O.block_forward_runs(case["x"], oracle_block(case["block"]), case["vecs"], runs, cs, sn, oa)
+    compare("tiny/y", got, y)
+    compare("tiny/delta", got - case["x"], y - case["x"])
+
+
+@pytest.mark.parametrize("first", [1, 71])
+def test_cached_block_one_active_or_one_cached_row(ctx_tiny, first):
+    case = synth.block_case("tiny")
+    sh = case["shape"]
+    _, oa = arch_pair(sh)
+    H, count = sh.heads, sh.S - first
+    say("cached block tiny first =", first)
+    seq = GpuSeq(ctx_tiny, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    slot = torch.empty(2 * H * count * 128, dtype=torch.bfloat16, device="cuda")
+    x0 = L.dev_f32(case["x"])
+    ctx_tiny.block_forward_cached(bw, x0, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, True)
+    x1h = case["x"].copy()
+    x1h[:first] = synth.normal((first, sh.hidden), seed=sh.seed + 401)
+    x1 = L.dev_f32(x1h)
+    ctx_tiny.block_forward_cached(bw, x1, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, False)
+    torch.cuda.synchronize()
+    cs, sn, vec = _oracle_inputs(case, oa)
+    ob = oracle_block(case["block"])
+    k_ref, v_ref = O.reference_kv(case["x"], ob, vec, cs, sn, oa, first)
+    y = O.block_forward_cached(x1h, ob, vec, cs, sn, oa, first, k_ref, v_ref)
+    got = np_of(x1)
+    assert (got[first:] == x1h[first:]).all()
+    compare("tiny/step y", got[:first], y[:first])
+    compare("tiny/step delta", got[:first] - x1h[:first], y[:first] - x1h[:first])
+
 # --------------------------------------------------------------- sampler grid
 
 @pytest.mark.parametrize("shift", [1.0, 3.0, 0.37])
