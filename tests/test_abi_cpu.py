@@ -80,3 +80,32 @@ def test_ctx_create_without_gpu_reports_device():
     st, h = _create(L.make_arch(hidden=256, heads=2, ffn=1024))
     assert st == L.EDEVICE
     assert not h.value
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    # compile a host-only probe of the header with the system C compiler and
+    # compare sizes and field offsets with the binding's ctypes structures
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    fields = {"dit_arch": L.Arch, "dit_block": L.Block, "dit_model": L.Model}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "dit.h"', "int main(void) {"]
+    for cname, ct in fields.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in ct._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    for line in filter(None, out):
+        cname, what, val = line.split()
+        ct = fields[cname]
+        got = C.sizeof(ct) if what == "size" else getattr(ct, what).offset
+        assert got == int(val), f"{cname}.{what}: binding {got}, header {val}"
