@@ -921,6 +921,53 @@ def test_cached_block_one_active_or_one_cached_row(ctx_tiny, first):
     compare("tiny/step y", got[:first], y[:first])
     compare("tiny/step delta", got[:first] - x1h[:first], y[:first] - x1h[:first])
 
+
+def test_denoise_step_full_size_is_its_parts_bit_exact():
+    """At the 1024-px DiT's sizes (L=512, N=4096, hidden 3072, two blocks)
+    one denoise step equals the same step put together from the library's
+    single-step entry points (time vector, text rows and image-in product,
+    the blocks, final modulation, norm and product, Euler update), bit for
+    bit: the step's orchestration at the largest rows."""
+    m = synth.model_case("dit32", blocks=2)
+    sh = m["shape"]
+    la, _ = arch_pair(sh)
+    ctx = L.Context(la, max_rows=sh.S)
+    D, lat, S = sh.hidden, sh.latent, sh.S
+    say("denoise step parts, S =", S)
+    mw = L.ModelWeights.from_host(m["top"], m["blocks"])
+    top = mw.top
+    pos = torch.empty((S, 3), dtype=torch.int32, device="cuda")
+    ctx.positions(sh.L, sh.h, sh.w, pos)
+    cs = torch.empty((S, 64), dtype=torch.float32, device="cuda")
+    sn = torch.empty_like(cs)
+    ctx.rope_tables(pos, S, cs, sn)
+    txt = torch.empty((sh.L, D), dtype=torch.float32, device="cuda")
+    ctx.prologue(mw, L.dev_f32(m["ctx"]), sh.L, txt)
+    sigma, sigma_next = 0.75, 0.5
+    x = L.dev_f32(m["x_lat"])
+    v = torch.empty((sh.N, lat), dtype=torch.float32, device="cuda")
+    ctx.denoise_step(mw, x, txt, cs, sn, sh.L, sh.N, sigma, sigma_next, v)
+    # the same step from its parts
+    vec = torch.empty(D, dtype=torch.float32, device="cuda")
+    ctx.time_vector(top["w_t1"], top["w_t2"], sigma, vec)
+    seq = torch.empty((S, D), dtype=torch.float32, device="cuda")
+    seq[:sh.L] = txt
+    ctx.linear(L.dev_f32(m["x_lat"]).to(torch.bfloat16), top["w_in"], None, sh.N, D, lat, seq[sh.L:])
+    for b in mw.blocks:
+        ctx.block_forward(b, seq, vec, cs, sn, sh.L, sh.N)
+    fmod = torch.empty(2 * D, dtype=torch.float32, device="cuda")
+    ctx.modulation(top["w_fmod"], 2, vec, fmod)
+    h = torch.empty((sh.N, D), dtype=torch.bfloat16, device="cuda")
+    ctx.modulated_norm(seq[sh.L:], sh.N, fmod[:D], fmod[D:], None, la.final_eps, h)
+    v2 = torch.empty((sh.N, lat), dtype=torch.float32, device="cuda")
+    ctx.linear(h, top["w_final"], None, sh.N, lat, D, v2)
+    x2 = L.dev_f32(m["x_lat"])
+    ctx.euler_step(x2, v2, sh.N * lat, sigma, sigma_next)
+    torch.cuda.synchronize()
+    assert torch.equal(v, v2)
+    assert torch.equal(x, x2)
+    ctx.close()
+
 # --------------------------------------------------------------- sampler grid
 
 @pytest.mark.parametrize("shift", [1.0, 3.0, 0.37])
