@@ -237,9 +237,14 @@ class _RowSlicer:
 
 def linear_w8a8(x, w: Int8Rows) -> np.ndarray:
     """x W^T with x's rows quantized by quantize_rows_int8: the exact integer
-    dot products (int64) times x's row scale and W's row scale, in float64."""
+    dot products times x's row scale and W's row scale, in float64.  The
+    integer sums are taken by a float64 matrix product: every product of two
+    codes and every partial sum is an integer of magnitude below
+    K * 127^2 < 2^53, so each float64 addition is exact in any order."""
     q, s = quantize_rows_int8(x)
-    acc = q.astype(np.int64) @ np.asarray(w.q).astype(np.int64).T
+    wq = np.asarray(w.q)
+    assert q.shape[-1] * 127 * 127 < 2 ** 53
+    acc = q.astype(F64) @ wq.astype(F64).T
     return acc * np.asarray(s, F64)[..., None] * np.asarray(w.s, F64)[None, :]
 
 

@@ -968,6 +968,40 @@ def test_denoise_step_full_size_is_its_parts_bit_exact():
     assert torch.equal(x, x2)
     ctx.close()
 
+
+@pytest.mark.parametrize("norm", ["layer", "rms"])
+def test_cached_w8a8_sandwich_block(norm):
+    # the cached step, W8A8 weights and sandwich norms together, at 512 px
+    case = synth.block_case("s1088", norm_std=0.1 if norm == "rms" else 0.0, rms=(norm == "rms"), sandwich=True,
+                            w8a8=True)
+    sh = case["shape"]
+    la, oa = arch_pair(sh, norm)
+    ctx = L.Context(la, max_rows=sh.S)
+    first, H, D = _ref_first("s1088", sh), sh.heads, sh.hidden
+    count = sh.S - first
+    say("cached w8a8 sandwich block", norm, "first =", first)
+    seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    slot = torch.empty(2 * H * count * 128, dtype=torch.bfloat16, device="cuda")
+    x0 = L.dev_f32(case["x"])
+    ctx.block_forward_cached(bw, x0, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, True)
+    x1h = case["x"].copy()
+    x1h[:first] = synth.normal((first, D), seed=sh.seed + 402)
+    x1 = L.dev_f32(x1h)
+    ctx.block_forward_cached(bw, x1, seq.vec, seq.cos, seq.sin, sh.L, sh.N, first, slot, False)
+    torch.cuda.synchronize()
+    cs, sn, vec = _oracle_inputs(case, oa)
+    ob = oracle_block(case["block"])
+    y0, ref0 = O.block_forward(case["x"], ob, vec, cs, sn, oa, keep=True)
+    compare("record y", np_of(x0), y0)
+    k_ref, v_ref = ref0["k"][:, first:], ref0["v"][:, first:]      # what reference_kv returns
+    y = O.block_forward_cached(x1h, ob, vec, cs, sn, oa, first, k_ref, v_ref)
+    got = np_of(x1)
+    assert (got[first:] == x1h[first:]).all()
+    compare("step y", got[:first], y[:first])
+    compare("step delta", got[:first] - x1h[:first], y[:first] - x1h[:first])
+    ctx.close()
+
 # --------------------------------------------------------------- sampler grid
 
 @pytest.mark.parametrize("shift", [1.0, 3.0, 0.37])
