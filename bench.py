@@ -27,6 +27,7 @@ import time
 import numpy as np
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_INT8_TOPS = 5033.2        # dense INT8 matrix cores, twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 
 
@@ -412,8 +413,15 @@ def main():
             ctx.block_forward(bww, xw, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
         msw = time_call(torch, wfwd, args.steps, args.warmup)
         w_tf = total_flops / (msw * 1e-3) / 1e12
+        w_st = stage_split(ctx, wfwd, args.steps)
+        up_ops = stage_flops(S, D, H, F)["up"]
+        up_tops = up_ops / (w_st["up"] * 1e-3) / 1e12
         w8 = {"ms": round(msw, 4), "tflops": round(w_tf, 2), "flops_per_step": total_flops,
-              "stages_ms_per_step": stage_split(ctx, wfwd, args.steps)}
+              "stages_ms_per_step": w_st,
+              "roofline": {"kernel": "W8A8 up product (int8 matrix cores)", "bound": "mfma",
+                           "achieved": round(up_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                           "frac": round(up_tops / PEAK_INT8_TOPS, 4), "ops_per_launch": up_ops,
+                           "avg_ms": w_st["up"]}}
         log(f"W8A8 block: {msw:.3f} ms  {w_tf:.1f} TFLOP/s (int8 ops)")
         del bww, xw, cw
         torch.cuda.empty_cache()
