@@ -179,6 +179,10 @@ dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bo
         return fail(c, DIT_EINVAL, "unknown wtype %d", b->wtype);
     if (b->wtype == DIT_W_INT8_ROW && !sequential)
         return fail(c, DIT_EINVAL, "W8A8 weights are taken by the sequential block forms only");
+    // the SwiGLU rows of a W8A8 block are quantized one row per workgroup,
+    // at most 16384 wide; refused here, before the attention half updates x
+    if (b->wtype == DIT_W_INT8_ROW && c->arch.ffn > 16384)
+        return fail(c, DIT_EUNSUPPORTED, "W8A8 blocks take ffn up to 16384 (arch ffn %d)", c->arch.ffn);
     for (int i = 0; i < 4; ++i) {
         if (!b->w[i]) return fail(c, DIT_EINVAL, "block weight w[%d] is NULL", i);
         if (b->wtype != DIT_W_BF16 && !b->scale[i]) return fail(c, DIT_EINVAL, "int8 weight %d has no scales", i);
@@ -600,6 +604,17 @@ dit_status time_vector(dit_ctx *c, const uint16_t *w1, const uint16_t *w2, float
     return DIT_OK;
 }
 
+// The DiT's time input for a step at sigma ([HC] s.6): the timestep
+// sigma * 1000, divided by 1000 again, each an fp32 operation rounded on its
+// own (equal to sigma on grids such as linspace(1, 0, n); after a shift the
+// two can differ in the last bit).
+#pragma clang fp contract(off)
+float dit_time_input(float sigma) {
+    const float ts = sigma * 1000.f;
+    return ts / 1000.f;
+}
+#pragma clang fp contract(on)
+
 dit_status check_model(dit_ctx *c, const dit_model *m) {
     if (!m) return fail(c, DIT_EINVAL, "model is NULL");
     if (m->n_blocks < 0 || m->n_blocks > 1024) return fail(c, DIT_ERANGE, "n_blocks %d outside 0..1024", m->n_blocks);
@@ -991,7 +1006,7 @@ dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, cons
     const int D = A.hidden, S = L + N, lat = A.latent;
     hipStream_t st = ctx->stream;
 
-    DIT_TRY(time_vector(ctx, m->w_t1, m->w_t2, sigma, ctx->vec));
+    DIT_TRY(time_vector(ctx, m->w_t1, m->w_t2, dit_time_input(sigma), ctx->vec));
     {
         Stage tm(ctx, DIT_ST_IMG_IN);
         if (L > 0 &&

@@ -37,11 +37,13 @@
 //  - the row sum is one more MFMA per 32 keys with an all-ones A operand
 //    (it sums the same bf16-rounded P the values are weighted with); the
 //    running maximum is rescaled lazily: only when a tile's maximum exceeds
-//    it by more than 2^8 (exponents stay <= 2^8, exact either way).
-//  - the softmax is trimmed to the exponentials: queries are pre-multiplied
-//    by log2(e)/sqrt(128) and the score MFMAs start from minus the running
-//    maximum, so p = 2^score needs no separate scale-and-subtract; the
-//    maxima use three-input max and lane-row swaps.
+//    it by more than 2^8 (exponents stay <= 2^8, exact either way), and
+//    only upward, so no factor above 1 ever multiplies the partial sums.
+//  - the score scale is applied in fp32: q enters the MFMAs exactly as
+//    stored (bf16), the fp32 scores s = q.k are turned into base-2 exponent
+//    units relative to the running maximum by one fused multiply-add each,
+//    x = s * log2(e)/sqrt(128) - m, and p = 2^x; the maxima use three-input
+//    max and lane-row swaps.
 //  - blocks are remapped so that each XCD (own L2) serves whole heads.
 #include "common.h"
 #include "kernels.h"
@@ -114,24 +116,18 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     const uint16_t *Kh = Kg + static_cast<int64_t>(h) * S * HD;
     const uint16_t *Vh = Vt + static_cast<int64_t>(h) * HD * ldv;
 
-    // queries of this lane as B operands: [tq][kstep over d], multiplied by
-    // log2(e)/sqrt(128) (and rounded to bf16 again) so that the scores come
-    // out of the MFMAs in base-2 exponent units
-    const float sc = 0.08838834764831845f * 1.4426950408889634f;
+    // queries of this lane as B operands: [tq][kstep over d], as stored
     bf16x8 qf[2][4];
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
         const int qr = min(q0 + tq * 16 + l16, Sq - 1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(Qh + static_cast<int64_t>(qr) * HD + ks * 32 + g * 8);
-            const u32x4 u = {pack_bf16x2(bf16lo_to_f32(w[0]) * sc, bf16hi_to_f32(w[0]) * sc),
-                             pack_bf16x2(bf16lo_to_f32(w[1]) * sc, bf16hi_to_f32(w[1]) * sc),
-                             pack_bf16x2(bf16lo_to_f32(w[2]) * sc, bf16hi_to_f32(w[2]) * sc),
-                             pack_bf16x2(bf16lo_to_f32(w[3]) * sc, bf16hi_to_f32(w[3]) * sc)};
-            qf[tq][ks] = __builtin_bit_cast(bf16x8, u);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+            qf[tq][ks] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(Qh + static_cast<int64_t>(qr) * HD + ks * 32 + g * 8));
     }
+    // fp32 score scale in base-2 units: 1/sqrt(128) * log2(e)
+    const float sc = 0.08838834764831845f * 1.4426950408889634f;
 
     const int ntiles = (S + KT - 1) / KT;
     // Direct global -> LDS through buffer loads, one wave instruction = 1 KB:
@@ -178,9 +174,9 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 #pragma unroll
         for (int j = 0; j < 2; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     rsum[0] = rsum[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // running maximum (base-2 units) per query; the score MFMAs start from
-    // -mb, so the scores arrive with it already subtracted.  mb = 0 and
-    // started = false until the first tile has set it.
+    // running maximum (base-2 units) per query, subtracted from the scaled
+    // scores in the softmax.  mb = 0 and started = false until the first
+    // tile has set it.
     float mb[2] = {0.f, 0.f};
     bool started = false;
     const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
@@ -193,8 +189,8 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 
     // ---- the matrix phase: O^T += V^T P^T and the row sums of tile tv (two
     // 32-key steps; its first V^T fragments are already in fa), then
-    // S^T = K Q^T of tile tk (64 keys x 32 queries; s[tk][tq][r] holds
-    // x = score * log2(e)/sqrt(128) - mb for key 32*(tk/2) + 8g + 4*(tk%2) + r).
+    // S^T = K Q^T of tile tk (64 keys x 32 queries; s[tk][tq][r] holds the
+    // fp32 score q.k of key 32*(tk/2) + 8g + 4*(tk%2) + r).
     // The LDS reads go in quarters of 4 fragments, each issued two quarters
     // before the MFMAs that use it (at most 8 reads in flight).
     bf16x8 fa[8], fb[8];
@@ -227,12 +223,12 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
                 oacc[4 * h + u][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[u], pf[j][tq], oacc[4 * h + u][tq], 0, 0, 0);
     };
     auto qk4 = [&](const bf16x8 *f, int ks) {
-        const f32x4 init[2] = {f32x4{-mb[0], -mb[0], -mb[0], -mb[0]}, f32x4{-mb[1], -mb[1], -mb[1], -mb[1]}};
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int tk = 0; tk < 4; ++tk)
 #pragma unroll
             for (int tq = 0; tq < 2; ++tq)
-                s[tk][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[tk], qf[tq][ks], ks == 0 ? init[tq] : s[tk][tq], 0, 0, 0);
+                s[tk][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[tk], qf[tq][ks], ks == 0 ? zero : s[tk][tq], 0, 0, 0);
     };
     // tv = -1 (the first matrix phase) reads V^T buffer NVB-1, which is
     // zeroed before the loop, with P = 0; tk = ntiles (the last) computes
@@ -252,12 +248,21 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 #undef DIT_STEP
     };
 
-    // ---- online softmax of tile t: common case, the tile's maximum of x is
-    // <= 2^8 above the running maximum and p = 2^x needs no subtraction.
-    // Otherwise (and for the first tile) the maximum moves up by the tile's
-    // max m: the partial output and sums are scaled by 2^-m and p = 2^(x - m).
+    // ---- online softmax of tile t: x = s * sc - mb (one fma each).  Common
+    // case: the tile's maximum of x is <= 2^8 above the running maximum and
+    // p = 2^x needs no further subtraction.  Otherwise the maximum moves up
+    // by the tile's max m (never down: m >= 0 once started) and the partial
+    // output and sums are scaled by 2^-m <= 1, p = 2^(x - m).  The first
+    // tile sets the maximum to its own (any value); the partial results are
+    // still zero then and are not scaled.
     auto softmax = [&](int t) {
         const int kv0 = t * KT;
+#pragma unroll
+        for (int tk = 0; tk < 4; ++tk)
+#pragma unroll
+            for (int tq = 0; tq < 2; ++tq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s[tk][tq][r] = __builtin_fmaf(s[tk][tq][r], sc, -mb[tq]);
         if (kv0 + KT > S) {
 #pragma unroll
             for (int tk = 0; tk < 4; ++tk)
@@ -282,11 +287,13 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
             for (int tq = 0; tq < 2; ++tq) {
-                const float m = mt[tq];
-                const float alpha = __builtin_amdgcn_exp2f(-m);
+                const float m = started ? fmaxf(mt[tq], 0.f) : mt[tq];
+                if (started) {
+                    const float alpha = __builtin_amdgcn_exp2f(-m);
 #pragma unroll
-                for (int dd = 0; dd < 8; ++dd) oacc[dd][tq] *= alpha;
-                rsum[tq] *= alpha;
+                    for (int dd = 0; dd < 8; ++dd) oacc[dd][tq] *= alpha;
+                    rsum[tq] *= alpha;
+                }
                 mb[tq] += m;
 #pragma unroll
                 for (int tk = 0; tk < 4; ++tk) s[tk][tq] -= m;

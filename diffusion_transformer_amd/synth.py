@@ -232,12 +232,15 @@ def normal(shape, seed: int, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
     return (rng.standard_normal(shape, dtype=np.float32) * np.float32(std) + np.float32(mean)).astype(np.float32)
 
 
-def rows_sample(S: int, count: int, L: int = 0, seed: int = 123) -> np.ndarray:
+def rows_sample(S: int, count: int, L: int = 0, seed: int = 123, tile: int = 256) -> np.ndarray:
     """Sorted distinct row indexes for sampled checks: the first and last
-    text and image rows plus `count` random ones."""
+    text and image rows, one random row inside every `tile` consecutive rows
+    (so no block of rows goes unchecked), plus `count` random ones."""
     rng = np.random.default_rng(seed)
     pick = {0, S - 1}
     if L > 0:
         pick.update({L - 1, L})
+    for t0 in range(0, S, tile):
+        pick.add(int(rng.integers(t0, min(S, t0 + tile))))
     pick.update(rng.choice(S, size=min(count, S), replace=False).tolist())
     return np.array(sorted(pick), dtype=np.int64)

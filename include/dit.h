@@ -196,9 +196,7 @@ dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint
  * 1000) / 1000, every step one rounded fp32 operation; sigmas[n] = 0 (the
  * grid holds n + 1 values, t n).  Step i runs dit_denoise_step with
  * sigma = sigmas[i] and sigma_next = sigmas[i+1]; that step's time input is
- * sigma, which on an unshifted grid equals t[i] bit for bit ([HC] s.6
- * states it for the 8-step grid); after a shift the two can differ in the
- * last bit.  DIT_EINVAL for NULL pointers, a shift
+ * t[i], computed from sigma the same way.  DIT_EINVAL for NULL pointers, a shift
  * that is not positive and finite or a sigma outside [0, 1]; DIT_ERANGE
  * for n outside 1..10000.  dit_last_error(NULL) holds the message. */
 dit_status dit_sigma_schedule(const float *sample_sigmas, int n, float shift, float *sigmas, float *t);
@@ -312,7 +310,8 @@ dit_status dit_double_block_forward(dit_ctx *ctx, const dit_block *txt, const di
 dit_status dit_prologue(dit_ctx *ctx, const dit_model *m, const float *ctx_feats, int L,
                         float *txt);
 
-/* One denoise step ([HC] s.6): t = sigma; vel = DiT(x_lat, txt, t) (image
+/* One denoise step ([HC] s.6): the DiT's time input t = (sigma * 1000) /
+ * 1000 (two fp32 operations, as dit_sigma_schedule's t); vel = DiT(x_lat, txt, t) (image
  * rows x_lat*w_in^T after the text rows txt, every block, the final
  * modulated LayerNorm of the image rows with (shift, scale) = w_fmod *
  * silu(vec), then w_final); x_lat += (sigma_next - sigma) * vel in fp32.

@@ -8,9 +8,12 @@ constant generators, no pre- or post-processing.
 Every function is the plain definition of one step, written in NumPy float64
 unless a page fixes another precision (the rotary tables and the Euler update
 are float32 there).  Inputs are whatever values the caller passes (normally
-bf16-representable numbers drawn by the seeded generators); nothing here
-rounds to bf16 -- the oracle computes the exact-as-possible result the GPU
-path approximates.
+bf16-representable numbers drawn by the seeded generators).  The one place
+the oracle rounds to bf16 is where a page puts a rounding into the method
+itself: an int8 block-32 weight is the exact product code * scale, handed to
+the bf16 products as that product rounded to the nearest bf16
+(`dequant_int8_b32_bf16`); everything else is the exact-as-possible result
+the GPU path approximates.
 
 Sources (web pages; cited by title and section):
   [HC]  "Host contract -- RGBA-Image-2.1-Turbo (Core AI port of
@@ -658,6 +661,26 @@ def double_block_forward(x, bw_txt: BlockWeights, bw_img: BlockWeights, vec, cos
 # [HC] s.1 int8lin weights: one bf16 scale per block of 32
 # ---------------------------------------------------------------------------
 
+def bf16_rne(x) -> np.ndarray:
+    """The bf16 value nearest to each float32 value of x, ties to the even
+    significand (round to nearest even).  Written as the choice between the
+    two bf16 neighbours of x -- its float32 bit pattern with the low 16 bits
+    cleared, and the next bf16 away from zero -- whichever is nearer, the
+    one with an even last significand bit on a tie.  Finite inputs.
+    Returns float32."""
+    x = np.asarray(x, F32)
+    u = x.view(np.uint32)
+    lo_bits = u & np.uint32(0xFFFF0000)
+    hi_bits = lo_bits + np.uint32(0x10000)
+    lo = lo_bits.view(F32).astype(F64)
+    hi = hi_bits.view(F32).astype(F64)
+    xv = x.astype(F64)
+    d_lo, d_hi = np.abs(xv - lo), np.abs(hi - xv)
+    lo_even = ((lo_bits >> np.uint32(16)) & np.uint32(1)) == 0
+    take_lo = (d_lo < d_hi) | ((d_lo == d_hi) & lo_even)
+    return np.where(take_lo, lo, hi).astype(F32)
+
+
 def dequant_int8_b32(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     """W[o, k] = q[o, k] * s[o, k // 32] ([HC] s.1: symmetric int8, one scale
     per block of 32 along the input axis).  With |q| <= 127 (7 bits) and a
@@ -669,6 +692,16 @@ def dequant_int8_b32(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     out, inn = q.shape
     assert inn % 32 == 0 and s.shape == (out, inn // 32)
     return q.astype(F32) * np.repeat(s, 32, axis=1)
+
+
+def dequant_int8_b32_bf16(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """The int8 block-32 weight as the bf16 products take it: the exact
+    product q * s rounded to the nearest bf16, ties to even.  [HC] s.1 has
+    the int8 weights dequantised inside the graph and the products computed
+    in bf16; the exact fp32 product needs up to 15 significant bits, so a
+    bf16 operand is its rounding (the reading taken is round to nearest
+    even).  Returns float32 [out, in] of bf16 values."""
+    return bf16_rne(dequant_int8_b32(q, s))
 
 
 # ---------------------------------------------------------------------------
@@ -745,15 +778,17 @@ def velocity(x_lat, txt, mw: ModelWeights, cos, sin, t, arch: Arch):
 
 def denoise(x_lat, ctx_feats, mw: ModelWeights, cos, sin, sigmas, arch: Arch,
             keep_velocities: bool = False):
-    """The few-step Euler flow-matching loop ([HC] s.6): for each i,
-    t = sigma_i, vel = DiT(x, t), x = x + (sigma_{i+1} - sigma_i) vel in fp32.
+    """The few-step Euler flow-matching loop ([HC] s.6): for each i, the
+    DiT's time input t = (sigma_i * 1000) / 1000 (the timestep, divided again,
+    in fp32), vel = DiT(x, t), x = x + (sigma_{i+1} - sigma_i) vel in fp32.
     The DiT's velocity is handed to the fp32 update as fp32 (its graph
     boundary is fp32, [HC] s.1)."""
     txt = text_rows(ctx_feats, mw)
     x = np.asarray(x_lat, F32)
     vels = []
     for i in range(len(sigmas) - 1):
-        vel = velocity(x, txt, mw, cos, sin, float(sigmas[i]), arch).astype(F32)
+        t = (F32(sigmas[i]) * F32(1000)) / F32(1000)
+        vel = velocity(x, txt, mw, cos, sin, float(t), arch).astype(F32)
         vels.append(vel)
         x = euler_step(x, vel, sigmas[i], sigmas[i + 1])
     return (x, vels) if keep_velocities else x

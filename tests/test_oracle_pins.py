@@ -281,6 +281,77 @@ def test_dequant_exact_and_block_index():
     assert O.dequant_int8_b32(np.full((1, 32), -127, np.int8), np.full((1, 1), 0.0390625, np.float32))[0, 0] == np.float32(-4.9609375)
 
 
+def _bf16_nearest_brute(x):
+    """Nearest bf16 value of each float32 x by search over every finite
+    bf16 value (all 2^16 bit patterns, sorted), ties to the even bit
+    pattern: an independent statement of round to nearest even."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    keep = np.isfinite(vals) & ~((vals == 0) & (bits != 0))      # one zero
+    vals, bits = vals[keep].astype(np.float64), bits[keep]
+    order = np.argsort(vals, kind="stable")
+    vals, bits = vals[order], bits[order]
+    out = np.empty(len(x), np.float64)
+    for i, v in enumerate(np.asarray(x, np.float64)):
+        j = np.searchsorted(vals, v)
+        cand = [c for c in (j - 1, j) if 0 <= c < len(vals)]
+        d = [abs(vals[c] - v) for c in cand]
+        best = [c for c, dd in zip(cand, d) if dd == min(d)]
+        if len(best) == 2:                              # a tie: the even pattern
+            best = [c for c in best if bits[c] % 2 == 0]
+        out[i] = vals[best[0]]
+    return out
+
+
+def test_bf16_rne_worked_ties():
+    one = np.float32(1.0)
+    t = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), -(1 + 3 * 2 ** -8), 1 + 2 ** -8 + 2 ** -20,
+                  2 ** -130, 0.0], np.float32)
+    want = [1.0, 1 + 2 ** -6, -1.0, -(1 + 2 ** -6), 1 + 2 ** -7, 2 ** -130, 0.0]
+    assert O.bf16_rne(t).astype(np.float64).tolist() == want
+    assert O.bf16_rne(one) == one
+
+
+def test_bf16_rne_is_the_nearest_bf16():
+    rng = np.random.default_rng(41)
+    x = np.concatenate([rng.standard_normal(3000).astype(np.float32) * np.float32(3.0),
+                        (rng.integers(-127, 128, 3000) * synth.bf16_round(np.abs(rng.standard_normal(3000)) * 0.01)
+                         ).astype(np.float32),
+                        np.float32(1.0) + np.arange(-64, 64, dtype=np.float32) * np.float32(2 ** -9)])
+    got = O.bf16_rne(x)
+    assert (got.astype(np.float64) == _bf16_nearest_brute(x)).all()
+    assert (got.view(np.uint32) & 0xFFFF == 0).all()
+    assert (np.abs(got.astype(np.float64) - x) <= np.abs(x.astype(np.float64)) * 2 ** -8).all()
+
+
+def test_dequant_bf16_is_the_rounded_exact_product():
+    rng = np.random.default_rng(42)
+    q, s = synth.int8_weight(rng, 32, 256)
+    exact = O.dequant_int8_b32(q, s)
+    w = O.dequant_int8_b32_bf16(q, s)
+    assert (w.astype(np.float64) == _bf16_nearest_brute(exact.reshape(-1)).reshape(w.shape)).all()
+    # products that are already bf16 values (a power-of-two scale) stay exact
+    q2 = rng.integers(-127, 128, (4, 64)).astype(np.int8)
+    s2 = np.full((4, 2), 0.25, np.float32)
+    assert (O.dequant_int8_b32_bf16(q2, s2) == O.dequant_int8_b32(q2, s2)).all()
+    # 127 * 0.0390625 = 4.9609375 needs 12 significant bits: its bf16 is 4.96875
+    assert O.dequant_int8_b32_bf16(np.full((1, 32), 127, np.int8), np.full((1, 1), 0.0390625, np.float32))[0, 0] \
+        == np.float32(4.96875)
+
+
+@pytest.mark.parametrize("bad", ["truncate", "ties_away"])
+def test_pins_catch_bf16_rounding_mistakes(bad):
+    rng = np.random.default_rng(43)
+    x = np.concatenate([rng.standard_normal(500).astype(np.float32),
+                        np.float32(1.0) + np.arange(-16, 16, dtype=np.float32) * np.float32(2 ** -8)])
+    u = x.view(np.uint32)
+    if bad == "truncate":
+        wrong = (u & np.uint32(0xFFFF0000)).view(np.float32)
+    else:
+        wrong = ((u + np.uint32(0x8000)) & np.uint32(0xFFFF0000)).view(np.float32)
+    assert not (wrong.astype(np.float64) == _bf16_nearest_brute(x)).all()
+
+
 # ---------------------------------------------------------------- Euler
 
 def test_sigma_grid_and_euler_telescopes():
