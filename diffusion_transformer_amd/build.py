@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdit.so")
 
-SOURCES = ["dit_api.cpp", "k_misc.hip", "k_gemm.hip", "k_attn.hip"]
+SOURCES = ["dit_api.cpp", "k_misc.hip", "k_gemm.hip", "k_attn.hip", "dit_noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -88,6 +88,14 @@ dit_status check_launch(dit_ctx *c, hipError_t e, const char *what) {
     return DIT_OK;
 }
 
+}  // namespace
+
+// The last-error text of calls that take no context (dit_last_error(NULL)),
+// for the entry points defined in other sources of the library.
+void dit_set_global_error(const char *msg) { g_err = msg; }
+
+namespace {
+
 #define DIT_TRY(expr)                      \
     do {                                   \
         dit_status _s = (expr);            \

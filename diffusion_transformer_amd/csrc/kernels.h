@@ -110,3 +110,6 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
                             int S, int ldv, uint16_t *o, int ldo, hipStream_t st, int Sq = -1);
 
 }  // namespace dit
+
+// Sets the text dit_last_error(NULL) returns (dit_api.cpp).
+void dit_set_global_error(const char *msg);

@@ -70,6 +70,7 @@ _SIGS = {
     "dit_positions": (C.c_int, [_P, C.c_int, C.c_int, C.c_int, _P]),
     "dit_rope_tables": (C.c_int, [_P, _P, C.c_int, _P, _P]),
     "dit_time_vector": (C.c_int, [_P, _P, _P, C.c_float, _P]),
+    "dit_time_vector_noalloc": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, C.c_float, _P]),
     "dit_modulation": (C.c_int, [_P, _P, C.c_int, _P, _P]),
     "dit_modulated_norm": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_float, _P]),
     "dit_linear": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, _P]),
@@ -160,6 +161,15 @@ def _ptr(t, dtype=None, name="tensor"):
 
 def _stream():
     return torch.cuda.current_stream().cuda_stream
+
+
+def time_vector_noalloc(hidden, time_dim, w_t1, w_t2, t, vec):
+    """dit_time_vector_noalloc on torch's current device and stream (no
+    context; the library allocates nothing)."""
+    st = _lib.dit_time_vector_noalloc(_stream(), int(hidden), int(time_dim), _ptr(w_t1, torch.bfloat16, "w_t1"),
+                                      _ptr(w_t2, torch.bfloat16, "w_t2"), float(t), _ptr(vec, torch.float32, "vec"))
+    if st != OK:
+        raise DitError(st, last_error(None))
 
 
 class Context:

@@ -170,6 +170,26 @@ dit_status dit_rope_tables(dit_ctx *ctx, const int32_t *pos, int S, float *cos, 
 dit_status dit_time_vector(dit_ctx *ctx, const uint16_t *w_t1, const uint16_t *w_t2, float t,
                            float *vec);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * conditioning vector of dit_time_vector with no context.  Same kernels
+ * and result as dit_time_vector (bit for bit) for an arch with these hidden
+ * and time_dim, on the calling thread's current device, enqueued on
+ * `stream` (a hipStream_t of that device; NULL = its null stream).
+ * w_t1 bf16 [hidden, time_dim], w_t2 bf16 [hidden, hidden], vec fp32
+ * [hidden] output, all caller-owned device memory.  The two intermediate
+ * rows live in a fixed device array of the library, 2 * 4096 floats per
+ * device (held until the process ends): hidden and time_dim must each be a
+ * multiple of 8 in 8..4096, else DIT_ERANGE.  Nothing in it must start at
+ * zero.  Calls that overlap on one device (other streams, other threads)
+ * race on that array; order them.  The first call on a device looks the
+ * array's address up (hipGetSymbolAddress) and keeps it: make that call
+ * before capturing.  Allocates nothing.  Errors: DIT_EINVAL (NULL pointer),
+ * DIT_ERANGE, DIT_EDEVICE (no current device, lookup or launch failed);
+ * message in dit_last_error(NULL). */
+dit_status dit_time_vector_noalloc(void *stream, int hidden, int time_dim, const uint16_t *w_t1,
+                                   const uint16_t *w_t2, float t, float *vec);
+
 /* Modulation GEMV ([GZ] Modulation): mod = w_mod * silu(vec), w_mod bf16
  * [chunks*D, D], vec fp32 [D], mod fp32 [chunks*D].  chunks in 1..6. */
 dit_status dit_modulation(dit_ctx *ctx, const uint16_t *w_mod, int chunks, const float *vec,
