@@ -340,11 +340,13 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
                    "norm1");
     }
     // one launch per product for both streams (image tiles first) when both
-    // take the ping-pong kernel; int8 weights of either stream: two launches
-    const bool w8 = bt->wtype == DIT_W_INT8_B32 || bi->wtype == DIT_W_INT8_B32;
+    // take the ping-pong kernel with the same weight type; streams with
+    // different weight types: two launches
+    const bool mixed = bt->wtype != bi->wtype;
+    const bool w8 = bi->wtype == DIT_W_INT8_B32;
     auto two = [&](int kind, const uint16_t *a_base, int64_t a_ld, const GemmEpi (&ep)[2], int w, int n, int k) {
         const Stream &ti = sts[1], &tt = sts[0];
-        if (w8) {
+        if (mixed) {
             hipError_t e = hipSuccess;
             for (int i = 1; i >= 0 && e == hipSuccess; --i) {
                 const Stream &t = sts[i];
@@ -355,8 +357,8 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
             return e;
         }
         (void)kind;
-        return launch_gemm2(a_base + int64_t(ti.r0) * a_ld, ti.b->w[w], nullptr, ti.rows, ep[1],
-                            a_base + int64_t(tt.r0) * a_ld, tt.b->w[w], nullptr, tt.rows, ep[0], false, n, k, st);
+        return launch_gemm2(a_base + int64_t(ti.r0) * a_ld, ti.b->w[w], bscale(ti.b, w), ti.rows, ep[1],
+                            a_base + int64_t(tt.r0) * a_ld, tt.b->w[w], bscale(tt.b, w), tt.rows, ep[0], w8, n, k, st);
     };
     {
         GemmEpi e[2]{};

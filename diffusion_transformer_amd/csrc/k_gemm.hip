@@ -390,6 +390,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm7() { asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 }  // namespace
 
@@ -596,11 +598,30 @@ __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // fragments take K in the same order, so the dot products are those of the
 // rows), and the int32 sums are scaled by ep.a_scale[row] * ep.w_scale[col]
 // before the epilogue.  Everything else is the bf16 kernel's.
-template <int EPI, bool KS, bool I8 = false>
+//
+// B32: int8 weights with one bf16 scale per 32 inputs ("Host contract --
+// RGBA-Image-2.1-Turbo" s.1, int8 weights dequantised inside the graph,
+// products in bf16), dequantised into LDS.  W reaches the chip as int8 (half
+// the bytes of bf16): each wave moves its share of a k-tile's codes and their
+// scales into a staging area of its own (buffer loads into LDS, one memory
+// phase ahead), and at the start of its next memory phase each lane turns
+// exactly the 32 codes it loaded (one row, one block of 32) into bf16,
+// code * scale rounded to nearest even, written into the one bf16 W buffer
+// in the layout the fragment reads expect.  A group converts the W half the
+// other group reads, in the phase just before that read:
+//   phase 2t   : group 1 converts half 0 of k-tile t+1 (read by group 0 in 2t+1)
+//   phase 2t+1 : group 0 converts half 1 of k-tile t+1 (read by group 1 in 2t+2)
+// so a single bf16 W buffer suffices (the half being written was last read
+// the phase before).  The product code * scale is exact: with the code's
+// sign bit flipped, u = code + 128 in 1..255 converts exactly, and
+// u * s - 128 * s is (code) * s, at most 15 significant bits.  LDS: three A
+// buffers (96 KB), one W buffer (32 KB), codes (16 KB) and scales (2 KB).
+template <int EPI, bool KS, bool I8 = false, bool B32 = false>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M, int N, int K,
           GemmEpi ep, const uint16_t *__restrict__ A2, const uint16_t *__restrict__ W2, int M2, GemmEpi ep2) {
     static_assert(!(KS && I8), "the k-split form is bf16 only");
+    static_assert(!(B32 && (KS || I8)), "the block-32 form is a plain one-weight product");
     constexpr int BM = PP_BM, BN = PP_BN;
     constexpr uint32_t ESZ = I8 ? 1 : 2;          // bytes per element
     constexpr int BKE = 128 / ESZ;                // elements per 128-byte k-tile row
@@ -717,14 +738,14 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     };
     // fragments of k-tile kt only (prologue)
     auto load_frags = [&](int kt) {
-        const u32x4 *La = Abuf + (kt % 3) * P3_BUF, *Lw = Wbuf + (kt & 1) * P3_BUF;
+        const u32x4 *La = Abuf + (kt % 3) * P3_BUF, *Lw = Wbuf + (B32 ? 0 : (kt & 1)) * P3_BUF;
 #pragma unroll
         for (int f = 0; f < 24; ++f) frag(La, Lw, f);
     };
     // memory phase: fragments of k-tile kt, with W loads 0-3 of k-tile kw
     // and A loads 0-3 of k-tile ka in between
     auto memory = [&](int kt, int kw, int ka) {
-        const u32x4 *La = Abuf + (kt % 3) * P3_BUF, *Lw = Wbuf + (kt & 1) * P3_BUF;
+        const u32x4 *La = Abuf + (kt % 3) * P3_BUF, *Lw = Wbuf + (B32 ? 0 : (kt & 1)) * P3_BUF;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
 #pragma unroll
@@ -732,6 +753,98 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
             __builtin_amdgcn_sched_barrier(0);
             if (r < 4) issue_w(kw, r);
             else issue_a(ka, r - 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- B32 staging.  Wave (grp, wg) stages rows rr = 32wg + j, j < 32, of
+    // the W half ah = grp^1: load i (0, 1) moves rows j = 2m + i, m < 16, four
+    // lanes to a row (lane l: m = l>>2, bytes 16(l&3) of the row's 64 codes
+    // of the k-tile), so each 1 KB load reads 16 contiguous 64-byte row
+    // pieces; one dword load brings every row's two block scales (lanes 2j,
+    // 2j+1: row j).  Lane l later converts exactly the 32 codes it loaded:
+    // 16 of row 2m (chunks 2(l&3), 2(l&3)+1, block (l&3)>>1) and the same 16
+    // of row 2m + 1, into W slots 128ah + 64i + 16wg + m (even rows first,
+    // then odd rows, as the fragment reads expect; 16 consecutive lanes of a
+    // chunk write 4 consecutive 128-byte slots at 4 chunk positions each).
+    u32x4 *const Wst = lds + 4 * P3_BUF + (grp * 4 + wg) * 128;                    // codes: 2 x 64 chunks
+    uint32_t *const Sst = reinterpret_cast<uint32_t *>(lds + 4 * P3_BUF + 8 * 128) + (grp * 4 + wg) * 64;
+    const int b_m = lane >> 2, b_q = lane & 3;
+    __amdgpu_buffer_rsrc_t rW8 = rW, rS = rW;
+    uint32_t w8_off = 0, s_off = 0;
+    if constexpr (B32) {
+        // descriptors end at the weight's (and scales') last row: nothing
+        // past them is ever read
+        const int64_t rem = static_cast<int64_t>(N - n0);
+        const int64_t wb = rem * K, sb = rem * (K / 32) * 2;
+        rW8 = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(reinterpret_cast<const char *>(W) + static_cast<int64_t>(n0) * K),
+                                                static_cast<short>(0), static_cast<int>(wb < 0x7fffffff ? wb : 0x7fffffff),
+                                                0x00020000);
+        rS = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(ep.w_bscale + static_cast<int64_t>(n0) * (K / 32)),
+                                               static_cast<short>(0), static_cast<int>(sb < 0x7fffffff ? sb : 0x7fffffff),
+                                               0x00020000);
+        w8_off = static_cast<uint32_t>((128 * ah + 32 * wg + 2 * b_m) * K + 16 * b_q);
+        s_off = static_cast<uint32_t>((128 * ah + 32 * wg + (lane >> 1)) * (K / 32) * 2);
+    }
+    // codes and scales of k-tile kt (clamped past the last: those land in a
+    // staging area nobody converts any more; every memory phase issues the
+    // same three loads, codes first)
+    auto issue_stage = [&](int kt) {
+        const uint32_t ks = static_cast<uint32_t>(min(kt, T - 1));
+        bdma16(rW8, w8_off, 64u * ks, Wst);
+        bdma16(rW8, w8_off + static_cast<uint32_t>(K), 64u * ks, Wst + 64);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void_t *)Sst, 4, s_off, 4u * ks, 0, 0);
+    };
+    // chunk h (0, 1) of this lane's 16 codes of row 2m + i: the two dwords
+    // w0, w1 holding them, times the row's scale sd (block b_q >> 1) -> bf16
+    u32x4 *const b_dst = Wbuf + (128 * ah + 16 * wg + b_m) * 8;
+    auto convert_chunk = [&](uint32_t w0, uint32_t w1, uint32_t sd, int i, int h) {
+        const float sc = (b_q >> 1) ? bf16hi_to_f32(sd) : bf16lo_to_f32(sd);
+        const float msc = -128.0f * sc;
+        w0 ^= 0x80808080u;
+        w1 ^= 0x80808080u;
+        auto dq = [&](uint32_t w, int b) {   // (byte b of w) - 128, times the scale: exact
+            return __builtin_fmaf(static_cast<float>((w >> (8 * b)) & 0xffu), sc, msc);
+        };
+        const int slot = 128 * ah + 64 * i + 16 * wg + b_m;
+        b_dst[64 * i * 8 + ((2 * b_q + h) ^ ((slot >> 1) & 7))] =
+            u32x4{pack_bf16x2(dq(w0, 0), dq(w0, 1)), pack_bf16x2(dq(w0, 2), dq(w0, 3)),
+                  pack_bf16x2(dq(w1, 0), dq(w1, 1)), pack_bf16x2(dq(w1, 2), dq(w1, 3))};
+    };
+    auto convert = [&]() {
+        const u32x4 c0 = Wst[lane], c1 = Wst[64 + lane];
+        const uint32_t s0 = Sst[4 * b_m], s1 = Sst[4 * b_m + 2];
+        convert_chunk(c0[0], c0[1], s0, 0, 0);
+        convert_chunk(c0[2], c0[3], s0, 0, 1);
+        convert_chunk(c1[0], c1[1], s1, 1, 0);
+        convert_chunk(c1[2], c1[3], s1, 1, 1);
+    };
+    // B32 memory phase: the staged codes of k-tile kc (loaded at the start of
+    // this wave's previous memory phase, before its 4 A loads) are read
+    // first and converted a chunk at a time between the fragment reads of
+    // k-tile kt; once they are consumed the codes of k-tile kc + 1 are
+    // staged, then the A loads of k-tile ka go out between the remaining
+    // reads.  Nothing is converted past the last k-tile.
+    auto memory_b32 = [&](int kt, int kc, int ka) {
+        wait_vm4();
+        const u32x4 *La = Abuf + (kt % 3) * P3_BUF, *Lw = Wbuf;
+        const u32x4 c0 = Wst[lane], c1 = Wst[64 + lane];
+        const uint32_t s0 = Sst[4 * b_m], s1 = Sst[4 * b_m + 2];
+        const bool conv = kc < T;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) frag(La, Lw, 3 * r + q);
+            __builtin_amdgcn_sched_barrier(0);
+            if (r < 4) {
+                if (conv) {
+                    const u32x4 &c = r < 2 ? c0 : c1;
+                    convert_chunk(c[2 * (r & 1)], c[2 * (r & 1) + 1], r < 2 ? s0 : s1, r >> 1, r & 1);
+                }
+                if (r == 3) issue_stage(kc + 1);   // after the last use of the staged codes
+            } else {
+                issue_a(ka, r - 4);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -756,17 +869,27 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
     };
 
     // prologue: k-tiles 0 and 1 whole, and A rows 128-255 of k-tile 2 (group
-    // 0's load of the phase before the first); all land before the first read
+    // 0's load of the phase before the first); all land before the first read.
+    // B32: the codes of k-tile 0 are converted here (each group its half
+    // grp^1) and those of k-tile 1 staged.
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             issue_a(kt, i);
-            issue_w(kt, i);
+            if constexpr (!B32) issue_w(kt, i);
         }
     if (grp == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) issue_a(2, i);
+    }
+    if constexpr (B32) {
+        issue_stage(0);
+        wait_vm0();
+        convert();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkm0();
+        issue_stage(1);
     }
     wait_vm0();
     pp_barrier();
@@ -790,18 +913,30 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
             compute();
             __builtin_amdgcn_sched_barrier(0);
         } else {
-            memory(t, t + 2, t + 2);
-            wait_lgkm0();
-            wait_vm8();
+            if constexpr (B32) {
+                memory_b32(t, t + 1, t + 2);
+                wait_lgkm0();
+                wait_vm7();
+            } else {
+                memory(t, t + 2, t + 2);
+                wait_lgkm0();
+                wait_vm8();
+            }
         }
         pp_barrier();
         // phase 2t+1: group 0 reads its fragments of t+1 and loads W half 1
         // of t+2 and A rows 128-255 of t+3; group 1 computes t
         if (grp == 0) {
             if (t + 1 < T) {
-                memory(t + 1, t + 2, t + 3);
-                wait_lgkm0();
-                wait_vm8();
+                if constexpr (B32) {
+                    memory_b32(t + 1, t + 1, t + 3);
+                    wait_lgkm0();
+                    wait_vm7();
+                } else {
+                    memory(t + 1, t + 2, t + 3);
+                    wait_lgkm0();
+                    wait_vm8();
+                }
             }
         } else {
             compute();
@@ -864,20 +999,20 @@ static hipError_t launch_cfg(const uint16_t *A, const void *W, const uint16_t *W
     return hipGetLastError();
 }
 
-template <int EPI, bool KS = false, bool I8 = false>
+template <int EPI, bool KS = false, bool I8 = false, bool B32 = false>
 static hipError_t launch_pp(const uint16_t *A, const uint16_t *W, int M, int N, int K, const GemmEpi &ep,
                             hipStream_t st) {
     const int grid = static_cast<int>(cdiv(M, PP_BM) * cdiv(N, PP_BN));
-    k_gemm_p3<EPI, KS, I8><<<grid, 512, 0, st>>>(A, W, M, N, K, ep, nullptr, nullptr, 0, ep);
+    k_gemm_p3<EPI, KS, I8, B32><<<grid, 512, 0, st>>>(A, W, M, N, K, ep, nullptr, nullptr, 0, ep);
     return hipGetLastError();
 }
 
 // Two products of one epilogue kind, same N and K, in one ping-pong launch.
-template <int EPI>
+template <int EPI, bool B32 = false>
 static hipError_t launch_pp2(const uint16_t *A, const uint16_t *W, int M, const GemmEpi &ep, const uint16_t *A2,
                              const uint16_t *W2, int M2, const GemmEpi &ep2, int N, int K, hipStream_t st) {
     const int grid = static_cast<int>((cdiv(M, PP_BM) + cdiv(M2, PP_BM)) * cdiv(N, PP_BN));
-    k_gemm_p3<EPI, false><<<grid, 512, 0, st>>>(A, W, M, N, K, ep, A2, W2, M2, ep2);
+    k_gemm_p3<EPI, false, false, B32><<<grid, 512, 0, st>>>(A, W, M, N, K, ep, A2, W2, M2, ep2);
     return hipGetLastError();
 }
 
@@ -909,7 +1044,9 @@ bool gemm_pingpong_ok(int M, int N, int K, bool w8, const GemmEpi &ep, bool a_ro
     if (ep.k_split > 0)
         epi_ok = epi_ok && ep.kind == EPI_GATE_RES && ep.w2 && ep.k_split % BK == 0 && ep.k_split >= 128 &&
                  K - ep.k_split >= 128;
-    return big_tiles >= 128 && !w8 && epi_ok && K >= 128 && N % 256 == 0 && (a_rows_padded || M % 256 == 0);
+    // int8 block-32 weights: the plain one-weight products
+    if (w8) epi_ok = epi_ok && ep.kind != EPI_QKV_SWIGLU && ep.k_split == 0;
+    return big_tiles >= 128 && epi_ok && K >= 128 && N % 256 == 0 && (a_rows_padded || M % 256 == 0);
 }
 
 hipError_t launch_gemm2(const uint16_t *A, const void *W, const uint16_t *Ws, int M, const GemmEpi &ep,
@@ -925,6 +1062,18 @@ hipError_t launch_gemm2(const uint16_t *A, const void *W, const uint16_t *Ws, in
         return e;
     }
     const uint16_t *Wb = static_cast<const uint16_t *>(W), *Wb2 = static_cast<const uint16_t *>(W2);
+    if (w8) {
+        GemmEpi e1 = ep, e2 = ep2;
+        e1.w_bscale = Ws;
+        e2.w_bscale = Ws2;
+        switch (ep.kind) {
+            case EPI_F32: return launch_pp2<EPI_F32, true>(A, Wb, M, e1, A2, Wb2, M2, e2, N, K, st);
+            case EPI_GATE_RES: return launch_pp2<EPI_GATE_RES, true>(A, Wb, M, e1, A2, Wb2, M2, e2, N, K, st);
+            case EPI_SWIGLU: return launch_pp2<EPI_SWIGLU, true>(A, Wb, M, e1, A2, Wb2, M2, e2, N, K, st);
+            case EPI_QKV: return launch_pp2<EPI_QKV, true>(A, Wb, M, e1, A2, Wb2, M2, e2, N, K, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (ep.kind) {
         case EPI_F32: return launch_pp2<EPI_F32>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
         case EPI_GATE_RES: return launch_pp2<EPI_GATE_RES>(A, Wb, M, ep, A2, Wb2, M2, ep2, N, K, st);
@@ -958,6 +1107,17 @@ hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Ws, boo
     if (M <= 0) return hipSuccess;
     if (gemm_pingpong_ok(M, N, K, w8, ep, a_rows_padded)) {
         const uint16_t *Wb = static_cast<const uint16_t *>(W);
+        if (w8) {
+            GemmEpi e = ep;
+            e.w_bscale = Ws;
+            switch (ep.kind) {
+                case EPI_F32: return launch_pp<EPI_F32, false, false, true>(A, Wb, M, N, K, e, st);
+                case EPI_GATE_RES: return launch_pp<EPI_GATE_RES, false, false, true>(A, Wb, M, N, K, e, st);
+                case EPI_SWIGLU: return launch_pp<EPI_SWIGLU, false, false, true>(A, Wb, M, N, K, e, st);
+                case EPI_QKV: return launch_pp<EPI_QKV, false, false, true>(A, Wb, M, N, K, e, st);
+                default: return hipErrorInvalidValue;
+            }
+        }
         if (ep.k_split > 0) return launch_pp<EPI_GATE_RES, true>(A, Wb, M, N, K, ep, st);
         switch (ep.kind) {
             case EPI_F32: return launch_pp<EPI_F32>(A, Wb, M, N, K, ep, st);

@@ -78,6 +78,9 @@ struct GemmEpi {
     // per output column
     const float *a_scale;
     const float *w_scale;
+    // int8 block-32 weights on the ping-pong kernel (launch_gemm sets it):
+    // the weight's bf16 scales [N, K/32]
+    const uint16_t *w_bscale;
 };
 
 // C = A[M,K] * W[N,K]^T, A bf16; W bf16 (w8 = false) or int8 with bf16

@@ -102,7 +102,8 @@ def test_modulated_norm(norm, rows, D):
 # --------------------------------------------------------------- products
 
 @pytest.mark.parametrize("M,N,K", [(72, 256, 256), (1088, 3072, 3072), (4608, 64, 3072), (4096, 3072, 64),
-                                   (333, 768, 1024), (1, 128, 128), (4608, 9216, 3072)])
+                                   (333, 768, 1024), (1, 128, 128), (4608, 9216, 3072), (4608, 2048, 128),
+                                   (4608, 3072, 12288)])
 @pytest.mark.parametrize("w8", [False, True])
 def test_linear(ctx_big, M, N, K, w8):
     say("linear", M, N, K, "int8" if w8 else "bf16")
