@@ -183,13 +183,15 @@ dit_status check_ctx(dit_ctx *c) {
 // sandwich block's post norms and W8A8 weights; the others reject them.
 dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bool sequential = false) {
     if (!b) return fail(c, DIT_EINVAL, "block is NULL");
-    if (b->wtype != DIT_W_BF16 && b->wtype != DIT_W_INT8_B32 && b->wtype != DIT_W_INT8_ROW)
+    if (b->wtype != DIT_W_BF16 && b->wtype != DIT_W_INT8_B32 && b->wtype != DIT_W_INT8_ROW &&
+        b->wtype != DIT_W_INT8_ROT)
         return fail(c, DIT_EINVAL, "unknown wtype %d", b->wtype);
-    if (b->wtype == DIT_W_INT8_ROW && !sequential)
+    const bool w8a8 = b->wtype == DIT_W_INT8_ROW || b->wtype == DIT_W_INT8_ROT;
+    if (w8a8 && !sequential)
         return fail(c, DIT_EINVAL, "W8A8 weights are taken by the sequential block forms only");
     // the SwiGLU rows of a W8A8 block are quantized one row per workgroup,
     // at most 16384 wide; refused here, before the attention half updates x
-    if (b->wtype == DIT_W_INT8_ROW && c->arch.ffn > 16384)
+    if (w8a8 && c->arch.ffn > 16384)
         return fail(c, DIT_EUNSUPPORTED, "W8A8 blocks take ffn up to 16384 (arch ffn %d)", c->arch.ffn);
     for (int i = 0; i < 4; ++i) {
         if (!b->w[i]) return fail(c, DIT_EINVAL, "block weight w[%d] is NULL", i);
@@ -473,10 +475,12 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
         DIT_LAUNCH(c, launch_gemv(b->w_mod, vecs + int64_t(r) * D, 6 * D, D, true, mod + int64_t(r) * 6 * D, st),
                    "modulation");
     }
-    // W8A8 (DIT_W_INT8_ROW): every product takes its A rows as INT8 codes
-    // and a scale a row in aq / as -- from the norms directly, from a
-    // quantization pass over o and a
-    const bool q8 = b->wtype == DIT_W_INT8_ROW;
+    // W8A8 (DIT_W_INT8_ROW, DIT_W_INT8_ROT): every product takes its A rows
+    // as INT8 codes and a scale a row in aq / as -- from the norms directly,
+    // from a quantization pass over o and a; with DIT_W_INT8_ROT each 256
+    // values of a row are rotated by the regular Hadamard of 256 first
+    const bool q8 = b->wtype == DIT_W_INT8_ROW || b->wtype == DIT_W_INT8_ROT;
+    const bool rot = b->wtype == DIT_W_INT8_ROT;
     auto norms = [&](const float *shift_of, int which, uint16_t *out, const float *nw) -> dit_status {
         for (int i = 0; i < n_runs; ++i) {
             const int f = runs[3 * i], e = runs[3 * i + 1], m = runs[3 * i + 2];
@@ -485,7 +489,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
             Stage t(c, which);
             if (q8)
                 DIT_LAUNCH(c, launch_modnorm_i8(x + int64_t(f) * D, e - f, D, sh, sc, nw, rms, A.eps,
-                                                c->aq + int64_t(f) * D, c->as + f, st),
+                                                c->aq + int64_t(f) * D, c->as + f, st, rot),
                            "norm");
             else
                 DIT_LAUNCH(c, launch_modnorm(x + int64_t(f) * D, e - f, D, sh, sc, nw, rms, A.eps, out + int64_t(f) * D, st),
@@ -508,7 +512,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
                      const float *post) -> dit_status {
         if (q8) {
             Stage t(c, DIT_ST_QUANT);
-            DIT_LAUNCH(c, launch_quant_rows(a_base, S, K, c->aq, c->as, st), "quantize rows");
+            DIT_LAUNCH(c, launch_quant_rows(a_base, S, K, c->aq, c->as, st, rot), "quantize rows");
         }
         if (post) {
             GemmEpi f{};
@@ -868,6 +872,16 @@ dit_status dit_quantize_rows(dit_ctx *ctx, const uint16_t *x, int rows, int K, i
     if (K < 8 || K % 8 || K > 16384) return fail(ctx, DIT_EINVAL, "K %d: must be a multiple of 8 in 8..16384", K);
     DIT_TRY(check_ctx(ctx));
     DIT_LAUNCH(ctx, launch_quant_rows(x, rows, K, q, s, ctx->stream), "quantize rows");
+    return DIT_OK;
+}
+
+dit_status dit_convrot_quantize_rows(dit_ctx *ctx, const uint16_t *x, int rows, int K, int8_t *q, float *s) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!x || !q || !s) return fail(ctx, DIT_EINVAL, "x, q or s is NULL");
+    if (rows < 1) return fail(ctx, DIT_ERANGE, "rows %d < 1", rows);
+    if (K < 256 || K % 256 || K > 16384) return fail(ctx, DIT_EINVAL, "K %d: must be a multiple of 256 in 256..16384", K);
+    DIT_TRY(check_ctx(ctx));
+    DIT_LAUNCH(ctx, launch_quant_rows(x, rows, K, q, s, ctx->stream, true), "convrot quantize rows");
     return DIT_OK;
 }
 

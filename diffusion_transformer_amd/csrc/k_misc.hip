@@ -332,6 +332,36 @@ __device__ __forceinline__ float block_max(float v, float *red) {
     return t;
 }
 
+// ConvRot's rotation ("gizai:dit" reference: linearInto and
+// Block.dequantized: each 256 inputs x go to y = R x, R the regular
+// Hadamard of 256): the fast transform over the 8 index bits, butterflies
+// (a, b) -> (a + b, a - b) in the Hadamard's own (Sylvester) order, then the
+// exact 1/16.  A group of 256 values is spread over 256/NPL lanes, NPL
+// values a lane: value index NPL * (lane % (256/NPL)) + k is v[k], so the
+// low bits are a lane's own and the others pair lanes lane ^ m.
+template <int NPL>
+__device__ __forceinline__ void convrot256(float (&v)[NPL]) {
+#pragma unroll
+    for (int h = 1; h < NPL; h <<= 1)
+#pragma unroll
+        for (int k = 0; k < NPL; ++k)
+            if (!(k & h)) {
+                const float a = v[k], b = v[k + h];
+                v[k] = a + b;
+                v[k + h] = a - b;
+            }
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int m = 1; m < 256 / NPL; m <<= 1)
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+            const float p = __shfl_xor(v[k], m, kWave);
+            v[k] = (lane & m) ? p - v[k] : v[k] + p;
+        }
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) v[k] *= 0.0625f;
+}
+
 __device__ __forceinline__ uint32_t q8x4(float a, float b, float c, float d, float inv) {
     auto q = [inv](float v) -> uint32_t {
         const float r = fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
@@ -341,7 +371,9 @@ __device__ __forceinline__ uint32_t q8x4(float a, float b, float c, float d, flo
 }
 
 // The modulated norm of k_modnorm with its row taken to INT8 codes (out)
-// and one fp32 scale (s[r]) in the same pass.
+// and one fp32 scale (s[r]) in the same pass; ROT: rotated by ConvRot
+// first (D a multiple of 256: slot i of wave w holds group 4i + w).
+template <bool ROT>
 __global__ void __launch_bounds__(kNormThreads)
 k_modnorm_i8(const float *__restrict__ x, int D, const float *__restrict__ shift,
              const float *__restrict__ scale, const float *__restrict__ nw, int rms, float eps,
@@ -383,6 +415,11 @@ k_modnorm_i8(const float *__restrict__ x, int D, const float *__restrict__ shift
         v[i].y = (v[i].y - mu) * rstd * w.y * (1.f + sc.y) + sh.y;
         v[i].z = (v[i].z - mu) * rstd * w.z * (1.f + sc.z) + sh.z;
         v[i].w = (v[i].w - mu) * rstd * w.w * (1.f + sc.w) + sh.w;
+        if constexpr (ROT) {
+            float g[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            convrot256<4>(g);     // the whole wave takes this branch (D % 256 == 0)
+            v[i] = make_float4(g[0], g[1], g[2], g[3]);
+        }
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
     }
     amax = block_max(amax, red);
@@ -397,12 +434,44 @@ k_modnorm_i8(const float *__restrict__ x, int D, const float *__restrict__ shift
 }
 
 // bf16 rows [rows, K] to INT8 codes and a scale a row; K % 8 == 0, K <= 16384.
+// ROT: rotated by ConvRot first (K a multiple of 256: chunk slot i of lane
+// group t / 32 holds group 8i + t / 32, 8 values a lane); the rotation runs
+// on every slot, zeros past the row included, so that all lanes take part.
+template <bool ROT>
 __global__ void __launch_bounds__(kNormThreads)
 k_quant_rows(const uint16_t *__restrict__ x, int K, int8_t *__restrict__ out, float *__restrict__ s_out) {
     __shared__ float red[kNormThreads / 64];
     const int64_t r = blockIdx.x;
     const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + r * K);
     const int n8 = K / 8;
+    if constexpr (ROT) {
+        float f[8][8];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = threadIdx.x + i * kNormThreads;
+            const u32x4 w = c < n8 ? xr[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f[i][2 * j] = bf16lo_to_f32(w[j]);
+                f[i][2 * j + 1] = bf16hi_to_f32(w[j]);
+            }
+            if (i * kNormThreads < n8) convrot256<8>(f[i]);   // uniform over the block
+#pragma unroll
+            for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[i][k]));
+        }
+        amax = block_max(amax, red);
+        const float inv = amax > 0.f ? 127.f / amax : 0.f;
+        u32x2 *orow = reinterpret_cast<u32x2 *>(out + r * K);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = threadIdx.x + i * kNormThreads;
+            if (c < n8)
+                orow[c] = u32x2{q8x4(f[i][0], f[i][1], f[i][2], f[i][3], inv), q8x4(f[i][4], f[i][5], f[i][6], f[i][7], inv)};
+        }
+        if (threadIdx.x == 0) s_out[r] = amax / 127.f;
+        return;
+    }
     u32x4 v[8];
     float amax = 0.f;
 #pragma unroll
@@ -428,17 +497,24 @@ k_quant_rows(const uint16_t *__restrict__ x, int K, int8_t *__restrict__ out, fl
 }
 
 hipError_t launch_modnorm_i8(const float *x, int rows, int D, const float *shift, const float *scale,
-                             const float *norm_w, bool rms, float eps, int8_t *out, float *s, hipStream_t st) {
+                             const float *norm_w, bool rms, float eps, int8_t *out, float *s, hipStream_t st,
+                             bool rot) {
     if (rows <= 0) return hipSuccess;
-    if (D % 4 != 0 || D > 16 * kNormThreads) return hipErrorInvalidValue;
-    k_modnorm_i8<<<rows, kNormThreads, 0, st>>>(x, D, shift, scale, norm_w, rms ? 1 : 0, eps, out, s);
+    if (D % 4 != 0 || D > 16 * kNormThreads || (rot && D % 256 != 0)) return hipErrorInvalidValue;
+    if (rot)
+        k_modnorm_i8<true><<<rows, kNormThreads, 0, st>>>(x, D, shift, scale, norm_w, rms ? 1 : 0, eps, out, s);
+    else
+        k_modnorm_i8<false><<<rows, kNormThreads, 0, st>>>(x, D, shift, scale, norm_w, rms ? 1 : 0, eps, out, s);
     return hipGetLastError();
 }
 
-hipError_t launch_quant_rows(const uint16_t *x, int rows, int K, int8_t *out, float *s, hipStream_t st) {
+hipError_t launch_quant_rows(const uint16_t *x, int rows, int K, int8_t *out, float *s, hipStream_t st, bool rot) {
     if (rows <= 0) return hipSuccess;
-    if (K % 8 != 0 || K > 64 * kNormThreads) return hipErrorInvalidValue;
-    k_quant_rows<<<rows, kNormThreads, 0, st>>>(x, K, out, s);
+    if (K % 8 != 0 || K > 64 * kNormThreads || (rot && K % 256 != 0)) return hipErrorInvalidValue;
+    if (rot)
+        k_quant_rows<true><<<rows, kNormThreads, 0, st>>>(x, K, out, s);
+    else
+        k_quant_rows<false><<<rows, kNormThreads, 0, st>>>(x, K, out, s);
     return hipGetLastError();
 }
 

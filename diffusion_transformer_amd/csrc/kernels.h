@@ -27,12 +27,16 @@ hipError_t launch_gemv(const uint16_t *W, const float *x, int O, int I, bool sil
 // D a multiple of 4.  rms: RMSNorm times norm_w; else LayerNorm.
 // The modulated norm's rows as INT8 codes out [rows, D] and a scale a row
 // s [rows] (symmetric: s = amax / 127, q = rint(v * 127 / amax)).
+// rot: each 256 values of the row rotated by the regular Hadamard of 256
+// (ConvRot) before the quantization; D % 256 == 0.
 hipError_t launch_modnorm_i8(const float *x, int rows, int D, const float *shift, const float *scale,
-                             const float *norm_w, bool rms, float eps, int8_t *out, float *s, hipStream_t st);
+                             const float *norm_w, bool rms, float eps, int8_t *out, float *s, hipStream_t st,
+                             bool rot = false);
 
 // bf16 rows x [rows, K] as INT8 codes and a scale a row (as above);
-// K % 8 == 0, K <= 16384.
-hipError_t launch_quant_rows(const uint16_t *x, int rows, int K, int8_t *out, float *s, hipStream_t st);
+// K % 8 == 0, K <= 16384; rot as above (K % 256 == 0).
+hipError_t launch_quant_rows(const uint16_t *x, int rows, int K, int8_t *out, float *s, hipStream_t st,
+                             bool rot = false);
 
 // x[r] += gate * (norm(y[r]) * w) for r < rows: a sandwich block's norm of
 // a product's output rows before the gate ([GZ] POST_ATTN / POST_MLP); the

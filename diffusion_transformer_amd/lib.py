@@ -29,7 +29,7 @@ _lib = C.CDLL(LIB_PATH)
 OK, EINVAL, ERANGE, ENOMEM, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 STAGES = ("mod", "norm1", "qkv", "attn", "out", "norm2", "up", "down", "time", "img_in", "final",
           "euler", "txt_in", "par_in", "par_out", "post", "quant")
-W_BF16, W_INT8_B32, W_INT8_ROW = 0, 1, 2
+W_BF16, W_INT8_B32, W_INT8_ROW, W_INT8_ROT = 0, 1, 2, 3
 NORM_LAYER, NORM_RMS = 0, 1
 _NAMES = {0: "DIT_OK", -1: "DIT_EINVAL", -2: "DIT_ERANGE", -3: "DIT_ENOMEM", -4: "DIT_EDEVICE",
           -5: "DIT_EUNSUPPORTED"}
@@ -75,6 +75,7 @@ _SIGS = {
     "dit_modulated_norm": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_float, _P]),
     "dit_linear": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, _P]),
     "dit_quantize_rows": (C.c_int, [_P, _P, C.c_int, C.c_int, _P, _P]),
+    "dit_convrot_quantize_rows": (C.c_int, [_P, _P, C.c_int, C.c_int, _P, _P]),
     "dit_sigma_schedule": (C.c_int, [_P, C.c_int, C.c_float, _P, _P]),
     "dit_modulated_norm_int8": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_float, _P, _P]),
     "dit_linear_w8a8": (C.c_int, [_P, _P, _P, _P, _P, C.c_int, C.c_int, C.c_int, _P]),
@@ -242,6 +243,10 @@ class Context:
         self._call("dit_quantize_rows", _ptr(x, torch.bfloat16, "x"), rows, K, _ptr(q, torch.int8, "q"),
                    _ptr(s, torch.float32, "s"))
 
+    def convrot_quantize_rows(self, x, rows, K, q, s):
+        self._call("dit_convrot_quantize_rows", _ptr(x, torch.bfloat16, "x"), rows, K, _ptr(q, torch.int8, "q"),
+                   _ptr(s, torch.float32, "s"))
+
     def modulated_norm_int8(self, x, rows, shift, scale, norm_w, eps, q, s):
         self._call("dit_modulated_norm_int8", _ptr(x, torch.float32, "x"), rows,
                    _ptr(shift, torch.float32, "shift"), _ptr(scale, torch.float32, "scale"),
@@ -343,12 +348,12 @@ class BlockWeights:
 
     LIN = ("w_qkv", "w_out", "w_up", "w_down")
 
-    def __init__(self, tensors: dict, int8: bool = False):
+    def __init__(self, tensors: dict, int8: bool = False, rotated: bool = False):
         self.t = tensors
         self.int8 = int8
         w8a8 = "q8_w_qkv" in tensors
         b = Block()
-        b.wtype = W_INT8_ROW if w8a8 else W_INT8_B32 if int8 else W_BF16
+        b.wtype = (W_INT8_ROT if rotated else W_INT8_ROW) if w8a8 else W_INT8_B32 if int8 else W_BF16
         for i, n in enumerate(self.LIN):
             if w8a8:
                 b.w[i] = _ptr(tensors["q8_" + n], torch.int8, "q8_" + n)
@@ -367,8 +372,9 @@ class BlockWeights:
         self.struct = b
 
     @classmethod
-    def from_host(cls, bw: dict, device="cuda"):
-        """From synth.block_weights' dict (float32 values / int8 codes)."""
+    def from_host(cls, bw: dict, device="cuda", rotated: bool = False):
+        """From synth.block_weights' dict (float32 values / int8 codes);
+        rotated: W8A8 rows in ConvRot's basis (DIT_W_INT8_ROT)."""
         t = {}
         int8 = "q_w_qkv" in bw
         for k, v in bw.items():
@@ -378,7 +384,7 @@ class BlockWeights:
                 t[k] = dev_f32(v, device)
             else:
                 t[k] = dev_bf16(v, device)
-        return cls(t, int8=int8)
+        return cls(t, int8=int8, rotated=rotated)
 
 
 class ModelWeights:

@@ -53,7 +53,7 @@ typedef enum {
 
 /* Weight storage of the four block linears ([HC] s.1: bf16, or int8 with
  * one bf16 scale per block of 32 along the input axis). */
-typedef enum { DIT_W_BF16 = 0, DIT_W_INT8_B32 = 1, DIT_W_INT8_ROW = 2 } dit_wtype;
+typedef enum { DIT_W_BF16 = 0, DIT_W_INT8_B32 = 1, DIT_W_INT8_ROW = 2, DIT_W_INT8_ROT = 3 } dit_wtype;
 
 /* Norm before attention and MLP: LayerNorm without affine, or RMSNorm times
  * a per-feature weight ([GZ] normedInto; Block.parallel's modulated LayerNorm). */
@@ -88,13 +88,20 @@ typedef struct {
  * wtype DIT_W_BF16: w[i] are bf16; scale[i] must be NULL.
  * wtype DIT_W_INT8_B32: w[i] are int8 [out, in]; scale[i] are bf16
  *   [out, in/32]; weight = code * scale[o][k/32].
- * wtype DIT_W_INT8_ROW (W8A8; [GZ] linear, quantizedOf): w[i] are int8
- *   [out, in], scale[i] fp32 [out]; weight = code * scale[o].  Each
- *   product's input rows are taken to INT8 with one scale a row
- *   (s = max|row| / 127, codes rint(v * 127 / max|row|)), fused into the
- *   modulated norm for QKV and UP; the int32 sums times both scales.  Only
- *   the sequential forms take it; x, cos and sin must then be 16-byte
- *   aligned (the INT8 products have no unaligned fallback: DIT_EDEVICE).
+ * wtype DIT_W_INT8_ROW (W8A8 with per-token activations and per-output
+ *   weights, [K4] Appendix B D4): w[i] are int8 [out, in], scale[i] fp32
+ *   [out]; weight = code * scale[o].  Each product's input rows are taken
+ *   to INT8 with one scale a row (s = max|row| / 127, codes rint(v * 127 /
+ *   max|row|)), fused into the modulated norm for QKV and UP; the int32
+ *   sums times both scales.  Only the sequential forms take it (ffn up to
+ *   16384); x, cos and sin must then be 16-byte aligned (the INT8 products
+ *   have no unaligned fallback: DIT_EDEVICE).
+ * wtype DIT_W_INT8_ROT ([GZ] linearInto, quantizedOf, Block.quantized:
+ *   ConvRot): as DIT_W_INT8_ROW with the INT8 rows stored in the rotated
+ *   basis -- every 256 consecutive inputs of a product's input row are
+ *   rotated by the regular (Sylvester-order) Hadamard of 256, scaled by
+ *   1/16, before the row is quantized; the weights of the unrotated input
+ *   are code * scale times that rotation ([GZ] Block.dequantized).
  * norm_w: fp32.  [0] NORM1, [1] NORM2 ([D], required for DIT_NORM_RMS,
  *   ignored for DIT_NORM_LAYER), [2] Q_NORM, [3] K_NORM ([hd], required).
  * w_mod: bf16 [6D, D]; its output rows are shift, scale, gate of the
@@ -227,6 +234,13 @@ dit_status dit_sigma_schedule(const float *sample_sigmas, int n, float shift, fl
  * -127, 127), each step one correctly rounded fp32 operation (an all-zero
  * row: s = 0, q = 0).  K a multiple of 8, at most 16384. */
 dit_status dit_quantize_rows(dit_ctx *ctx, const uint16_t *x, int rows, int K, int8_t *q, float *s);
+
+/* ConvRot then INT8 rows ([GZ] linearInto, quantizedOf): x bf16 [rows, K]
+ * -> each 256 consecutive values y = R x with R the regular Hadamard of 256
+ * (Sylvester order, entries +-1/16), in fp32 -> q int8 [rows, K] and s fp32
+ * [rows] quantized as dit_quantize_rows quantizes.  K a multiple of 256, at
+ * most 16384. */
+dit_status dit_convrot_quantize_rows(dit_ctx *ctx, const uint16_t *x, int rows, int K, int8_t *q, float *s);
 
 /* dit_modulated_norm with its output rows as INT8 codes q [rows, D] and a
  * scale a row s [rows], quantized as dit_quantize_rows quantizes (from the

@@ -203,10 +203,39 @@ def linear(x: np.ndarray, w) -> np.ndarray:
 @dataclass
 class Int8Rows:
     """A linear's weights as INT8 rows q [out, in] and one float32 scale per
-    row s [out]: W = q * s[:, None]."""
+    row s [out]: W = q * s[:, None].  rotated: the rows are stored in
+    ConvRot's basis ([GZ] Block.quantized, Block.dequantized, comfyInt8Rows:
+    rotated by the regular Hadamard of 256), so the product's input rows are
+    rotated the same way before they are quantized (convrot), and the weights
+    of the unrotated input are (q * s) R per group of 256 inputs."""
 
     q: np.ndarray
     s: np.ndarray
+    rotated: bool = False
+
+
+def hadamard(n: int = 256) -> np.ndarray:
+    """The regular Hadamard matrix of order n (a power of two) in its own
+    (Sylvester) order, H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]], scaled by
+    1/sqrt(n) so that it is orthogonal.  float64 [n, n]."""
+    assert n >= 1 and n & (n - 1) == 0
+    h = np.ones((1, 1), dtype=F64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / math.sqrt(n)
+
+
+def convrot(x, group: int = 256) -> np.ndarray:
+    """ConvRot's rotation of the product's input rows ([GZ] linearInto,
+    Block.dequantized: each 256 inputs x are taken to y = R x with R the
+    regular Hadamard of 256): every consecutive group of 256 values of the
+    last axis times R (symmetric, so the row form y = x R^T is x R), in
+    float64.  The last axis must be a multiple of 256."""
+    x = np.asarray(x, dtype=F64)
+    k = x.shape[-1]
+    assert k % group == 0
+    r = hadamard(group)
+    return (x.reshape(x.shape[:-1] + (k // group, group)) @ r.T).reshape(x.shape)
 
 
 def quantize_rows_int8(x):
@@ -234,16 +263,20 @@ class _RowSlicer:
 
     def __getitem__(self, sl):
         if isinstance(self.w, Int8Rows):
-            return Int8Rows(q=np.asarray(self.w.q)[sl], s=np.asarray(self.w.s)[sl])
+            return Int8Rows(q=np.asarray(self.w.q)[sl], s=np.asarray(self.w.s)[sl], rotated=self.w.rotated)
         return np.asarray(self.w, F64)[sl]
 
 
 def linear_w8a8(x, w: Int8Rows) -> np.ndarray:
-    """x W^T with x's rows quantized by quantize_rows_int8: the exact integer
-    dot products times x's row scale and W's row scale, in float64.  The
-    integer sums are taken by a float64 matrix product: every product of two
-    codes and every partial sum is an integer of magnitude below
+    """x W^T with x's rows quantized by quantize_rows_int8 (after ConvRot's
+    rotation when the weights are rotated: the rotated rows are rounded once
+    to float32, the precision the quantization decides in): the exact
+    integer dot products times x's row scale and W's row scale, in float64.
+    The integer sums are taken by a float64 matrix product: every product
+    of two codes and every partial sum is an integer of magnitude below
     K * 127^2 < 2^53, so each float64 addition is exact in any order."""
+    if w.rotated:
+        x = convrot(x).astype(F32)
     q, s = quantize_rows_int8(x)
     wq = np.asarray(w.q)
     assert q.shape[-1] * 127 * 127 < 2 ** 53

@@ -86,7 +86,7 @@ def arch_pair(sh, norm="layer"):
     return la, oa
 
 
-def oracle_block(bw: dict) -> "O.BlockWeights":
+def oracle_block(bw: dict, rotated: bool = False) -> "O.BlockWeights":
     """The oracle's view of synth.block_weights' dict: int8 block-32 weights
     become the bf16 operands the products take (the exact code * scale
     rounded to nearest even, oracle.dequant_int8_b32_bf16), so the parity of
@@ -95,7 +95,7 @@ def oracle_block(bw: dict) -> "O.BlockWeights":
         if "q_" + n in bw:
             return O.dequant_int8_b32_bf16(bw["q_" + n], bw["s_" + n])
         if "q8_" + n in bw:
-            return O.Int8Rows(q=bw["q8_" + n], s=bw["s8_" + n])
+            return O.Int8Rows(q=bw["q8_" + n], s=bw["s8_" + n], rotated=rotated)
         return bw[n]
     return O.BlockWeights(w_qkv=lin("w_qkv"), w_out=lin("w_out"), w_up=lin("w_up"),
                           w_down=lin("w_down"), w_mod=bw["w_mod"], q_norm=bw["q_norm"],

@@ -739,6 +739,34 @@ def test_quantize_rows_bit_exact(ctx_tiny, rows, K):
     assert (np_of(q) == qr).all()
 
 
+@pytest.mark.parametrize("rows,K", [(5, 256), (72, 768), (300, 3072), (4608, 12288), (3, 16384)])
+def test_convrot_quantize_rows(ctx_tiny, rows, K):
+    """ConvRot then INT8 rows: the GPU rotates in fp32 butterflies, the oracle
+    takes the plain product with the Hadamard matrix in float64 and rounds it
+    once to fp32, so a code may sit one step away where the two roundings
+    straddle a half step.  Every GPU code must still be a nearest code of the
+    exact rotated value (within its half step and the rotation's rounding),
+    and such one-step codes must be rare."""
+    x = _bf16_rows(rows, K, seed=rows + K + 7)
+    q = torch.empty((rows, K), dtype=torch.int8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    say("convrot quantize rows", rows, K)
+    ctx_tiny.convrot_quantize_rows(L.dev_bf16(x), rows, K, q, s)
+    torch.cuda.synchronize()
+    y = O.convrot(x)
+    qr, sr = O.quantize_rows_int8(y.astype(np.float32))
+    qg, sg = np_of(q).astype(np.int64), np_of(s).astype(np.float64)
+    amax = np.abs(y).max(axis=1)
+    assert np.all(np.abs(sg - sr) <= 1e-6 * sr + 1e-30)
+    assert (sg[1] == 0.0) and (qg[1] == 0).all()                                    # zero row
+    d = np.abs(qg - qr.astype(np.int64))
+    assert d.max() <= 1 and d.sum() <= max(2, 1e-3 * d.size), f"{int(d.sum())} codes differ by one"
+    err = np.abs(qg * sg[:, None] - y)
+    assert np.all(err <= sg[:, None] * (0.5 + 1e-3) + amax[:, None] * 1e-6)
+    # a constant row rotates exactly: each group's first value is 16x it
+    assert (qg[2].reshape(-1, 256)[:, 0] == 127).all() and (qg[2].reshape(-1, 256)[:, 1:] == 0).all()
+
+
 @pytest.mark.parametrize("norm", ["layer", "rms"])
 @pytest.mark.parametrize("rows", [72, 4608])
 def test_modulated_norm_int8(norm, rows):
@@ -788,10 +816,10 @@ def test_linear_w8a8(ctx_big, M, N, K):
     assert np.all(np.abs(got - ref) <= 3e-7 * np.abs(ref) + 1e-30)
 
 
-def _w8a8_gpu(ctx, case, runs=None):
+def _w8a8_gpu(ctx, case, runs=None, rotated=False):
     sh = case["shape"]
     seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
-    bw = L.BlockWeights.from_host(case["block"])
+    bw = L.BlockWeights.from_host(case["block"], rotated=rotated)
     x = L.dev_f32(case["x"])
     if runs is None:
         ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
@@ -801,19 +829,24 @@ def _w8a8_gpu(ctx, case, runs=None):
     return x
 
 
-@pytest.mark.parametrize("name,norm,norm_std,sandwich", [("tiny", "layer", 0.0, False), ("tiny", "rms", 0.1, False),
-                                                          ("tiny", "layer", 0.0, True), ("s1088", "layer", 0.0, False)])
-def test_w8a8_block_full_parity(name, norm, norm_std, sandwich):
+@pytest.mark.parametrize("name,norm,norm_std,sandwich,rot", [("tiny", "layer", 0.0, False, False),
+                                                              ("tiny", "rms", 0.1, False, False),
+                                                              ("tiny", "layer", 0.0, True, False),
+                                                              ("s1088", "layer", 0.0, False, False),
+                                                              ("tiny", "layer", 0.0, False, True),
+                                                              ("tiny", "rms", 0.1, True, True),
+                                                              ("s1088", "layer", 0.0, False, True)])
+def test_w8a8_block_full_parity(name, norm, norm_std, sandwich, rot):
     case = synth.block_case(name, norm_std=norm_std, rms=(norm == "rms"), sandwich=sandwich, w8a8=True)
     sh = case["shape"]
     la, oa = arch_pair(sh, norm)
     ctx = L.Context(la, max_rows=sh.S)
-    say("w8a8 block", name, norm, "sandwich" if sandwich else "", "S =", sh.S)
-    got = np_of(_w8a8_gpu(ctx, case))
+    say("w8a8 block", name, norm, "sandwich" if sandwich else "", "convrot" if rot else "", "S =", sh.S)
+    got = np_of(_w8a8_gpu(ctx, case, rotated=rot))
     D, F, H = sh.hidden, sh.ffn, sh.heads
     S, Sp = sh.S, (sh.S + 63) // 64 * 64
     cs, sn, vec = _oracle_inputs(case, oa)
-    y, ref = O.block_forward(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, keep=True)
+    y, ref = O.block_forward(case["x"], oracle_block(case["block"], rotated=rot), vec, cs, sn, oa, keep=True)
     compare(f"{name}/q", np_of(ctx.debug_copy(2, torch.bfloat16, (H, S, 128))), ref["q"], bf16_stored=True)
     compare(f"{name}/k", np_of(ctx.debug_copy(3, torch.bfloat16, (H, S, 128))), ref["k"], bf16_stored=True)
     v = np_of(ctx.debug_copy(4, torch.bfloat16, (H, 128, Sp)))[:, :, :S].transpose(0, 2, 1)
@@ -825,18 +858,19 @@ def test_w8a8_block_full_parity(name, norm, norm_std, sandwich):
     ctx.close()
 
 
-def test_w8a8_block_full_size_sampled_rows(ctx_big):
+@pytest.mark.parametrize("rot", [False, True])
+def test_w8a8_block_full_size_sampled_rows(ctx_big, rot):
     case = synth.block_case("s4608_w8a8")
     sh = case["shape"]
     _, oa = arch_pair(sh)
     D, F = sh.hidden, sh.ffn
-    say("w8a8 block s4608")
-    got = np_of(_w8a8_gpu(ctx_big, case))
+    say("w8a8 block s4608", "convrot" if rot else "")
+    got = np_of(_w8a8_gpu(ctx_big, case, rotated=rot))
     o_got = np_of(ctx_big.debug_copy(5, torch.bfloat16, (sh.S, D)))
     a_got = np_of(ctx_big.debug_copy(7, torch.bfloat16, (sh.S, F)))
     cs, sn, vec = _oracle_inputs(case, oa)
     rows = synth.rows_sample(sh.S, 48, L=sh.L)
-    y, o, x1, a = O.block_forward_rows(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, rows)
+    y, o, x1, a = O.block_forward_rows(case["x"], oracle_block(case["block"], rotated=rot), vec, cs, sn, oa, rows)
     compare("s4608_w8a8/o", o_got[rows], o, bf16_stored=True)
     compare("s4608_w8a8/a", a_got[rows], a, bf16_stored=True)
     compare("s4608_w8a8/y", got[rows], y)

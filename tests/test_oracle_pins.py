@@ -730,6 +730,63 @@ def test_w8a8_linear_error_bound():
     assert err.max() > 0                                                     # the rounding is there
 
 
+def test_hadamard_sylvester_and_orthogonal():
+    h4 = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]]) / 2.0
+    assert (O.hadamard(4) == h4).all()
+    r = O.hadamard(256)
+    assert np.abs(r @ r.T - np.eye(256)).max() < 1e-14
+    # the regular (Sylvester) order: entry (i, j) is (-1)^popcount(i & j) / 16
+    rng = np.random.default_rng(70)
+    for i, j in rng.integers(0, 256, (500, 2)):
+        assert r[i, j] == (-1.0) ** bin(int(i) & int(j)).count("1") / 16.0
+
+
+def test_convrot_one_hot_groups_and_norms():
+    x = np.zeros((2, 768))
+    x[0, 256 + 37] = 5.0                     # one value in the second group
+    y = O.convrot(x)
+    assert (y[0, :256] == 0).all() and (y[0, 512:] == 0).all()
+    assert np.allclose(np.abs(y[0, 256:512]), 5.0 / 16)             # spread evenly over its group
+    assert np.allclose(y[0, 256:512], 5.0 * O.hadamard(256)[:, 37])
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((3, 512))
+    y = O.convrot(x)
+    assert np.allclose(np.linalg.norm(y.reshape(3, 2, 256), axis=2), np.linalg.norm(x.reshape(3, 2, 256), axis=2))
+    assert np.allclose(O.convrot(y), x)                                # R R = I (R symmetric)
+
+
+def test_rotated_weights_leave_the_exact_product():
+    # the rotated input against weights in the rotated basis is the product:
+    # (x R)(W R)^T = x W^T group by group
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((5, 512))
+    w = rng.standard_normal((7, 512))
+    assert np.abs(O.convrot(x) @ O.convrot(w).T - x @ w.T).max() < 1e-12
+
+
+def test_rotated_w8a8_linear_brute_force():
+    rng = np.random.default_rng(73)
+    x = rng.standard_normal((3, 256)) * np.array([[1.0], [30.0], [0.01]])
+    x[1, 17] = 400.0                                                      # an outlier
+    w = O.Int8Rows(q=rng.integers(-127, 128, (4, 256)).astype(np.int8), s=rng.uniform(0.001, 0.01, 4).astype(np.float32),
+                   rotated=True)
+    y32 = np.array([[sum(x[i, j] * (-1.0) ** bin(k & j).count("1") for j in range(256)) / 16.0 for k in range(256)]
+                    for i in range(3)]).astype(np.float32)
+    qx, sx = O.quantize_rows_int8(y32)
+    got = O.linear(x, w)
+    for i in range(3):
+        for j in range(4):
+            acc = sum(int(qx[i, k]) * int(w.q[j, k]) for k in range(256))
+            assert abs(got[i, j] - acc * float(sx[i]) * float(w.s[j])) <= 1e-9 * max(1.0, abs(got[i, j]))
+    # the outlier row: rotated, its error against the exact product of the
+    # rotated-basis weights is far below the unrotated quantization's
+    wd = w.q.astype(np.float64) * w.s[:, None].astype(np.float64)
+    exact = x @ O.convrot(wd).T
+    qp, sp = O.quantize_rows_int8(x)
+    unrot = (qp.astype(np.float64) * sp[:, None]) @ O.convrot(wd).T
+    assert np.abs(got[1] - exact[1]).max() < 0.5 * np.abs(unrot[1] - exact[1]).max()
+
+
 def test_w8a8_block_is_close_to_the_float_block():
     # the same block with INT8 weights, its products' inputs taken to INT8:
     # close to the float block of the dequantized weights, not equal
