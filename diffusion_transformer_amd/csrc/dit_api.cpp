@@ -47,6 +47,9 @@ struct dit_ctx {
     float *as = nullptr;
     float *seq = nullptr, *vel = nullptr;
     size_t bytes[9] = {};
+    // QK-norm + rotary inside the QKV product's epilogue (true), or the
+    // product's bf16 projection and then the separate prep pass
+    bool qk_fused = true;
     std::string err;
     // stage timing
     bool timing = false;
@@ -578,9 +581,24 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
     e.sin = sn;
     e.qk_eps = A.qk_eps;
     e.rows_total = Sk;
-    {
+    if (c->qk_fused) {
         Stage t(c, DIT_ST_QKV);
         DIT_LAUNCH(c, product(c->h, 0, S, 0, 3 * D, D, e), "qkv");
+    } else {
+        // the unfused arm: the projection stored in bf16 (the parallel
+        // block's [o | a] buffer, unused by the sequential forms until the
+        // sandwich norms' output product), then the q/k/v prep pass
+        GemmEpi pe{};
+        pe.kind = EPI_BF16;
+        pe.act = c->oa;
+        pe.ld_act = 3 * D;
+        {
+            Stage t(c, DIT_ST_QKV);
+            DIT_LAUNCH(c, product(c->h, 0, S, 0, 3 * D, D, pe), "qkv");
+        }
+        Stage t(c, DIT_ST_QK_PREP);
+        DIT_LAUNCH(c, launch_qk_prep(c->oa, S, H, Sk, b->norm_w[2], b->norm_w[3], cs, sn, A.qk_eps, c->q, c->k, c->vt, Sp, st),
+                   "qk prep");
     }
     if (Sk > S) DIT_TRY(ref_copy(c, nullptr, slot, S, Sk, false));
     {
@@ -685,7 +703,7 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
         Sx * D * 2, Sx * F * 2,                                        // o a
         S * size_t(arch->latent) * 2, S * size_t(arch->text_dim) * 2,  // latb ctxb
         S * D * 4, S * size_t(arch->latent) * 4,                       // seq vel
-        S * std::max((D + F) * 2, D * 4),                              // oa (yf)
+        S * std::max(std::max((D + F) * 2, D * 4), D * 6),             // oa (yf, the unfused arm's qkv)
         Sx * std::max(D, F), Sx * 4,                                   // aq as
     };
     size_t off[sizeof sizes / sizeof sizes[0]];
@@ -862,6 +880,31 @@ dit_status dit_sigma_schedule(const float *sample_sigmas, int n, float shift, fl
         t[i] = ts / 1000.f;
     }
     sigmas[n] = 0.f;
+    return DIT_OK;
+}
+
+dit_status dit_set_qk_prep(dit_ctx *ctx, int fused) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (fused != 0 && fused != 1) return fail(ctx, DIT_EINVAL, "fused = %d is not 0 or 1", fused);
+    ctx->qk_fused = fused != 0;
+    return DIT_OK;
+}
+
+dit_status dit_qk_prep(dit_ctx *ctx, const uint16_t *qkv, int S, const float *q_norm, const float *k_norm,
+                       const float *cos_t, const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *vt) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (!qkv || !q_norm || !k_norm || !cos_t || !sin_t || !q || !k || !vt)
+        return fail(ctx, DIT_EINVAL, "qkv, q_norm, k_norm, cos, sin, q, k or vt is NULL");
+    if (S < 1 || S > ctx->max_rows) return fail(ctx, DIT_ERANGE, "S %d outside 1..%d", S, ctx->max_rows);
+    auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    if (!al16(qkv) || !al16(q_norm) || !al16(k_norm) || !al16(cos_t) || !al16(sin_t) || !al16(q) || !al16(k) || !al16(vt))
+        return fail(ctx, DIT_EINVAL, "qkv, q_norm, k_norm, cos, sin, q, k and vt must be 16-byte aligned");
+    DIT_TRY(check_ctx(ctx));
+    const dit_arch &A = ctx->arch;
+    Stage t(ctx, DIT_ST_QK_PREP);
+    DIT_LAUNCH(ctx, launch_qk_prep(qkv, S, A.heads, S, q_norm, k_norm, cos_t, sin_t, A.qk_eps, q, k, vt, round_up(S, 64),
+                                   ctx->stream),
+               "qk prep");
     return DIT_OK;
 }
 

@@ -6,6 +6,7 @@
 // "944 -> 346 ms: optimizing FLUX.2 klein-4B on one TPU v6e chip" s.4.4 for
 // the fused head norm + rotary):
 //   EPI_F32       out[r][c] = C                              (plain fp32 store)
+//   EPI_BF16      act[r][c] = bf16(C)                        (plain bf16 store)
 //   EPI_GATE_RES  x[r][c] += gate[c] * C                     (gated residual, in place)
 //   EPI_SWIGLU    act[r][j] = bf16(silu(C[r][2j]) * C[r][2j+1])   (UP rows interleaved)
 //   EPI_QKV       per 128-wide head of Q and K: RMSNorm times the head-norm
@@ -110,7 +111,25 @@ __device__ __forceinline__ void gemm_epilogue(f32x4 (&acc)[TMW][TN], int m0, int
     const int rbase = m0 + wm * TMW * 16 + 4 * (lane >> 4);
     const int pl = lane & 15;
 
-    if constexpr (EPI == EPI_F32 || EPI == EPI_GATE_RES) {
+    if constexpr (EPI == EPI_BF16) {
+        const int ld = ep.ld_act ? ep.ld_act : N;
+#pragma unroll
+        for (int tm = 0; tm < TMW; ++tm) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rbase + tm * 16 + r;
+                if (row >= M) continue;
+#pragma unroll
+                for (int tp = 0; tp < TN / 2; ++tp) {
+                    const int c = col0 + 2 * (tp * 16 + pl);
+                    if (c >= N) continue;
+                    *reinterpret_cast<uint32_t *>(ep.act + static_cast<int64_t>(row) * ld + c) =
+                        pack_bf16x2(acc[tm][tp][r], acc[tm][tp + TN / 2][r]);
+                }
+            }
+        }
+    } else if constexpr (EPI == EPI_F32 || EPI == EPI_GATE_RES) {
 #pragma unroll
         for (int tm = 0; tm < TMW; ++tm) {
             __builtin_amdgcn_sched_barrier(0);   // bound the loads kept in flight
@@ -542,6 +561,11 @@ __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, in
                     if (grow >= M) continue;
                     const f32x4 v = *reinterpret_cast<const f32x4 *>(
                         L + row * 1024 + ((cc ^ (((row >> 2) & 1) << 3)) << 4));
+                    if constexpr (EPI == EPI_BF16) {
+                        *reinterpret_cast<u32x2 *>(ep.act + static_cast<int64_t>(grow) * (ep.ld_act ? ep.ld_act : N) + n0 +
+                                                   4 * cc) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        continue;
+                    }
                     f32x4 *dst = reinterpret_cast<f32x4 *>(ep.out + static_cast<int64_t>(grow) * ep.ldo + n0 + 4 * cc);
                     if constexpr (EPI == EPI_F32) {
                         *dst = v;
@@ -984,6 +1008,9 @@ static hipError_t launch_cfg(const uint16_t *A, const void *W, const uint16_t *W
         case EPI_F32:
             k_gemm<BM, BN, W8, EPI_F32><<<grid, C::NT, 0, st>>>(A, W, Ws, M, N, K, ep);
             break;
+        case EPI_BF16:
+            k_gemm<BM, BN, W8, EPI_BF16><<<grid, C::NT, 0, st>>>(A, W, Ws, M, N, K, ep);
+            break;
         case EPI_GATE_RES:
             k_gemm<BM, BN, W8, EPI_GATE_RES><<<grid, C::NT, 0, st>>>(A, W, Ws, M, N, K, ep);
             break;
@@ -1025,6 +1052,7 @@ static bool pp_epilogue_ok(const GemmEpi &ep, int N) {
     bool epi_ok = false;
     switch (ep.kind) {
         case EPI_F32: epi_ok = al16(ep.out) && ep.ldo % 4 == 0; break;
+        case EPI_BF16: epi_ok = al16(ep.act) && ep.ld_act % 8 == 0; break;
         case EPI_GATE_RES: epi_ok = al16(ep.out) && ep.ldo % 4 == 0 && al16(ep.gate); break;
         case EPI_SWIGLU: epi_ok = act_ok; break;
         case EPI_QKV: epi_ok = qkv_ok; break;
@@ -1095,6 +1123,7 @@ hipError_t launch_gemm_w8a8(const int8_t *A, const float *a_scale, const int8_t 
     const auto *w = reinterpret_cast<const uint16_t *>(W);
     switch (ep.kind) {
         case EPI_F32: return launch_pp<EPI_F32, false, true>(a, w, M, N, K, ep, st);
+        case EPI_BF16: return launch_pp<EPI_BF16, false, true>(a, w, M, N, K, ep, st);
         case EPI_GATE_RES: return launch_pp<EPI_GATE_RES, false, true>(a, w, M, N, K, ep, st);
         case EPI_SWIGLU: return launch_pp<EPI_SWIGLU, false, true>(a, w, M, N, K, ep, st);
         case EPI_QKV: return launch_pp<EPI_QKV, false, true>(a, w, M, N, K, ep, st);
@@ -1112,6 +1141,7 @@ hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Ws, boo
             e.w_bscale = Ws;
             switch (ep.kind) {
                 case EPI_F32: return launch_pp<EPI_F32, false, false, true>(A, Wb, M, N, K, e, st);
+                case EPI_BF16: return launch_pp<EPI_BF16, false, false, true>(A, Wb, M, N, K, e, st);
                 case EPI_GATE_RES: return launch_pp<EPI_GATE_RES, false, false, true>(A, Wb, M, N, K, e, st);
                 case EPI_SWIGLU: return launch_pp<EPI_SWIGLU, false, false, true>(A, Wb, M, N, K, e, st);
                 case EPI_QKV: return launch_pp<EPI_QKV, false, false, true>(A, Wb, M, N, K, e, st);
@@ -1121,6 +1151,7 @@ hipError_t launch_gemm(const uint16_t *A, const void *W, const uint16_t *Ws, boo
         if (ep.k_split > 0) return launch_pp<EPI_GATE_RES, true>(A, Wb, M, N, K, ep, st);
         switch (ep.kind) {
             case EPI_F32: return launch_pp<EPI_F32>(A, Wb, M, N, K, ep, st);
+            case EPI_BF16: return launch_pp<EPI_BF16>(A, Wb, M, N, K, ep, st);
             case EPI_GATE_RES: return launch_pp<EPI_GATE_RES>(A, Wb, M, N, K, ep, st);
             case EPI_SWIGLU: return launch_pp<EPI_SWIGLU>(A, Wb, M, N, K, ep, st);
             case EPI_QKV: return launch_pp<EPI_QKV>(A, Wb, M, N, K, ep, st);

@@ -314,6 +314,104 @@ hipError_t launch_post_norm_gate(const float *y, int rows, int D, const float *w
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ q/k/v prep
+// The QKV projection's heads made ready for the attention in a pass of their
+// own, the unfused arm of the QKV product's epilogue ("944 -> 346 ms:
+// optimizing FLUX.2 klein-4B on one TPU v6e chip" s.4.4 runs this prep as a
+// separate kernel over the stored projection; "gizai:dit" prepOf): per
+// 128-wide head of q and k, RMSNorm (fp32 statistics) times the head-norm
+// weight, then the adjacent-pair rotation with the row's cos/sin, to bf16
+// q, k [H, Sh, 128]; v heads transposed to vt [H, 128, ldv].  qkv bf16
+// [S, 3 * H * 128] (all queries, all keys, all values).  One workgroup per
+// (64-row tile, head of q, k or v): 16 KB in, 16 KB out, HBM-bound.
+constexpr int kPrepRows = 64;
+
+__global__ void __launch_bounds__(256)
+k_qk_prep(const uint16_t *__restrict__ qkv, int S, int H, int Sh, const float *__restrict__ qn,
+          const float *__restrict__ kn, const float *__restrict__ cs, const float *__restrict__ sn, float eps,
+          uint16_t *__restrict__ q, uint16_t *__restrict__ k, uint16_t *__restrict__ vt, int ldv) {
+    __shared__ uint16_t tile[kPrepRows][128 + 8];
+    const int r0 = blockIdx.x * kPrepRows;
+    const int hh = blockIdx.y, region = hh / H, head = hh % H;
+    const int64_t ld = static_cast<int64_t>(3) * H * 128;
+    const int t = threadIdx.x;
+    if (region < 2) {
+        // 16 lanes to a (row, head): lane l16 holds features 8 l16 .. 8 l16 + 7,
+        // i.e. rotation pairs 4 l16 .. 4 l16 + 3
+        const float *nw = region == 0 ? qn : kn;
+        uint16_t *dst = region == 0 ? q : k;
+        const int l16 = t & 15;
+        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(nw + 8 * l16);
+        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(nw + 8 * l16 + 4);
+        const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+        for (int it = 0; it < kPrepRows / 16; ++it) {
+            const int r = r0 + it * 16 + (t >> 4);
+            const int rr = min(r, S - 1);
+            const u32x4 raw = *reinterpret_cast<const u32x4 *>(qkv + rr * ld + hh * 128 + 8 * l16);
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = bf16lo_to_f32(raw[j]);
+                v[2 * j + 1] = bf16hi_to_f32(raw[j]);
+            }
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+            ss += __shfl_xor(ss, 1, kWave);
+            ss += __shfl_xor(ss, 2, kWave);
+            ss += __shfl_xor(ss, 4, kWave);
+            ss += __shfl_xor(ss, 8, kWave);
+            const float rstd = rsqrtf(ss * (1.0f / 128.0f) + eps);
+            const f32x4 c = *reinterpret_cast<const f32x4 *>(cs + static_cast<int64_t>(rr) * 64 + 4 * l16);
+            const f32x4 sv = *reinterpret_cast<const f32x4 *>(sn + static_cast<int64_t>(rr) * 64 + 4 * l16);
+            uint32_t o[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float a = v[2 * p] * rstd * w[2 * p], b = v[2 * p + 1] * rstd * w[2 * p + 1];
+                o[p] = pack_bf16x2(a * c[p] - b * sv[p], a * sv[p] + b * c[p]);
+            }
+            if (r < S)
+                *reinterpret_cast<u32x4 *>(dst + (static_cast<int64_t>(head) * Sh + r) * 128 + 8 * l16) =
+                    u32x4{o[0], o[1], o[2], o[3]};
+        }
+    } else {
+        // v: 64 rows x 128 features through LDS, out as 128 feature rows of 64 keys
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = t + 256 * i, row = c >> 4, col = (c & 15) * 8;
+            const int r = min(r0 + row, S - 1);
+            *reinterpret_cast<u32x4 *>(&tile[row][col]) =
+                *reinterpret_cast<const u32x4 *>(qkv + r * ld + hh * 128 + col);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = t + 256 * i, d = e >> 3, kb = (e & 7) * 8;
+            uint16_t *out = vt + (static_cast<int64_t>(head) * 128 + d) * ldv + r0 + kb;
+            const int valid = S - (r0 + kb);
+            if (valid >= 8) {
+                u32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = static_cast<uint32_t>(tile[kb + 2 * j][d]) | (static_cast<uint32_t>(tile[kb + 2 * j + 1][d]) << 16);
+                *reinterpret_cast<u32x4 *>(out) = o;
+            } else {
+                for (int j = 0; j < valid; ++j) out[j] = tile[kb + j][d];
+            }
+        }
+    }
+}
+
+hipError_t launch_qk_prep(const uint16_t *qkv, int S, int H, int Sh, const float *qn, const float *kn, const float *cs,
+                          const float *sn, float eps, uint16_t *q, uint16_t *k, uint16_t *vt, int ldv, hipStream_t st) {
+    if (S <= 0) return hipSuccess;
+    if (Sh < S || ldv < S || ldv % 8) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>((S + kPrepRows - 1) / kPrepRows), static_cast<unsigned>(3 * H));
+    k_qk_prep<<<grid, 256, 0, st>>>(qkv, S, H, Sh, qn, kn, cs, sn, eps, q, k, vt, ldv);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ INT8 rows
 // Symmetric INT8 codes of a row over one scale (W8A8 products' inputs):
 // inv = 127 / amax and q = rint(v * inv) clamped to +-127, s = amax / 127,

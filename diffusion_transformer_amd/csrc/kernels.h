@@ -47,22 +47,28 @@ hipError_t launch_post_norm_gate(const float *y, int rows, int D, const float *w
 hipError_t launch_modnorm(const float *x, int rows, int D, const float *shift, const float *scale,
                           const float *norm_w, bool rms, float eps, uint16_t *out, hipStream_t st);
 
+// The unfused q/k/v prep: qkv bf16 [S, 3H*128] -> q, k bf16 [H, Sh, 128]
+// (head norm x weight, rotation with cos/sin [S, 64]), vt bf16 [H, 128, ldv]
+// (rows [0, S) of each; ldv % 8 == 0, 16-byte aligned buffers).
+hipError_t launch_qk_prep(const uint16_t *qkv, int S, int H, int Sh, const float *qn, const float *kn, const float *cs,
+                          const float *sn, float eps, uint16_t *q, uint16_t *k, uint16_t *vt, int ldv, hipStream_t st);
+
 // ---- products (k_gemm.hip) -------------------------------------------------
-enum EpiKind { EPI_F32 = 0, EPI_GATE_RES = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_QKV_SWIGLU = 4 };
+enum EpiKind { EPI_F32 = 0, EPI_GATE_RES = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_QKV_SWIGLU = 4, EPI_BF16 = 5 };
 
 struct GemmEpi {
     int kind;
     float *out;            // EPI_F32: out [M, ldo] fp32; EPI_GATE_RES: x [M, ldo] += gate * acc
     int ldo;
     const float *gate;     // EPI_GATE_RES: [N]
-    uint16_t *act;         // EPI_SWIGLU: bf16 [M, N/2]
+    uint16_t *act;         // EPI_SWIGLU: bf16 [M, N/2]; EPI_BF16: bf16 [M, ld_act] = C
     // EPI_QKV
     uint16_t *q, *k, *vt;  // q, k [H, M, 128]; vt [H, 128, ldv]
     int heads, ldv;
     const float *qn, *kn;  // [128] head-norm weights
     const float *cos, *sin;// [M, 64]
     float qk_eps;
-    int ld_act;            // EPI_SWIGLU: row stride of act (0: N/2)
+    int ld_act;            // EPI_SWIGLU: row stride of act (0: N/2); EPI_BF16: row stride (0: N)
     // Two-weight products of the parallel block (bf16 weights only):
     //  EPI_QKV_SWIGLU: columns < n_split take W [n_split, K] and the QKV
     //    epilogue; columns >= n_split take w2 [N - n_split, K] and the SwiGLU

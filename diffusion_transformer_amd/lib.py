@@ -28,7 +28,7 @@ _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, ERANGE, ENOMEM, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 STAGES = ("mod", "norm1", "qkv", "attn", "out", "norm2", "up", "down", "time", "img_in", "final",
-          "euler", "txt_in", "par_in", "par_out", "post", "quant")
+          "euler", "txt_in", "par_in", "par_out", "post", "quant", "qk_prep")
 W_BF16, W_INT8_B32, W_INT8_ROW, W_INT8_ROT = 0, 1, 2, 3
 NORM_LAYER, NORM_RMS = 0, 1
 _NAMES = {0: "DIT_OK", -1: "DIT_EINVAL", -2: "DIT_ERANGE", -3: "DIT_ENOMEM", -4: "DIT_EDEVICE",
@@ -80,6 +80,8 @@ _SIGS = {
     "dit_modulated_norm_int8": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_float, _P, _P]),
     "dit_linear_w8a8": (C.c_int, [_P, _P, _P, _P, _P, C.c_int, C.c_int, C.c_int, _P]),
     "dit_attention": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, _P]),
+    "dit_qk_prep": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, _P, _P, _P, _P]),
+    "dit_set_qk_prep": (C.c_int, [_P, C.c_int]),
     "dit_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_parallel_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_double_block_forward": (C.c_int, [_P, C.POINTER(Block), C.POINTER(Block), _P, _P, _P, _P, C.c_int,
@@ -257,6 +259,14 @@ class Context:
         self._call("dit_linear_w8a8", _ptr(a, torch.int8, "a"), _ptr(a_scale, torch.float32, "a_scale"),
                    _ptr(w, torch.int8, "w"), _ptr(w_scale, torch.float32, "w_scale"), M, N, K,
                    _ptr(out, torch.float32, "out"))
+
+    def qk_prep(self, qkv, S, q_norm, k_norm, cos, sin, q, k, vt):
+        self._call("dit_qk_prep", _ptr(qkv, torch.bfloat16, "qkv"), S, _ptr(q_norm, torch.float32, "q_norm"),
+                   _ptr(k_norm, torch.float32, "k_norm"), _ptr(cos, torch.float32, "cos"), _ptr(sin, torch.float32, "sin"),
+                   _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(vt, torch.bfloat16, "vt"))
+
+    def set_qk_prep(self, fused: bool):
+        self._call("dit_set_qk_prep", 1 if fused else 0)
 
     def attention(self, q, k, vt, heads, S, o):
         self._call("dit_attention", _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"),

@@ -256,6 +256,27 @@ dit_status dit_modulated_norm_int8(dit_ctx *ctx, const float *x, int rows, const
 dit_status dit_linear_w8a8(dit_ctx *ctx, const int8_t *a, const float *a_scale, const int8_t *w,
                            const float *w_scale, int M, int N, int K, float *out);
 
+/* The q/k/v preparation as a pass of its own ([K4] s.4.4 runs it as a
+ * separate kernel over the stored projection; [GZ] prepOf): qkv bf16
+ * [S, 3*H*128] (the QKV product's output: all queries, all keys, all
+ * values, head j of each at columns j*128..) -> q, k bf16 [H, S, 128], each
+ * 128-wide head RMS-normed (fp32 statistics, the arch's qk_eps) times
+ * q_norm / k_norm [128] fp32 and turned by the adjacent-pair rotation with
+ * cos/sin [S, 64] fp32; vt bf16 [H, 128, Sp] the value heads transposed
+ * (Sp = S rounded up to 64; columns S..Sp-1 are not written).  H = the
+ * arch's heads; all pointers 16-byte aligned; 1 <= S <= max_rows. */
+dit_status dit_qk_prep(dit_ctx *ctx, const uint16_t *qkv, int S, const float *q_norm, const float *k_norm,
+                       const float *cos, const float *sin, uint16_t *q, uint16_t *k, uint16_t *vt);
+
+/* Which arm of the q/k preparation the sequential block forms run
+ * (dit_block_forward, dit_block_forward_runs, dit_block_forward_cached,
+ * the blocks of dit_denoise_step): fused = 1 (the default) folds the head
+ * norm and rotation into the QKV product's epilogue; fused = 0 stores the
+ * product's projection in bf16 and runs dit_qk_prep's pass (an extra bf16
+ * rounding of the projection, and 6 * S * hidden bytes more traffic).  The
+ * parallel and double-stream blocks always run the fused epilogue. */
+dit_status dit_set_qk_prep(dit_ctx *ctx, int fused);
+
 /* Joint attention ([K4] s.4.3): for each head h, o[:, h*128:(h+1)*128] =
  * bf16(softmax(q_h k_h^T / sqrt(128)) v_h), no mask.  q, k bf16
  * [heads, S, 128]; vt bf16 [heads, 128, Sp] with Sp = S rounded up to a
@@ -387,7 +408,8 @@ typedef enum {
     DIT_ST_PAR_OUT = 14,/* parallel block: [OUT | DOWN] product + gated residual */
     DIT_ST_POST = 15,   /* sandwich block: norm of a product's output, gate, residual */
     DIT_ST_QUANT = 16,  /* W8A8 block: attention / SwiGLU rows to INT8 */
-    DIT_NSTAGES = 17
+    DIT_ST_QK_PREP = 17,/* unfused arm: q/k head norm + rotary, v transposed */
+    DIT_NSTAGES = 18
 } dit_stage;
 
 /* Per-stage timing, a measurement aid ([K4] s.3: every op of the busy time

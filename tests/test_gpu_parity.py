@@ -379,6 +379,96 @@ def test_block_rejects_bad_rows(ctx_tiny):
         assert e.value.status == L.ERANGE
 
 
+# --------------------------------------------------------------- unfused q/k/v prep (B arm)
+
+@pytest.mark.parametrize("name", ["tiny", "s1088", "s4608"])
+def test_qk_prep_standalone(ctx_big, name):
+    """The prep pass on a stored bf16 projection: q and k against the
+    oracle's head norm and rotation, vt the exact transpose of the values,
+    and the rotation's special tables bit for bit."""
+    sh = synth.SHAPES[name]
+    S, H = sh.S, sh.heads
+    la, _ = arch_pair(sh)
+    ctx = ctx_big if name != "tiny" else L.Context(la, max_rows=S)
+    rng = np.random.default_rng(S + H)
+    qkv = synth.bf16_round(rng.standard_normal((S, 3 * H * 128)).astype(np.float32) * np.float32(2.0))
+    qn = synth.bf16_round(1.0 + 0.1 * rng.standard_normal(128).astype(np.float32))
+    kn = synth.bf16_round(1.0 + 0.1 * rng.standard_normal(128).astype(np.float32))
+    pos = O.positions(sh.L, sh.h, sh.w)
+    cs, sn = O.rope_tables(pos, sh.axes)
+    Sp = (S + 63) // 64 * 64
+    say("qk prep", name, S, H)
+
+    def run(c, s_):
+        q = torch.empty((H, S, 128), dtype=torch.bfloat16, device="cuda")
+        k = torch.empty_like(q)
+        vt = torch.zeros((H, 128, Sp), dtype=torch.bfloat16, device="cuda")
+        ctx.qk_prep(L.dev_bf16(qkv), S, L.dev_f32(qn), L.dev_f32(kn), L.dev_f32(c), L.dev_f32(s_), q, k, vt)
+        torch.cuda.synchronize()
+        return q, k, vt
+
+    q, k, vt = run(cs, sn)
+    heads = lambda cols: O.heads_of(cols, H, 128)
+    rows = np.arange(S) if S <= 1088 else synth.rows_sample(S, 200)
+    qr = O.head_prep(heads(qkv[rows, :H * 128]), qn, 1e-6, cs[rows], sn[rows])
+    kr = O.head_prep(heads(qkv[rows, H * 128:2 * H * 128]), kn, 1e-6, cs[rows], sn[rows])
+    compare(f"{name}/q", np_of(q)[:, rows], qr, bf16_stored=True)
+    compare(f"{name}/k", np_of(k)[:, rows], kr, bf16_stored=True)
+    v = heads(qkv[:, 2 * H * 128:])
+    assert (np_of(vt)[:, :, :S] == v.transpose(0, 2, 1)).all()
+    one, zero = np.ones_like(cs), np.zeros_like(cs)
+    bits = lambda t: t.view(torch.int16).cpu().numpy()
+    qi, ki, _ = run(one, zero)
+    qt, kt, _ = run(zero, one)
+    for a, b in ((bits(qi), bits(qt)), (bits(ki), bits(kt))):
+        assert (b[..., 0::2] == (a[..., 1::2] ^ np.int16(-0x8000))).all() and (b[..., 1::2] == a[..., 0::2]).all()
+    if ctx is not ctx_big:
+        ctx.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "s1088", "s4608"])
+def test_block_unfused_qk_prep(ctx_big, name):
+    """The block with the q/k/v prep as a pass of its own (the B arm): its
+    intermediates and output against the oracle, and the stage timers show
+    which arm ran."""
+    case = synth.block_case(name)
+    sh = case["shape"]
+    la, oa = arch_pair(sh)
+    ctx = ctx_big if name == "s4608" else L.Context(la, max_rows=sh.S)
+    say("block, unfused qk prep", name)
+    ctx.set_qk_prep(False)
+    try:
+        ctx.timing(True)
+        x, _, _ = _block_gpu(ctx, case)
+        tm = ctx.timing_read()
+        ctx.timing(False)
+    finally:
+        ctx.set_qk_prep(True)
+    assert tm["qk_prep"][1] == 1, "the prep pass did not run"
+    got = np_of(x)
+    cs, sn, vec = _oracle_inputs(case, oa)
+    if sh.S <= 1088:
+        inter = _intermediates(ctx, sh, sh.S)
+        y, ref = O.block_forward(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, keep=True)
+        for kk in ("q", "k", "v", "o", "a"):
+            compare(f"{name}/{kk}", inter[kk], ref[kk], bf16_stored=True)
+        compare(f"{name}/y", got, y)
+        compare(f"{name}/delta", got - case["x"], y - case["x"])
+    else:
+        rows = synth.rows_sample(sh.S, 48, L=sh.L)
+        y, o, x1, a = O.block_forward_rows(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, rows)
+        compare(f"{name}/y", got[rows], y)
+        compare(f"{name}/delta", got[rows] - case["x"][rows], y - case["x"][rows])
+    # the fused arm (the default) runs no prep pass
+    ctx.timing(True)
+    _block_gpu(ctx, case)
+    tm = ctx.timing_read()
+    ctx.timing(False)
+    assert tm["qk_prep"][1] == 0
+    if ctx is not ctx_big:
+        ctx.close()
+
+
 # --------------------------------------------------------------- parallel block
 
 def _parallel_case(name, **kw):
