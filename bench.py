@@ -13,6 +13,12 @@ Prints ONE JSON line on stdout (progress goes to stderr):
              (random-init bf16 weights), timed over I images;
   roofline   the dominant kernel's algorithmic TFLOP/s from HIP events around
              its launches, against the bf16 dense MFMA peak;
+  per_step_ms   p50 / min / max of single block forwards (HIP events per call);
+  hbm_kernels   the HBM-bound kernels' algorithmic bytes per launch over their
+             launch time (stage timers), against 8 TB/s;
+  calibration   secondary denominators measured on this machine: a chained large
+             bf16 GEMM rate (20 chained 8192^3 products, the vendor library)
+             and a 1 GiB device copy's bandwidth;
   cpu_baseline  the CPU oracle timed on this host on a bounded sample.
 """
 
@@ -50,6 +56,8 @@ def parse():
     p.add_argument("--no-sandwich", action="store_true", help="skip the sandwich block timing")
     p.add_argument("--no-cached", action="store_true", help="skip the timing of the step with cached reference rows")
     p.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 block timing")
+    p.add_argument("--no-unfused", action="store_true", help="skip the unfused q/k/v prep arm's timing")
+    p.add_argument("--no-calibration", action="store_true", help="skip the GEMM and copy calibration")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
                         "scale reference for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -75,7 +83,97 @@ def stage_flops(S, D, H, F):
 
 
 STAGE_SOURCE = {"qkv": "k_gemm.hip", "out": "k_gemm.hip", "up": "k_gemm.hip", "down": "k_gemm.hip",
-                "attn": "k_attn.hip", "mod": "k_misc.hip", "par_in": "k_gemm.hip", "par_out": "k_gemm.hip"}
+                "attn": "k_attn.hip", "mod": "k_misc.hip", "par_in": "k_gemm.hip", "par_out": "k_gemm.hip",
+                "norm": "k_misc.hip", "qk_prep": "k_misc.hip", "euler": "k_misc.hip"}
+
+
+def stage_bytes(S, D, H, F):
+    """Compulsory HBM bytes per launch of the block's stages at S rows (bf16
+    operands, fp32 residual): every operand read once, every result written
+    once, no re-reads."""
+    return {
+        "mod": 6 * D * D * 2,                                   # W_mod
+        "norm1": S * D * 4 + S * D * 2,                         # x in, h out
+        "norm2": S * D * 4 + S * D * 2,
+        "qkv": S * D * 2 + 3 * D * D * 2 + 3 * S * D * 2,       # h, W_qkv, q k v out
+        "attn": 3 * S * D * 2 + S * D * 2,                      # q k v in, o out
+        "out": S * D * 2 + D * D * 2 + 2 * S * D * 4,           # o, W_out, x read + write
+        "up": S * D * 2 + 2 * F * D * 2 + S * F * 2,            # h2, W_up, a out
+        "down": S * F * 2 + F * D * 2 + 2 * S * D * 4,          # a, W_down, x read + write
+        "qk_prep": 3 * S * D * 2 + 3 * S * D * 2,               # projection in, q k vt out
+    }
+
+
+def sh_blocks_bytes(block_bytes, blocks=32):
+    """Compulsory bytes of one denoise step of the 32-block DiT: its blocks'
+    (the small in/out products and the final layer are under 0.1 %)."""
+    return blocks * block_bytes
+
+
+def percentiles(ms):
+    a = sorted(ms)
+    return {"p50": round(a[len(a) // 2], 4), "min": round(a[0], 4), "max": round(a[-1], 4), "reps": len(a)}
+
+
+def time_each(torch, fn, reps):
+    """Per-call ms of fn() from a pair of HIP events around each call on the
+    current stream (fn's launches go to that stream)."""
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def calibration(torch):
+    """Secondary denominators (never replacing the spec peaks): the rate of 20
+    chained 8192^3 bf16 products through torch.matmul (the vendor GEMM
+    library), and the bandwidth of a 1 GiB device-to-device copy."""
+    n = 8192
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    c = torch.empty_like(a)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(20):
+        torch.matmul(a, b, out=c)
+    e1.record(st)
+    torch.cuda.synchronize()
+    gemm = 20 * 2 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(st)
+    torch.cuda.synchronize()
+    copy = 10 * 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gemm_bf16_chained_tflops": round(gemm, 1), "gemm_note": "20 chained 8192^3 bf16 torch.matmul",
+            "copy_gbs": round(copy, 1), "copy_note": "1 GiB device-to-device copy, read + write bytes"}
+
+
+def hbm_rows(stages, counts_bytes):
+    """{stage: {ms, bytes, gbs, frac}} for the HBM-bound stages present."""
+    out = {}
+    for k, nbytes in counts_bytes.items():
+        if k in stages and stages[k] > 0:
+            gbs = nbytes / (stages[k] * 1e-3) / 1e9
+            out[k] = {"ms": round(stages[k], 4), "bytes": int(nbytes), "gbs": round(gbs, 1),
+                      "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def source_sha(name):
@@ -133,7 +231,7 @@ def summarize_counters(fetch_csv, write_csv, out_json):
         pending = None
         for d in order:
             n = names[d]
-            pp = re.search(r"k_gemm_p3<(\d), (true|false), false>", n)   # the bf16 form
+            pp = re.search(r"k_gemm_p3<(\d), (true|false), false, false>", n)   # the bf16 form
             epi = pp or re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
             epi = int(epi.group(1)) if epi else None
             if pp and pp.group(2) == "true":
@@ -150,6 +248,12 @@ def summarize_counters(fetch_csv, write_csv, out_json):
                 stage_of[d] = "down" if pending == "up" else "out"
             elif "k_gemv" in n:
                 stage_of[d] = "mod"
+            elif "k_modnorm" in n:
+                stage_of[d] = "norm"
+            elif "k_qk_prep" in n:
+                stage_of[d] = "qk_prep"
+            elif "k_euler" in n:
+                stage_of[d] = "euler"
             if d in stage_of:
                 pending = stage_of[d]
         acc = collections.defaultdict(list)
@@ -273,6 +377,12 @@ def main():
     ctx.timing(False)
     stages = {k: v[0] / v[1] for k, v in tm.items() if v[1]}
     log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+    per_step = percentiles(time_each(torch, lambda: ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N),
+                                     max(20, args.steps)))
+    log(f"single block forwards: p50 {per_step['p50']:.3f} ms, min {per_step['min']:.3f} ms")
+    sb_bytes = stage_bytes(S, D, H, F)
+    block_bytes = sum(v for k, v in sb_bytes.items() if k != "qk_prep")
+    hbm = hbm_rows(stages, {k: sb_bytes[k] for k in ("mod", "norm1", "norm2")})
     dom = max((k for k in stages if k in fl), key=lambda k: stages[k])
     dom_tf = fl[dom] / (stages[dom] * 1e-3) / 1e12
     roofline = {"kernel": f"{dom} product" if dom not in ("attn", "mod") else dom, "bound": "mfma",
@@ -384,7 +494,30 @@ def main():
         sw = {"ms": round(mss, 4), "tflops": round(sw_tf, 2), "frac_bf16_peak": round(sw_tf / PEAK_BF16_TFLOPS, 4),
               "flops_per_step": total_flops, "stages_ms_per_step": stage_split(ctx, sfwd, args.steps)}
         log(f"sandwich block: {mss:.3f} ms  {sw_tf:.1f} TFLOP/s")
+        post = sw["stages_ms_per_step"].get("post")
+        if post:    # two launches a block: y read, x read and written, fp32 [S, D] each
+            hbm.update(hbm_rows({"post": post / 2}, {"post": 12 * S * D}))
         del bws, xs, sb
+
+    # ---------------------------------------------------------------- unfused q/k/v prep (B arm)
+    unfused = None
+    if not args.no_unfused:
+        log("block with the q/k/v prep as a pass of its own (unfused arm)")
+        bwu = L.BlockWeights.from_host(case["block"])
+        xu = L.dev_f32(case["x"])
+        ctx.set_qk_prep(False)
+
+        def ufwd():
+            ctx.block_forward(bwu, xu, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        msu = time_call(torch, ufwd, args.steps, args.warmup)
+        u_st = stage_split(ctx, ufwd, args.steps)
+        ctx.set_qk_prep(True)
+        u_tf = total_flops / (msu * 1e-3) / 1e12
+        unfused = {"ms": round(msu, 4), "tflops": round(u_tf, 2), "frac_bf16_peak": round(u_tf / PEAK_BF16_TFLOPS, 4),
+                   "stages_ms_per_step": u_st, "arm": "unfused (QKV product stores bf16, then k_qk_prep)"}
+        hbm.update(hbm_rows(u_st, {"qk_prep": sb_bytes["qk_prep"]}))
+        log(f"unfused-arm block: {msu:.3f} ms  {u_tf:.1f} TFLOP/s; prep pass {u_st.get('qk_prep', 0):.4f} ms")
+        del bwu, xu
     del case
     torch.cuda.empty_cache()
 
@@ -395,9 +528,11 @@ def main():
         c8 = synth.block_case("s4608_int8")
         bw8 = L.BlockWeights.from_host(c8["block"])
         x8 = L.dev_f32(c8["x"])
-        ms8 = time_blocks(L, torch, ctx, bw8, x8, seq, sh, max(3, args.steps // 2), 2)
+        ms8 = time_blocks(L, torch, ctx, bw8, x8, seq, sh, args.steps, args.warmup)
         int8_tf = total_flops / (ms8 * 1e-3) / 1e12
-        log(f"int8 block: {ms8:.3f} ms  {int8_tf:.1f} TFLOP/s")
+        int8_st = stage_split(ctx, lambda: ctx.block_forward(bw8, x8, seq.vec, seq.cos, seq.sin, sh.L, sh.N), args.steps)
+        log(f"int8 block: {ms8:.3f} ms  {int8_tf:.1f} TFLOP/s; stages " +
+            ", ".join(f"{k} {v:.3f}" for k, v in int8_st.items()))
         del bw8, x8, c8
         torch.cuda.empty_cache()
 
@@ -423,14 +558,34 @@ def main():
                            "frac": round(up_tops / PEAK_INT8_TOPS, 4), "ops_per_launch": up_ops,
                            "avg_ms": w_st["up"]}}
         log(f"W8A8 block: {msw:.3f} ms  {w_tf:.1f} TFLOP/s (int8 ops)")
-        del bww, xw, cw
+        q_st = w_st.get("quant")
+        if q_st:    # two launches a block: o (D wide) and a (F wide), bf16 in, INT8 + scale out
+            hbm.update(hbm_rows({"quant": q_st / 2}, {"quant": (3 * S * D + 3 * S * F) // 2 + 8 * S}))
+        bwr = L.BlockWeights.from_host(cw["block"], rotated=True)
+
+        def rfwd8():
+            ctx.block_forward(bwr, xw, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        msr8 = time_call(torch, rfwd8, args.steps, args.warmup)
+        r_tf = total_flops / (msr8 * 1e-3) / 1e12
+        w8["convrot"] = {"ms": round(msr8, 4), "tflops": round(r_tf, 2),
+                         "stages_ms_per_step": stage_split(ctx, rfwd8, args.steps),
+                         "weights": "INT8 rows in the rotated basis; inputs rotated by the regular Hadamard of 256"}
+        log(f"W8A8 block with ConvRot: {msr8:.3f} ms  {r_tf:.1f} TFLOP/s (int8 ops)")
+        del bww, xw, cw, bwr
         torch.cuda.empty_cache()
     ctx.close()
+
+    calib = None if args.no_calibration else calibration(torch)
+    if calib:
+        log(f"calibration: chained 8192^3 bf16 GEMM {calib['gemm_bf16_chained_tflops']} TFLOP/s, "
+            f"1 GiB copy {calib['copy_gbs']} GB/s")
 
     # ---------------------------------------------------------------- whole image
     img = img8 = None
     if not args.no_denoise:
         img = bench_images(torch, L, synth, args.images)
+        if img.get("euler_ms"):   # x read and written, v read: fp32 [N, 64]
+            hbm.update(hbm_rows({"euler": img["euler_ms"]}, {"euler": 3 * 4 * sh.N * 64}))
         if not args.no_w8a8:
             img8 = bench_images(torch, L, synth, args.images, w8a8=True)
 
@@ -455,9 +610,17 @@ def main():
                    "L": sh.L, "N": sh.N, "hidden": D, "heads": H, "head_dim": 128, "ffn": F,
                    "flops_per_step": total_flops},
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "block_bytes": block_bytes,
+        "frac_hbm": round(block_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "per_step_ms": per_step,
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
+        "hbm_kernels": hbm,
+        "calibration": calib,
         "int8_block_tflops": None if int8_tf is None else round(int8_tf, 2),
+        "int8_block": None if int8_tf is None else {"ms": round(ms8, 4), "tflops": round(int8_tf, 2),
+                                                    "stages_ms_per_step": int8_st},
+        "unfused_qk_prep_block": unfused,
         "parallel_block": par,
         "double_block": dbl,
         "runs_block": runs_res,
@@ -466,6 +629,12 @@ def main():
         "w8a8_block": w8,
     }
     if img:
+        img = dict(img)
+        img.pop("euler_ms", None)
+        img["image_frac_bf16_peak"] = round(img["image_tflops"] / PEAK_BF16_TFLOPS, 4)
+        img_bytes = 4 * sh_blocks_bytes(block_bytes)
+        img["image_bytes"] = img_bytes
+        img["image_frac_hbm"] = round(img_bytes / (img["ms_per_image"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         out.update(img)
     if img8:
         out["w8a8_image"] = {k: img8[k] for k in ("images_per_s", "ms_per_image", "image_finite", "image_workload")}
@@ -537,6 +706,20 @@ def bench_images(torch, L, synth, images, w8a8=False):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / images
     finite = bool(torch.isfinite(x).all().item())
+
+    # the per-image prologue on its own (positions, tables, text rows), and
+    # the Euler update's launch time from the stage timers
+    def prologue():
+        ctx.positions(sh.L, sh.h, sh.w, pos)
+        ctx.rope_tables(pos, S, cs, sn)
+        ctx.prologue(model, ctx_feats, sh.L, txt)
+    pro = percentiles(time_each(torch, prologue, 10))
+    ctx.timing(True)
+    x.copy_(x0)
+    one_image(x)
+    tm = ctx.timing_read()
+    ctx.timing(False)
+    euler_ms = tm["euler"][0] / tm["euler"][1] if tm["euler"][1] else None
     blk = sum(stage_flops(S, D, H, F).values())
     img_flops = 4 * (sh.blocks * blk + 2 * sh.N * lat * D + 2 * sh.N * D * lat + 2 * D * 256
                      + 2 * D * D + 2 * 2 * D * D) + 2 * sh.L * sh.text_dim * D
@@ -546,6 +729,7 @@ def bench_images(torch, L, synth, images, w8a8=False):
     del model, blocks, top
     torch.cuda.empty_cache()
     return {"images_per_s": round(1000.0 / ms, 4), "ms_per_image": round(ms, 2),
+            "prologue_ms": pro, "steps_ms": round(ms - pro["p50"], 2), "euler_ms": euler_ms,
             "image_tflops": round(img_flops / ms / 1e9, 2), "image_flops": img_flops,
             "image_workload": "32-block DiT, 4 Euler steps (sigmas 1, .75, .5, .25, 0), L=512 + N=4096, "
                               f"latent 64, text features 4096-d, batch 1, random-init {'W8A8' if w8a8 else 'bf16'} "
@@ -581,8 +765,12 @@ def cpu_baseline():
     dt = time.perf_counter() - t0
     flops = O.block_flops(sh.S, oa) * reps
     log(f"cpu oracle: {dt:.1f} s for {reps} block(s), {flops / 1e9:.1f} GFLOP ({threads} threads)")
+    per_block = dt / reps
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2), "blocks": reps,
+            "image_seconds_extrapolated": round(4 * 32 * per_block, 1),
+            "image_note": "extrapolated: 4 steps x 32 blocks x the measured seconds per block (the in/out products "
+                          "and the text rows are under 0.1 % of the work)",
             "sample": f"{reps} whole block forward(s) of the float64 NumPy oracle on the same 1024-px block "
                       "(L=512 + N=4096 rows, hidden 3072, 24x128 heads, ffn 12288), 1652.6 GFLOP each, "
                       "repeated until 10 s of CPU work (at most 8)"}
