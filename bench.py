@@ -64,9 +64,10 @@ def parse():
     p.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                           "profiles", "traffic.json"),
                    help="measured HBM bytes per launch of the dominant kernel (from counter runs)")
-    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+    p.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE run and a "
-                        "WRITE_SIZE run (both with --copy-calibration) into --traffic-json")
+                        "WRITE_SIZE run (both with --copy-calibration), and optionally of a run of the MFMA "
+                        "counters, into --traffic-json")
     return p.parse_args()
 
 
@@ -84,7 +85,8 @@ def stage_flops(S, D, H, F):
 
 STAGE_SOURCE = {"qkv": "k_gemm.hip", "out": "k_gemm.hip", "up": "k_gemm.hip", "down": "k_gemm.hip",
                 "attn": "k_attn.hip", "mod": "k_misc.hip", "par_in": "k_gemm.hip", "par_out": "k_gemm.hip",
-                "norm": "k_misc.hip", "qk_prep": "k_misc.hip", "euler": "k_misc.hip"}
+                "norm": "k_misc.hip", "qk_prep": "k_misc.hip", "euler": "k_misc.hip", "quant": "k_misc.hip",
+                "post": "k_misc.hip"}
 
 
 def stage_bytes(S, D, H, F):
@@ -199,76 +201,120 @@ def traffic_for(args, stage):
     return rec.get("bytes_per_launch")
 
 
-def summarize_counters(fetch_csv, write_csv, out_json):
-    """Per-launch HBM bytes of the block's kernels from rocprofv3 counter
-    runs.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled so
-    that the 1 GiB calibration copy reads and writes exactly 1 GiB.  The
-    block's launches come in a fixed order (GEMV, norm, QKV, attention, OUT,
-    norm, UP, DOWN), which tells the OUT and DOWN launches of the shared
-    gated-residual product apart."""
+def summarize_counters(fetch_csv, write_csv, out_json, mfma_csv=None):
+    """Per-launch HBM bytes and matrix-core use of the path's kernels from
+    rocprofv3 counter runs (one counter set per run).  FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are each scaled so that the 1 GiB
+    calibration copy reads and writes exactly 1 GiB.  The optional third run
+    holds SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 / _I8.  GRBM_GUI_ACTIVE arrives summed over
+    the chip's 8 XCDs: per XCD it is the dispatch's active cycles, and over
+    the dispatch's duration it gives the clock the chip ran at.  The matrix
+    cores' busy fraction is busy cycles / (active cycles x 1024 SIMDs); the
+    counted MFMA work is MOPS x 512 FLOP (or int8 ops).  Kernels are keyed by stage: the block's
+    launches come in a fixed order (GEMV, norm, QKV, attention, OUT, norm,
+    UP, DOWN), which tells the OUT and DOWN launches of the shared
+    gated-residual product apart; the bf16 ping-pong forms are keyed by the
+    stage alone, the int8 block-32 (B32) and W8A8 (I8) forms with a suffix."""
     import csv
     import collections
     import re
 
-    def load(path, counter):
-        per = collections.defaultdict(float)
+    def load(path, counters):
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
         names = {}
         for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
+            c = r["Counter_Name"]
+            if c not in counters:
                 continue
             d = int(r["Dispatch_Id"])
-            per[d] += float(r["Counter_Value"])
+            per[d][c] += float(r["Counter_Value"])
+            per[d]["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
             names[d] = r["Kernel_Name"]
         return per, names
 
+    def stages_of(names):
+        stage_of, pending = {}, None
+        for d in sorted(d for d in names if "dit::" in names[d]):
+            n = names[d]
+            pp = re.search(r"k_gemm_p3<(\d), (true|false), (true|false), (true|false)>", n)
+            rg = re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
+            epi = int(pp.group(1)) if pp else int(rg.group(1)) if rg else None
+            suffix = ""
+            if pp and pp.group(3) == "true":
+                suffix = "_w8a8"
+            elif pp and pp.group(4) == "true":
+                suffix = "_b32"
+            st = None
+            if pp and pp.group(2) == "true":
+                st = "par_out"                   # parallel block: [OUT | DOWN] over [o | a]
+            elif epi == 4:
+                st = "par_in"                    # parallel block: [QKV | UP]
+            elif epi == 3:
+                st = "qkv"
+            elif epi == 2:
+                st = "up"
+            elif epi == 1:
+                st = "down" if pending == "up" else "out"
+            elif "k_attention" in n:
+                st = "attn"
+            elif "k_gemv" in n:
+                st = "mod"
+            elif "k_modnorm" in n:
+                st = "norm"
+            elif "k_qk_prep" in n:
+                st = "qk_prep"
+            elif "k_euler" in n:
+                st = "euler"
+            elif "k_quant_rows" in n:
+                st = "quant"
+            elif "k_post_norm_gate" in n:
+                st = "post"
+            if st is None:
+                continue
+            if st != "quant":          # a W8A8 block quantizes o and a between its products
+                pending = st
+            if pp or rg:
+                st = st + (suffix if pp else "_regstaged")
+            stage_of[d] = st
+        return stage_of
+
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        per, names = load(path, counter)
-        copy_kib = sum(v for d, v in per.items() if "copyBuffer" in names[d])
+        per, names = load(path, {counter})
+        copy_kib = sum(v[counter] for d, v in per.items() if "copyBuffer" in names[d])
         scale = (1 << 30) / 1024.0 / copy_kib if copy_kib else None
-        order = sorted(d for d in per if "dit::" in names[d])
-        stage_of = {}
-        pending = None
-        for d in order:
-            n = names[d]
-            pp = re.search(r"k_gemm_p3<(\d), (true|false), false, false>", n)   # the bf16 form
-            epi = pp or re.search(r"k_gemm<\d+, \d+, (?:true|false), (\d)>", n)
-            epi = int(epi.group(1)) if epi else None
-            if pp and pp.group(2) == "true":
-                stage_of[d] = "par_out"          # parallel block: [OUT | DOWN] over [o | a]
-            elif epi == 4:
-                stage_of[d] = "par_in"           # parallel block: [QKV | UP]
-            elif epi == 3:
-                stage_of[d] = "qkv"
-            elif "k_attention" in n:
-                stage_of[d] = "attn"
-            elif epi == 2:
-                stage_of[d] = "up"
-            elif epi == 1:
-                stage_of[d] = "down" if pending == "up" else "out"
-            elif "k_gemv" in n:
-                stage_of[d] = "mod"
-            elif "k_modnorm" in n:
-                stage_of[d] = "norm"
-            elif "k_qk_prep" in n:
-                stage_of[d] = "qk_prep"
-            elif "k_euler" in n:
-                stage_of[d] = "euler"
-            if d in stage_of:
-                pending = stage_of[d]
         acc = collections.defaultdict(list)
-        for d, st in stage_of.items():
-            acc[st].append(per[d])
+        for d, st in stages_of(names).items():
+            acc[st].append(per[d][counter])
         for st, v in acc.items():
             rec = res.setdefault(st, {})
             rec[counter.lower() + "_kib_mean"] = sum(v) / len(v)
             rec[counter.lower() + "_scale"] = scale
             rec["launches"] = len(v)
+    if mfma_csv:
+        cs = {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_I8"}
+        per, names = load(mfma_csv, cs)
+        acc = collections.defaultdict(list)
+        for d, st in stages_of(names).items():
+            acc[st].append(per[d])
+        for st, v in acc.items():
+            rec = res.setdefault(st, {})
+            xcd = 8
+            busy = [x["SQ_VALU_MFMA_BUSY_CYCLES"] / (x["GRBM_GUI_ACTIVE"] / xcd * 1024) for x in v if x["GRBM_GUI_ACTIVE"]]
+            ghz = [x["GRBM_GUI_ACTIVE"] / xcd / x["ns"] for x in v if x["ns"] > 0]
+            rec["mfma_busy_frac"] = round(sum(busy) / len(busy), 4) if busy else None
+            rec["clock_ghz"] = round(sum(ghz) / len(ghz), 3) if ghz else None
+            rec["mfma_bf16_flop_mean"] = sum(x["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for x in v) / len(v) * 512
+            rec["mfma_i8_op_mean"] = sum(x["SQ_INSTS_VALU_MFMA_MOPS_I8"] for x in v) / len(v) * 512
+            rec["mfma_launches"] = len(v)
     for st, rec in res.items():
         if rec.get("fetch_size_scale") and rec.get("write_size_scale"):
             rec["bytes_per_launch"] = int(1024 * (rec["fetch_size_kib_mean"] * rec["fetch_size_scale"]
                                                   + rec["write_size_kib_mean"] * rec["write_size_scale"]))
-        rec["source_sha256"] = source_sha(STAGE_SOURCE[st])
+        base = st.split("_")[0] if st.split("_")[0] in STAGE_SOURCE else st
+        src = STAGE_SOURCE.get(base) or STAGE_SOURCE.get(st) or ("k_gemm.hip" if "regstaged" in st else "k_misc.hip")
+        rec["source_sha256"] = source_sha(src)
     with open(out_json, "w") as f:
         json.dump(res, f, indent=1, sort_keys=True)
     print(json.dumps(res, indent=1, sort_keys=True))
@@ -317,7 +363,8 @@ def stage_split(ctx, fn, steps):
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.traffic_json)
+        c = args.summarize_counters
+        summarize_counters(c[0], c[1], args.traffic_json, c[2] if len(c) > 2 else None)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path is sized for one "
