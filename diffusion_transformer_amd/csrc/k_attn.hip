@@ -191,8 +191,10 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     // 32-key steps; its first V^T fragments are already in fa), then
     // S^T = K Q^T of tile tk (64 keys x 32 queries; s[tk][tq][r] holds the
     // fp32 score q.k of key 32*(tk/2) + 8g + 4*(tk%2) + r).
-    // The LDS reads go in quarters of 4 fragments, each issued two quarters
-    // before the MFMAs that use it (at most 8 reads in flight).
+    // The LDS reads go in quarters of 4 fragments, written two quarters
+    // before the MFMAs that use them; the compiler interleaves the reads and
+    // the MFMAs within the phase (no scheduling fences: measured 4 % faster
+    // than keeping each quarter's reads ahead of the MFMAs by a fence).
     bf16x8 fa[8], fb[8];
     auto prefetch_v = [&](int t) {   // V^T fragments of keys 8g .. 8g+7 of tile t >= -1
         const u32x4 *L = Vb + ((t + NVB) % NVB) * V_U4;
@@ -236,7 +238,7 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     auto mma = [&](int tv, int tk) {
         const u32x4 *LK = Kb + (tk % NKB) * K_U4;
         const u32x4 *LV = Vb + ((tv + NVB) % NVB) * V_U4;
-#define DIT_STEP(read, use) do { read; __builtin_amdgcn_sched_barrier(0); use; __builtin_amdgcn_sched_barrier(0); } while (0)
+#define DIT_STEP(read, use) do { read; use; } while (0)
         DIT_STEP(read_v4(fb, LV, 1, 0), pv4(fa, 0, 0));
         DIT_STEP(read_v4(fb + 4, LV, 1, 1), pv4(fa + 4, 0, 1));
         DIT_STEP(read_k4(fa, LK, 0), pv4(fb, 1, 0));
