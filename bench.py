@@ -234,7 +234,7 @@ def summarize_counters(fetch_csv, write_csv, out_json, mfma_csv=None):
         return per, names
 
     def stages_of(names):
-        stage_of, pending = {}, None
+        stage_of, pending, after_dq = {}, None, False
         for d in sorted(d for d in names if "dit::" in names[d]):
             n = names[d]
             pp = re.search(r"k_gemm_p3<(\d), (true|false), (true|false), (true|false)>", n)
@@ -270,11 +270,18 @@ def summarize_counters(fetch_csv, write_csv, out_json, mfma_csv=None):
                 st = "quant"
             elif "k_post_norm_gate" in n:
                 st = "post"
+            elif "k_dequant_bf16" in n:
+                st = "dequant"
             if st is None:
                 continue
-            if st != "quant":          # a W8A8 block quantizes o and a between its products
+            if st == "dequant":        # the bf16 product after it runs on dequantised int8 weights
+                after_dq = True
+            elif st != "quant":        # a W8A8 block quantizes o and a between its products
                 pending = st
             if pp or rg:
+                if after_dq and pp:
+                    suffix = "_dq"
+                after_dq = False
                 st = st + (suffix if pp else "_regstaged")
             stage_of[d] = st
         return stage_of
@@ -569,7 +576,7 @@ def main():
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- int8 block
-    int8_tf = None
+    int8_tf = int8i = None
     if not args.no_int8:
         log("int8-weight block")
         c8 = synth.block_case("s4608_int8")
@@ -578,8 +585,22 @@ def main():
         ms8 = time_blocks(L, torch, ctx, bw8, x8, seq, sh, args.steps, args.warmup)
         int8_tf = total_flops / (ms8 * 1e-3) / 1e12
         int8_st = stage_split(ctx, lambda: ctx.block_forward(bw8, x8, seq.vec, seq.cos, seq.sin, sh.L, sh.N), args.steps)
-        log(f"int8 block: {ms8:.3f} ms  {int8_tf:.1f} TFLOP/s; stages " +
+        log(f"int8 block (dequantisation pass, bf16 products): {ms8:.3f} ms  {int8_tf:.1f} TFLOP/s; stages " +
             ", ".join(f"{k} {v:.3f}" for k, v in int8_st.items()))
+        if int8_st.get("dequant"):      # codes + scales read, bf16 written: 2.0625 + 2 bytes a weight
+            nw = 3 * D * D + D * D + 2 * F * D + F * D
+            hbm.update(hbm_rows({"dequant": int8_st["dequant"] / 4}, {"dequant": nw // 4 * (1 + 1 / 16 + 2)}))
+        ctx.set_int8_products(True)
+        try:
+            ms8i = time_blocks(L, torch, ctx, bw8, x8, seq, sh, args.steps, args.warmup)
+            int8i_st = stage_split(ctx, lambda: ctx.block_forward(bw8, x8, seq.vec, seq.cos, seq.sin, sh.L, sh.N),
+                                   args.steps)
+        finally:
+            ctx.set_int8_products(False)
+        int8i = {"ms": round(ms8i, 4), "tflops": round(total_flops / (ms8i * 1e-3) / 1e12, 2),
+                 "stages_ms_per_step": int8i_st,
+                 "arm": "codes converted inside each product (dit_set_int8_products(ctx, 1))"}
+        log(f"int8 block (codes converted inside the products): {ms8i:.3f} ms")
         del bw8, x8, c8
         torch.cuda.empty_cache()
 
@@ -666,7 +687,9 @@ def main():
         "calibration": calib,
         "int8_block_tflops": None if int8_tf is None else round(int8_tf, 2),
         "int8_block": None if int8_tf is None else {"ms": round(ms8, 4), "tflops": round(int8_tf, 2),
-                                                    "stages_ms_per_step": int8_st},
+                                                    "stages_ms_per_step": int8_st,
+                                                    "arm": "dequantisation pass per weight, then bf16 products",
+                                                    "in_product": int8i},
         "unfused_qk_prep_block": unfused,
         "parallel_block": par,
         "double_block": dbl,

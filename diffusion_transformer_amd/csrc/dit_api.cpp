@@ -50,6 +50,16 @@ struct dit_ctx {
     // QK-norm + rotary inside the QKV product's epilogue (true), or the
     // product's bf16 projection and then the separate prep pass
     bool qk_fused = true;
+    // int8 block-32 weights: converted inside the product (true), or by a
+    // pass into wdq (two slots of wdq_slot bf16 values, allocated on first
+    // use) before a bf16 product
+    bool int8_in_product = false;
+    uint16_t *wdq = nullptr;
+    // a second stream of the context (default priority) on which the
+    // sequential block dequantises its later weights while the first
+    // products run; the events order it against the context's stream
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_ready[4] = {};
     std::string err;
     // stage timing
     bool timing = false;
@@ -125,10 +135,11 @@ struct Stage {
     dit_ctx *c;
     int stage;
     hipEvent_t a = nullptr;
-    Stage(dit_ctx *ctx, int s) : c(ctx), stage(s) {
+    hipStream_t hs;
+    Stage(dit_ctx *ctx, int s, hipStream_t on = nullptr) : c(ctx), stage(s), hs(on ? on : ctx->stream) {
         if (!c->timing) return;
         a = take_event(c);
-        if (a) hipEventRecord(a, c->stream);
+        if (a) hipEventRecord(a, hs);
     }
     ~Stage() {
         if (!a) return;
@@ -137,7 +148,7 @@ struct Stage {
             c->spare.push_back(a);
             return;
         }
-        hipEventRecord(b, c->stream);
+        hipEventRecord(b, hs);
         c->recs.push_back({stage, a, b});
     }
 };
@@ -212,6 +223,71 @@ dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bo
     return DIT_OK;
 }
 
+// The weight operand of product w of block b (N outputs, K inputs) as the
+// product launch takes it: bf16 weights as they are; int8 block-32 weights
+// either as codes and scales (converted inside the product) or, by default,
+// dequantised first into the context's scratch: two sets (the double-stream
+// block's streams) of one slot per block weight, each of that weight's size.
+struct WeightArg {
+    const void *w;
+    const uint16_t *scale;
+    bool w8;
+};
+size_t wdq_elems(const dit_ctx *c, int w) {
+    const size_t D = c->arch.hidden, F = c->arch.ffn;
+    const size_t n[4] = {3 * D * D, D * D, 2 * F * D, F * D};
+    return n[w];
+}
+uint16_t *wdq_slot(const dit_ctx *c, int set, int w) {
+    size_t off = set * (wdq_elems(c, 0) + wdq_elems(c, 1) + wdq_elems(c, 2) + wdq_elems(c, 3));
+    for (int i = 0; i < w; ++i) off += wdq_elems(c, i);
+    return c->wdq + off;
+}
+dit_status ensure_wdq(dit_ctx *c) {
+    if (c->wdq) return DIT_OK;
+    const size_t n = 2 * (wdq_elems(c, 0) + wdq_elems(c, 1) + wdq_elems(c, 2) + wdq_elems(c, 3));
+    void *p = nullptr;
+    if (hipMalloc(&p, n * sizeof(uint16_t)) != hipSuccess)
+        return fail(c, DIT_ENOMEM, "int8 dequantisation scratch (%zu bytes) failed", n * sizeof(uint16_t));
+    c->wdq = static_cast<uint16_t *>(p);
+    return DIT_OK;
+}
+bool codes_aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+dit_status ensure_side(dit_ctx *c) {
+    if (c->side) return DIT_OK;
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess)
+        return fail(c, DIT_EDEVICE, "creating the dequantisation stream failed");
+    bool ok = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) == hipSuccess;
+    for (hipEvent_t &e : c->ev_ready) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+    c->side = s;
+    return ok ? DIT_OK : fail(c, DIT_EDEVICE, "creating the dequantisation events failed");
+}
+// Dequantises int8 codes wp (N x K, block-32 scales) into dst of cap
+// values on stream hs when the context takes that path and it applies
+// (16-byte aligned codes that fit); otherwise the codes themselves.
+dit_status weight_arg_of(dit_ctx *c, const void *wp, const uint16_t *scale, bool int8, int N, int K, uint16_t *dst,
+                         size_t cap, hipStream_t hs, WeightArg *out) {
+    *out = WeightArg{wp, nullptr, false};
+    if (!int8) return DIT_OK;
+    if (c->int8_in_product || !codes_aligned(wp) || static_cast<size_t>(N) * K > cap) {
+        *out = WeightArg{wp, scale, true};
+        return DIT_OK;
+    }
+    {
+        Stage t(c, DIT_ST_DEQUANT, hs);
+        DIT_LAUNCH(c, launch_dequant_bf16(static_cast<const int8_t *>(wp), scale, N, K, dst, hs), "int8 dequantisation");
+    }
+    *out = WeightArg{dst, nullptr, false};
+    return DIT_OK;
+}
+dit_status weight_arg(dit_ctx *c, const dit_block *b, int w, int N, int K, int set, WeightArg *out) {
+    const bool int8 = b->wtype == DIT_W_INT8_B32;
+    if (int8 && !c->int8_in_product) DIT_TRY(ensure_wdq(c));
+    return weight_arg_of(c, b->w[w], bscale(b, w), int8, N, K, int8 && c->wdq ? wdq_slot(c, set, w) : nullptr,
+                         int8 && c->wdq ? wdq_elems(c, w) : 0, c->stream, out);
+}
+
 dit_status check_rows(dit_ctx *c, int L, int N) {
     if (L < 0 || L > 512) return fail(c, DIT_ERANGE, "L = %d outside 0..512", L);
     if (N < 1 || N > 4096) return fail(c, DIT_ERANGE, "N = %d outside 1..4096", N);
@@ -270,45 +346,60 @@ dit_status parallel_block_forward(dit_ctx *c, const dit_block *b, float *x, cons
     GemmEpi gk = g;
     gk.w2 = static_cast<const uint16_t *>(b->w[3]);
     gk.k_split = D;
-    const bool fused = !w8 && gemm_pingpong_ok(S, 3 * D + 2 * F, D, false, fin, true) &&
+    // the fused pair of products takes bf16 weights: bf16 blocks, and int8
+    // block-32 blocks dequantised by a pass first (16-byte aligned codes)
+    bool dq = !c->int8_in_product;
+    for (int i = 0; i < 4; ++i) dq = dq && (reinterpret_cast<uintptr_t>(b->w[i]) & 15) == 0;
+    const bool fused = (!w8 || dq) && gemm_pingpong_ok(S, 3 * D + 2 * F, D, false, fin, true) &&
                        gemm_pingpong_ok(S, D, D + F, false, gk, true);
+    WeightArg wa{}, wb{};
     if (fused) {
+        DIT_TRY(weight_arg(c, b, 0, 3 * D, D, 0, &wa));
+        DIT_TRY(weight_arg(c, b, 2, 2 * F, D, 0, &wb));
+        fin.w2 = static_cast<const uint16_t *>(wb.w);
         {
             Stage t(c, DIT_ST_PAR_IN);
-            DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], nullptr, false, S, 3 * D + 2 * F, D, fin, st, true), "qkv+up");
+            DIT_LAUNCH(c, launch_gemm(c->h, wa.w, nullptr, false, S, 3 * D + 2 * F, D, fin, st, true), "qkv+up");
         }
         {
             Stage t(c, DIT_ST_ATTN);
             DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->oa, D + F, st), "attention");
         }
+        DIT_TRY(weight_arg(c, b, 1, D, D, 0, &wa));
+        DIT_TRY(weight_arg(c, b, 3, D, F, 0, &wb));
+        gk.w2 = static_cast<const uint16_t *>(wb.w);
         {
             Stage t(c, DIT_ST_PAR_OUT);
-            DIT_LAUNCH(c, launch_gemm(c->oa, b->w[1], nullptr, false, S, D, D + F, gk, st, true), "out+down");
+            DIT_LAUNCH(c, launch_gemm(c->oa, wa.w, nullptr, false, S, D, D + F, gk, st, true), "out+down");
         }
         return DIT_OK;
     }
+    DIT_TRY(weight_arg(c, b, 0, 3 * D, D, 0, &wa));
     {
         Stage t(c, DIT_ST_QKV);
-        DIT_LAUNCH(c, launch_gemm(c->h, b->w[0], bscale(b, 0), w8, S, 3 * D, D, e, st, true), "qkv");
+        DIT_LAUNCH(c, launch_gemm(c->h, wa.w, wa.scale, wa.w8, S, 3 * D, D, e, st, true), "qkv");
     }
     GemmEpi u{};
     u.kind = EPI_SWIGLU;
     u.act = c->a;
+    DIT_TRY(weight_arg(c, b, 2, 2 * F, D, 0, &wa));
     {
         Stage t(c, DIT_ST_UP);
-        DIT_LAUNCH(c, launch_gemm(c->h, b->w[2], bscale(b, 2), w8, S, 2 * F, D, u, st, true), "up");
+        DIT_LAUNCH(c, launch_gemm(c->h, wa.w, wa.scale, wa.w8, S, 2 * F, D, u, st, true), "up");
     }
     {
         Stage t(c, DIT_ST_ATTN);
         DIT_LAUNCH(c, launch_attention(c->q, c->k, c->vt, H, S, Sp, c->o, D, st), "attention");
     }
+    DIT_TRY(weight_arg(c, b, 1, D, D, 0, &wa));
     {
         Stage t(c, DIT_ST_OUT);
-        DIT_LAUNCH(c, launch_gemm(c->o, b->w[1], bscale(b, 1), w8, S, D, D, g, st, true), "out");
+        DIT_LAUNCH(c, launch_gemm(c->o, wa.w, wa.scale, wa.w8, S, D, D, g, st, true), "out");
     }
+    DIT_TRY(weight_arg(c, b, 3, D, F, 0, &wa));
     {
         Stage t(c, DIT_ST_DOWN);
-        DIT_LAUNCH(c, launch_gemm(c->a, b->w[3], bscale(b, 3), w8, S, D, F, g, st, true), "down");
+        DIT_LAUNCH(c, launch_gemm(c->a, wa.w, wa.scale, wa.w8, S, D, F, g, st, true), "down");
     }
     return DIT_OK;
 }
@@ -348,22 +439,30 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
     // take the ping-pong kernel with the same weight type; streams with
     // different weight types: two launches
     const bool mixed = bt->wtype != bi->wtype;
-    const bool w8 = bi->wtype == DIT_W_INT8_B32;
+    // weights of both streams for product w: image stream in scratch slot 0,
+    // text stream in slot 1 (int8 block-32 weights dequantised by a pass)
+    WeightArg wgt[2]{};
+    auto weights = [&](int w, int n, int k) -> dit_status {
+        for (int i = 1; i >= 0; --i)
+            if (sts[i].rows) DIT_TRY(weight_arg(c, sts[i].b, w, n, k, 1 - i, &wgt[i]));
+        return DIT_OK;
+    };
     auto two = [&](int kind, const uint16_t *a_base, int64_t a_ld, const GemmEpi (&ep)[2], int w, int n, int k) {
         const Stream &ti = sts[1], &tt = sts[0];
-        if (mixed) {
+        (void)w;
+        if (mixed || wgt[0].w8 != wgt[1].w8) {
             hipError_t e = hipSuccess;
             for (int i = 1; i >= 0 && e == hipSuccess; --i) {
                 const Stream &t = sts[i];
                 if (t.rows)
-                    e = launch_gemm(a_base + int64_t(t.r0) * a_ld, t.b->w[w], bscale(t.b, w), t.b->wtype == DIT_W_INT8_B32,
-                                    t.rows, n, k, ep[i], st, true);
+                    e = launch_gemm(a_base + int64_t(t.r0) * a_ld, wgt[i].w, wgt[i].scale, wgt[i].w8, t.rows, n, k, ep[i],
+                                    st, true);
             }
             return e;
         }
         (void)kind;
-        return launch_gemm2(a_base + int64_t(ti.r0) * a_ld, ti.b->w[w], bscale(ti.b, w), ti.rows, ep[1],
-                            a_base + int64_t(tt.r0) * a_ld, tt.b->w[w], bscale(tt.b, w), tt.rows, ep[0], w8, n, k, st);
+        return launch_gemm2(a_base + int64_t(ti.r0) * a_ld, wgt[1].w, wgt[1].scale, ti.rows, ep[1],
+                            a_base + int64_t(tt.r0) * a_ld, wgt[0].w, wgt[0].scale, tt.rows, ep[0], wgt[1].w8, n, k, st);
     };
     {
         GemmEpi e[2]{};
@@ -383,6 +482,7 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
             e[i].row_base = t.r0;
             e[i].rows_total = S;
         }
+        DIT_TRY(weights(0, 3 * D, D));
         Stage tm(c, DIT_ST_QKV);
         DIT_LAUNCH(c, two(EPI_QKV, c->h, D, e, 0, 3 * D, D), "qkv");
     }
@@ -398,6 +498,7 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
             g[i].ldo = D;
             g[i].gate = sts[i].mod + 2 * D;
         }
+        DIT_TRY(weights(1, D, D));
         Stage tm(c, DIT_ST_OUT);
         DIT_LAUNCH(c, two(EPI_GATE_RES, c->o, D, g, 1, D, D), "out");
     }
@@ -414,6 +515,7 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
             u[i].kind = EPI_SWIGLU;
             u[i].act = c->a + int64_t(sts[i].r0) * F;
         }
+        DIT_TRY(weights(2, 2 * F, D));
         Stage tm(c, DIT_ST_UP);
         DIT_LAUNCH(c, two(EPI_SWIGLU, c->h2, D, u, 2, 2 * F, D), "up");
     }
@@ -425,6 +527,7 @@ dit_status double_block_forward(dit_ctx *c, const dit_block *bt, const dit_block
             g[i].ldo = D;
             g[i].gate = sts[i].mod + 5 * D;
         }
+        DIT_TRY(weights(3, D, F));
         Stage tm(c, DIT_ST_DOWN);
         DIT_LAUNCH(c, two(EPI_GATE_RES, c->a, F, g, 3, D, F), "down");
     }
@@ -469,7 +572,6 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
     const int D = A.hidden, F = A.ffn, H = A.heads;
     if (Sk < S) Sk = S;
     const int Sp = round_up(Sk, 64);
-    const bool w8 = b->wtype == DIT_W_INT8_B32;
     const bool rms = A.norm == DIT_NORM_RMS;
     hipStream_t st = c->stream;
     float *mod = c->mod;
@@ -501,12 +603,49 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
         return DIT_OK;
     };
     // the product of weight w over rows [r0, r0 + M) of A (bf16 a with row
-    // stride K, or the INT8 rows in aq / as)
+    // stride K, or the INT8 rows in aq / as); wa: the weight operand of
+    // bf16 and int8 block-32 blocks (weight_arg)
+    WeightArg wa{};
     auto product = [&](const uint16_t *a, int r0, int M, int w, int N, int K, const GemmEpi &ep) -> hipError_t {
         if (q8)
             return launch_gemm_w8a8(c->aq + int64_t(r0) * K, c->as + r0, static_cast<const int8_t *>(b->w[w]),
                                     static_cast<const float *>(b->scale[w]), M, N, K, ep, st);
-        return launch_gemm(a + int64_t(r0) * K, b->w[w], bscale(b, w), w8, M, N, K, ep, st, true);
+        return launch_gemm(a + int64_t(r0) * K, wa.w, wa.scale, wa.w8, M, N, K, ep, st, true);
+    };
+    // int8 block-32 weights dequantised by the pass: OUT, UP and DOWN on
+    // the side stream, started with the block, where they can take compute
+    // units the QKV product and the attention leave idle (their last rounds
+    // of tiles); each of those products waits for its own weight
+    bool async_dq = b->wtype == DIT_W_INT8_B32 && !c->int8_in_product;
+    for (int i = 0; i < 4; ++i) async_dq = async_dq && codes_aligned(b->w[i]);
+    auto fork_dequant = [&]() -> dit_status {
+        if (!async_dq) return DIT_OK;
+        DIT_TRY(ensure_wdq(c));
+        DIT_TRY(ensure_side(c));
+        if (hipEventRecord(c->ev_fork, st) != hipSuccess || hipStreamWaitEvent(c->side, c->ev_fork, 0) != hipSuccess)
+            return fail(c, DIT_EDEVICE, "ordering the dequantisation stream failed");
+        const int nk[4][2] = {{3 * D, D}, {D, D}, {2 * F, D}, {D, F}};
+        for (int w = 1; w < 4; ++w) {
+            {
+                Stage t(c, DIT_ST_DEQUANT, c->side);
+                DIT_LAUNCH(c, launch_dequant_bf16(static_cast<const int8_t *>(b->w[w]), bscale(b, w), nk[w][0], nk[w][1],
+                                                  wdq_slot(c, 0, w), c->side),
+                           "int8 dequantisation");
+            }
+            if (hipEventRecord(c->ev_ready[w], c->side) != hipSuccess)
+                return fail(c, DIT_EDEVICE, "recording a dequantised weight failed");
+        }
+        return DIT_OK;
+    };
+    auto prep = [&](int w, int N, int K) -> dit_status {
+        if (q8) return DIT_OK;
+        if (async_dq && w > 0) {
+            if (hipStreamWaitEvent(st, c->ev_ready[w], 0) != hipSuccess)
+                return fail(c, DIT_EDEVICE, "waiting for a dequantised weight failed");
+            wa = WeightArg{wdq_slot(c, 0, w), nullptr, false};
+            return DIT_OK;
+        }
+        return weight_arg(c, b, w, N, K, 0, &wa);
     };
     // OUT / DOWN: x[run] += gate(run) * (a_base[run] W^T), two runs per
     // launch; a sandwich block's product writes its rows in fp32 and the
@@ -517,6 +656,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
             Stage t(c, DIT_ST_QUANT);
             DIT_LAUNCH(c, launch_quant_rows(a_base, S, K, c->aq, c->as, st, rot), "quantize rows");
         }
+        DIT_TRY(prep(w, D, K));
         if (post) {
             GemmEpi f{};
             f.kind = EPI_F32;
@@ -561,8 +701,8 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
                 g[j].gate = mod + int64_t(runs[3 * (i + j) + 2]) * 6 * D + gate_at;
             }
             Stage t(c, stage);
-            DIT_LAUNCH(c, launch_gemm2(a_base + int64_t(f[0]) * lda, b->w[w], bscale(b, w), rows[0], g[0],
-                                       a_base + int64_t(f[1]) * lda, b->w[w], bscale(b, w), rows[1], g[1], w8, D, K, st),
+            DIT_LAUNCH(c, launch_gemm2(a_base + int64_t(f[0]) * lda, wa.w, wa.scale, rows[0], g[0],
+                                       a_base + int64_t(f[1]) * lda, wa.w, wa.scale, rows[1], g[1], wa.w8, D, K, st),
                        "gated product");
         }
         return DIT_OK;
@@ -581,6 +721,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
     e.sin = sn;
     e.qk_eps = A.qk_eps;
     e.rows_total = Sk;
+    DIT_TRY(prep(0, 3 * D, D));
     if (c->qk_fused) {
         Stage t(c, DIT_ST_QKV);
         DIT_LAUNCH(c, product(c->h, 0, S, 0, 3 * D, D, e), "qkv");
@@ -600,6 +741,9 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
         DIT_LAUNCH(c, launch_qk_prep(c->oa, S, H, Sk, b->norm_w[2], b->norm_w[3], cs, sn, A.qk_eps, c->q, c->k, c->vt, Sp, st),
                    "qk prep");
     }
+    // the later weights' dequantisation starts once the QKV product is done:
+    // it then shares the compute units with the attention
+    DIT_TRY(fork_dequant());
     if (Sk > S) DIT_TRY(ref_copy(c, nullptr, slot, S, Sk, false));
     {
         Stage t(c, DIT_ST_ATTN);
@@ -610,6 +754,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
     GemmEpi u{};
     u.kind = EPI_SWIGLU;
     u.act = c->a;
+    DIT_TRY(prep(2, 2 * F, D));
     {
         Stage t(c, DIT_ST_UP);
         DIT_LAUNCH(c, product(c->h2, 0, S, 2, 2 * F, D, u), "up");
@@ -751,6 +896,11 @@ void dit_ctx_destroy(dit_ctx *ctx) {
         drop_records(ctx);
         for (hipEvent_t e : ctx->spare) hipEventDestroy(e);
         hipFree(ctx->pool);
+        if (ctx->wdq) hipFree(ctx->wdq);
+        if (ctx->ev_fork) hipEventDestroy(ctx->ev_fork);
+        for (hipEvent_t e : ctx->ev_ready)
+            if (e) hipEventDestroy(e);
+        if (ctx->side) hipStreamDestroy(ctx->side);
     }
     delete ctx;
 }
@@ -859,7 +1009,16 @@ dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint
     e.kind = EPI_F32;
     e.out = out;
     e.ldo = N;
-    DIT_LAUNCH(ctx, launch_gemm(a, w, scale, wtype == DIT_W_INT8_B32, M, N, K, e, ctx->stream, false), "linear");
+    WeightArg wa{};
+    const bool int8 = wtype == DIT_W_INT8_B32;
+    if (int8 && !ctx->int8_in_product) DIT_TRY(ensure_wdq(ctx));
+    // the largest slot of the first set
+    int big = 0;
+    for (int i = 1; i < 4; ++i)
+        if (wdq_elems(ctx, i) > wdq_elems(ctx, big)) big = i;
+    DIT_TRY(weight_arg_of(ctx, w, scale, int8, N, K, ctx->wdq ? wdq_slot(ctx, 0, big) : nullptr,
+                          ctx->wdq ? wdq_elems(ctx, big) : 0, ctx->stream, &wa));
+    DIT_LAUNCH(ctx, launch_gemm(a, wa.w, wa.scale, wa.w8, M, N, K, e, ctx->stream, false), "linear");
     return DIT_OK;
 }
 
@@ -887,6 +1046,13 @@ dit_status dit_set_qk_prep(dit_ctx *ctx, int fused) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (fused != 0 && fused != 1) return fail(ctx, DIT_EINVAL, "fused = %d is not 0 or 1", fused);
     ctx->qk_fused = fused != 0;
+    return DIT_OK;
+}
+
+dit_status dit_set_int8_products(dit_ctx *ctx, int in_product) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (in_product != 0 && in_product != 1) return fail(ctx, DIT_EINVAL, "in_product = %d is not 0 or 1", in_product);
+    ctx->int8_in_product = in_product != 0;
     return DIT_OK;
 }
 

@@ -120,6 +120,43 @@ hipError_t launch_dequant(const int8_t *q, const uint16_t *s, int out, int in, f
     return hipGetLastError();
 }
 
+// bf16 weights from int8 block-32 codes for the bf16 products: w[o][k] =
+// bf16(q[o][k] * s[o][k/32]), the exact product rounded to nearest even.
+// Thread i converts codes 8i .. 8i+7 of the flat array (one 8-byte load;
+// with in % 32 == 0 the 8 share one block), so a wave's load reads 512
+// contiguous bytes and its store writes 1 KB.  The product is exact in
+// fp32: with the code's sign bit flipped, u = q + 128 in 0..255 converts
+// exactly and u * s - 128 * s is q * s (at most 16 significant bits).
+__global__ void __launch_bounds__(256) k_dequant_bf16(const u32x2 *__restrict__ q, const uint16_t *__restrict__ s,
+                                                      int64_t n8, u32x4 *__restrict__ w) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const u32x2 c = __builtin_nontemporal_load(q + i);
+        const float sc = bf16_to_f32(s[i >> 2]), msc = -128.0f * sc;
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t u = c[j] ^ 0x80808080u;
+            auto dq = [&](int b) { return __builtin_fmaf(static_cast<float>((u >> (8 * b)) & 0xffu), sc, msc); };
+            o[2 * j] = pack_bf16x2(dq(0), dq(1));
+            o[2 * j + 1] = pack_bf16x2(dq(2), dq(3));
+        }
+        w[i] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+}
+
+hipError_t launch_dequant_bf16(const int8_t *q, const uint16_t *s, int out, int in, uint16_t *w, hipStream_t st) {
+    const int64_t n = static_cast<int64_t>(out) * in;
+    if (n == 0) return hipSuccess;
+    if (in % 32 || (reinterpret_cast<uintptr_t>(q) & 7) || (reinterpret_cast<uintptr_t>(w) & 15))
+        return hipErrorInvalidValue;
+    const int64_t n8 = n / 8;
+    const int64_t want = (n8 + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(want < 8192 ? want : 8192);
+    k_dequant_bf16<<<grid, 256, 0, st>>>(reinterpret_cast<const u32x2 *>(q), s, n8, reinterpret_cast<u32x4 *>(w));
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- to bf16
 __global__ void k_to_bf16(const float *x, int64_t n, uint16_t *y) {
     int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;

@@ -14,6 +14,9 @@ hipError_t launch_rope_tables(const int32_t *pos, int S, int a0, int a1, int a2,
                               float *cos, float *sin, hipStream_t st);
 hipError_t launch_time_embedding(float t, int dim, float *temb, hipStream_t st);
 hipError_t launch_euler(float *x, const float *v, int64_t n, float dt, hipStream_t st);
+// w bf16 [out, in] = bf16(q * s) of int8 block-32 weights (in % 32 == 0,
+// q 8-byte and w 16-byte aligned).
+hipError_t launch_dequant_bf16(const int8_t *q, const uint16_t *s, int out, int in, uint16_t *w, hipStream_t st);
 hipError_t launch_dequant(const int8_t *q, const uint16_t *s, int out, int in, float *w,
                           hipStream_t st);
 hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *y, hipStream_t st);

@@ -28,7 +28,7 @@ _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, ERANGE, ENOMEM, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 STAGES = ("mod", "norm1", "qkv", "attn", "out", "norm2", "up", "down", "time", "img_in", "final",
-          "euler", "txt_in", "par_in", "par_out", "post", "quant", "qk_prep")
+          "euler", "txt_in", "par_in", "par_out", "post", "quant", "qk_prep", "dequant")
 W_BF16, W_INT8_B32, W_INT8_ROW, W_INT8_ROT = 0, 1, 2, 3
 NORM_LAYER, NORM_RMS = 0, 1
 _NAMES = {0: "DIT_OK", -1: "DIT_EINVAL", -2: "DIT_ERANGE", -3: "DIT_ENOMEM", -4: "DIT_EDEVICE",
@@ -82,6 +82,7 @@ _SIGS = {
     "dit_attention": (C.c_int, [_P, _P, _P, _P, C.c_int, C.c_int, _P]),
     "dit_qk_prep": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, _P, _P, _P, _P]),
     "dit_set_qk_prep": (C.c_int, [_P, C.c_int]),
+    "dit_set_int8_products": (C.c_int, [_P, C.c_int]),
     "dit_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_parallel_block_forward": (C.c_int, [_P, C.POINTER(Block), _P, _P, _P, _P, C.c_int, C.c_int]),
     "dit_double_block_forward": (C.c_int, [_P, C.POINTER(Block), C.POINTER(Block), _P, _P, _P, _P, C.c_int,
@@ -267,6 +268,11 @@ class Context:
 
     def set_qk_prep(self, fused: bool):
         self._call("dit_set_qk_prep", 1 if fused else 0)
+
+    def set_int8_products(self, in_product: bool):
+        """int8 block-32 weights: converted inside the product (True) or by
+        a dequantisation pass into scratch first (False, the default)."""
+        self._call("dit_set_int8_products", 1 if in_product else 0)
 
     def attention(self, q, k, vt, heads, S, o):
         self._call("dit_attention", _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"),

@@ -87,7 +87,10 @@ typedef struct {
  *   w[3] DOWN [D, F]
  * wtype DIT_W_BF16: w[i] are bf16; scale[i] must be NULL.
  * wtype DIT_W_INT8_B32: w[i] are int8 [out, in]; scale[i] are bf16
- *   [out, in/32]; weight = code * scale[o][k/32].
+ *   [out, in/32]; weight = code * scale[o][k/32], which the products take
+ *   rounded to bf16 (nearest even): by default dequantised by a pass of
+ *   its own into a context scratch buffer just before each product (see
+ *   dit_set_int8_products).
  * wtype DIT_W_INT8_ROW (W8A8 with per-token activations and per-output
  *   weights, [K4] Appendix B D4): w[i] are int8 [out, in], scale[i] fp32
  *   [out]; weight = code * scale[o].  Each product's input rows are taken
@@ -277,6 +280,18 @@ dit_status dit_qk_prep(dit_ctx *ctx, const uint16_t *qkv, int S, const float *q_
  * parallel and double-stream blocks always run the fused epilogue. */
 dit_status dit_set_qk_prep(dit_ctx *ctx, int fused);
 
+/* Where int8 block-32 products (DIT_W_INT8_B32, in every block form and
+ * dit_linear) turn codes into bf16 weights ([HC] s.1: dequantised inside
+ * the graph, products in bf16): in_product = 0 (the default) runs a
+ * dequantisation pass per weight into a scratch buffer the context
+ * allocates on first use (2 * max(3*hidden, 2*ffn) * hidden bf16 values,
+ * kept until dit_ctx_destroy; DIT_ENOMEM if that fails), then the bf16
+ * product; in_product = 1 converts each k-tile's codes inside the product
+ * (no scratch; the conversion's vector instructions then share the SIMDs
+ * with the matrix instructions).  Both give the same bf16 weights, bit for
+ * bit.  DIT_EINVAL for other values. */
+dit_status dit_set_int8_products(dit_ctx *ctx, int in_product);
+
 /* Joint attention ([K4] s.4.3): for each head h, o[:, h*128:(h+1)*128] =
  * bf16(softmax(q_h k_h^T / sqrt(128)) v_h), no mask.  q, k bf16
  * [heads, S, 128]; vt bf16 [heads, 128, Sp] with Sp = S rounded up to a
@@ -409,7 +424,8 @@ typedef enum {
     DIT_ST_POST = 15,   /* sandwich block: norm of a product's output, gate, residual */
     DIT_ST_QUANT = 16,  /* W8A8 block: attention / SwiGLU rows to INT8 */
     DIT_ST_QK_PREP = 17,/* unfused arm: q/k head norm + rotary, v transposed */
-    DIT_NSTAGES = 18
+    DIT_ST_DEQUANT = 18,/* int8 block-32 weights to bf16 before a product */
+    DIT_NSTAGES = 19
 } dit_stage;
 
 /* Per-stage timing, a measurement aid ([K4] s.3: every op of the busy time

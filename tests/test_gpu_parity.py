@@ -8,6 +8,8 @@ does exact-input fp32 arithmetic only).  Shapes cover several tiles on every
 grid axis, ragged tails and the full 1024-px block.
 """
 
+import contextlib
+
 import numpy as np
 import pytest
 
@@ -33,6 +35,21 @@ def ctx_big():
     c = L.Context(la, max_rows=4608)
     yield c
     c.close()
+
+
+@contextlib.contextmanager
+def int8_products(ctx, in_product):
+    """int8 block-32 weights converted inside the products (True) or by the
+    dequantisation pass (False, the default) for the body of the block."""
+    ctx.set_int8_products(bool(in_product))
+    try:
+        yield
+    finally:
+        ctx.set_int8_products(False)
+
+
+# the int8 block-32 workload in both conversion placements
+BLOCK_FORMS = [("s4608", False), ("s4608_int8", False), ("s4608_int8", True)]
 
 
 # --------------------------------------------------------------- positions, rope
@@ -104,9 +121,9 @@ def test_modulated_norm(norm, rows, D):
 @pytest.mark.parametrize("M,N,K", [(72, 256, 256), (1088, 3072, 3072), (4608, 64, 3072), (4096, 3072, 64),
                                    (333, 768, 1024), (1, 128, 128), (4608, 9216, 3072), (4608, 2048, 128),
                                    (4608, 3072, 12288)])
-@pytest.mark.parametrize("w8", [False, True])
+@pytest.mark.parametrize("w8", [False, "pass", "in_product"])
 def test_linear(ctx_big, M, N, K, w8):
-    say("linear", M, N, K, "int8" if w8 else "bf16")
+    say("linear", M, N, K, f"int8 ({w8})" if w8 else "bf16")
     rng = np.random.default_rng(M * 7 + N + K)
     a = synth.bf16_round(synth.normal((M, K), seed=M * 7 + N + K))
     if w8:
@@ -121,8 +138,9 @@ def test_linear(ctx_big, M, N, K, w8):
         wref = synth.bf16_round(synth.normal((N, K), seed=M + N * 3 + K, std=0.05))
         w_dev, s_dev = L.dev_bf16(wref), None
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    ctx_big.linear(L.dev_bf16(a), w_dev, s_dev, M, N, K, out)
-    torch.cuda.synchronize()
+    with int8_products(ctx_big, w8 == "in_product"):
+        ctx_big.linear(L.dev_bf16(a), w_dev, s_dev, M, N, K, out)
+        torch.cuda.synchronize()
     rows = np.arange(M) if M * N * K <= 2 ** 33 else synth.rows_sample(M, 300)
     ref = O.linear(a[rows], wref)
     got = np_of(out)[rows]
@@ -286,13 +304,49 @@ def test_block_full_parity(name, norm, norm_std):
     ctx.close()
 
 
-@pytest.mark.parametrize("name", ["s4608", "s4608_int8"])
-def test_block_full_size_sampled_rows(ctx_big, name):
+@pytest.mark.parametrize("name", ["tiny", "s1088"])
+@pytest.mark.parametrize("in_product", [False, True])
+def test_block_int8_full_parity(name, in_product):
+    """int8 block-32 weights in the sequential block, every row and
+    intermediate against the oracle.  A block with other int8 weights runs
+    first on the same context, not waited for: the dequantised copies of the
+    second block's weights (scratch shared by all calls, the later weights
+    converted on the context's second stream) must not mix with the
+    first's."""
+    case = synth.block_case(name)
+    sh = case["shape"]
+    case["block"] = synth.block_weights(np.random.default_rng(sh.seed + 50), sh, int8=True)
+    other = synth.block_weights(np.random.default_rng(sh.seed + 51), sh, int8=True)
+    la, oa = arch_pair(sh)
+    ctx = L.Context(la, max_rows=sh.S)
+    ctx.set_int8_products(in_product)
+    say("block int8", name, "in product" if in_product else "dequantisation pass", "S =", sh.S)
+    seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
+    bo, bw = L.BlockWeights.from_host(other), L.BlockWeights.from_host(case["block"])
+    x0, x = L.dev_f32(case["x"]), L.dev_f32(case["x"])
+    ctx.block_forward(bo, x0, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    torch.cuda.synchronize()
+    got = np_of(x)
+    inter = _intermediates(ctx, sh, sh.S)
+    cs, sn, vec = _oracle_inputs(case, oa)
+    y, ref = O.block_forward(case["x"], oracle_block(case["block"]), vec, cs, sn, oa, keep=True)
+    for k in ("h", "q", "k", "v", "o", "h2", "a"):
+        compare(f"{name}-int8/{k}", inter[k], ref[k], abs_=block_abs(ref[k]), bf16_stored=True)
+    compare(f"{name}-int8/y", got, y, abs_=block_abs(y))
+    d = y - case["x"]
+    compare(f"{name}-int8/delta", got - case["x"], d, abs_=block_abs(d))
+    ctx.close()
+
+
+@pytest.mark.parametrize("name,in_product", BLOCK_FORMS)
+def test_block_full_size_sampled_rows(ctx_big, name, in_product):
     case = synth.block_case(name)
     sh = case["shape"]
     _, oa = arch_pair(sh)
-    say("block", name, "S =", sh.S)
-    x, _, _ = _block_gpu(ctx_big, case)
+    say("block", name, "S =", sh.S, "int8 in product" if in_product else "")
+    with int8_products(ctx_big, in_product):
+        x, _, _ = _block_gpu(ctx_big, case)
     got = np_of(x)
     inter = _intermediates(ctx_big, sh, sh.S)
     cs, sn, vec = _oracle_inputs(case, oa)
@@ -510,17 +564,19 @@ def test_parallel_block_full_parity(name, norm, norm_std):
     ctx.close()
 
 
-@pytest.mark.parametrize("name", ["s4608", "s4608_int8"])
-def test_parallel_block_full_size_sampled_rows(ctx_big, name):
-    # s4608 with bf16 weights runs the two fused products ([QKV | UP] with
-    # both epilogues, [OUT | DOWN] over the concatenated rows); int8 the four
+@pytest.mark.parametrize("name,in_product", BLOCK_FORMS)
+def test_parallel_block_full_size_sampled_rows(ctx_big, name, in_product):
+    # s4608 runs the two fused products ([QKV | UP] with both epilogues,
+    # [OUT | DOWN] over the concatenated rows), with int8 weights on their
+    # dequantised copies; int8 weights converted inside the products: the four
     case = _parallel_case(name)
     sh = case["shape"]
     _, oa = arch_pair(sh)
     D, F = sh.hidden, sh.ffn
-    say("parallel block", name, "S =", sh.S)
-    got = np_of(_parallel_gpu(ctx_big, case))
-    if sh.int8:
+    say("parallel block", name, "S =", sh.S, "int8 in product" if in_product else "")
+    with int8_products(ctx_big, in_product):
+        got = np_of(_parallel_gpu(ctx_big, case))
+    if in_product:
         o_got = np_of(ctx_big.debug_copy(5, torch.bfloat16, (sh.S, D)))
         a_got = np_of(ctx_big.debug_copy(7, torch.bfloat16, (sh.S, F)))
     else:
@@ -568,14 +624,16 @@ def _double_gpu(ctx, case):
     return x
 
 
-@pytest.mark.parametrize("name", ["tiny", "s1088", "s4608"])
-def test_double_block_full_parity(ctx_big, name):
+@pytest.mark.parametrize("name,in_product", [("tiny", False), ("s1088", False), ("s4608", False),
+                                             ("s4608_int8", False), ("s4608_int8", True)])
+def test_double_block_full_parity(ctx_big, name, in_product):
     case = _double_case(name)
     sh = case["shape"]
     la, oa = arch_pair(sh)
-    ctx = ctx_big if name == "s4608" else L.Context(la, max_rows=sh.S)
-    say("double block", name, "L =", sh.L, "N =", sh.N)
-    got = np_of(_double_gpu(ctx, case))
+    ctx = ctx_big if name.startswith("s4608") else L.Context(la, max_rows=sh.S)
+    say("double block", name, "L =", sh.L, "N =", sh.N, "int8 in product" if in_product else "")
+    with int8_products(ctx, in_product):
+        got = np_of(_double_gpu(ctx, case))
     D, F, H = sh.hidden, sh.ffn, sh.heads
     S, Sp = sh.S, (sh.S + 63) // 64 * 64
     cs, sn, vec = _oracle_inputs(case, oa)
@@ -588,11 +646,14 @@ def test_double_block_full_parity(ctx_big, name):
     compare(f"{name}/q", np_of(ctx.debug_copy(2, torch.bfloat16, (H, S, 128))), ref["q"], bf16_stored=True)
     compare(f"{name}/k", np_of(ctx.debug_copy(3, torch.bfloat16, (H, S, 128))), ref["k"], bf16_stored=True)
     v = np_of(ctx.debug_copy(4, torch.bfloat16, (H, 128, Sp)))[:, :, :S].transpose(0, 2, 1)
-    compare(f"{name}/v", v, ref["v"], bf16_stored=True)
-    compare(f"{name}/o", np_of(ctx.debug_copy(5, torch.bfloat16, (S, D))), ref["o"], bf16_stored=True)
-    compare(f"{name}/a", np_of(ctx.debug_copy(7, torch.bfloat16, (S, F))), ref["a"], bf16_stored=True)
-    compare(f"{name}/y", got, y)
-    compare(f"{name}/delta", got - case["x"], y - case["x"])
+    # int8 weights: tolerance relative to the reference's largest magnitude
+    sc = (lambda r: block_abs(r)) if sh.int8 else (lambda r: ABS)
+    compare(f"{name}/v", v, ref["v"], abs_=sc(ref["v"]), bf16_stored=True)
+    compare(f"{name}/o", np_of(ctx.debug_copy(5, torch.bfloat16, (S, D))), ref["o"], abs_=sc(ref["o"]), bf16_stored=True)
+    compare(f"{name}/a", np_of(ctx.debug_copy(7, torch.bfloat16, (S, F))), ref["a"], abs_=sc(ref["a"]), bf16_stored=True)
+    compare(f"{name}/y", got, y, abs_=sc(y))
+    d = y - case["x"]
+    compare(f"{name}/delta", got - case["x"], d, abs_=sc(d))
     if ctx is not ctx_big:
         ctx.close()
 
@@ -739,13 +800,14 @@ def test_sandwich_block_full_parity(name, norm, norm_std):
     ctx.close()
 
 
-@pytest.mark.parametrize("name", ["s4608", "s4608_int8"])
-def test_sandwich_block_full_size_sampled_rows(ctx_big, name):
+@pytest.mark.parametrize("name,in_product", BLOCK_FORMS)
+def test_sandwich_block_full_size_sampled_rows(ctx_big, name, in_product):
     case = synth.block_case(name, sandwich=True)
     sh = case["shape"]
     _, oa = arch_pair(sh)
-    say("sandwich block", name, "S =", sh.S)
-    x, _, _ = _block_gpu(ctx_big, case)
+    say("sandwich block", name, "S =", sh.S, "int8 in product" if in_product else "")
+    with int8_products(ctx_big, in_product):
+        x, _, _ = _block_gpu(ctx_big, case)
     got = np_of(x)
     inter = _intermediates(ctx_big, sh, sh.S)
     cs, sn, vec = _oracle_inputs(case, oa)
