@@ -649,13 +649,15 @@ def main():
             f"1 GiB copy {calib['copy_gbs']} GB/s")
 
     # ---------------------------------------------------------------- whole image
-    img = img8 = None
+    img = img8 = imgi8 = None
     if not args.no_denoise:
         img = bench_images(torch, L, synth, args.images)
         if img.get("euler_ms"):   # x read and written, v read: fp32 [N, 64]
             hbm.update(hbm_rows({"euler": img["euler_ms"]}, {"euler": 3 * 4 * sh.N * 64}))
         if not args.no_w8a8:
             img8 = bench_images(torch, L, synth, args.images, w8a8=True)
+        if not args.no_int8:
+            imgi8 = bench_images(torch, L, synth, args.images, int8=True)
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None if args.no_cpu else cpu_baseline()
@@ -708,18 +710,22 @@ def main():
         out.update(img)
     if img8:
         out["w8a8_image"] = {k: img8[k] for k in ("images_per_s", "ms_per_image", "image_finite", "image_workload")}
+    if imgi8:
+        out["int8_image"] = {k: imgi8[k] for k in ("images_per_s", "ms_per_image", "image_finite", "image_workload")}
     out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
-def bench_images(torch, L, synth, images, w8a8=False):
+def bench_images(torch, L, synth, images, w8a8=False, int8=False):
     """Whole path per image at the 1024-px DiT: 32 blocks, 4 Euler steps;
-    with w8a8, blocks of INT8 weight rows (W8A8 products)."""
+    with w8a8, blocks of INT8 weight rows (W8A8 products); with int8, int8
+    block-32 weights (dequantised before the bf16 products)."""
     sh = synth.SHAPES["dit32"]
     S, D, H, F, lat = sh.S, sh.hidden, sh.heads, sh.ffn, sh.latent
     arch = L.make_arch(hidden=D, heads=H, ffn=F, latent=lat, text_dim=sh.text_dim)
     ctx = L.Context(arch, max_rows=S)
-    log(f"generating 32 blocks of random {'W8A8' if w8a8 else 'bf16'} weights on the GPU")
+    kind = "W8A8" if w8a8 else "int8 block-32" if int8 else "bf16"
+    log(f"generating 32 blocks of random {kind} weights on the GPU")
     g = torch.Generator(device="cuda")
     g.manual_seed(sh.seed)
 
@@ -733,6 +739,9 @@ def bench_images(torch, L, synth, images, w8a8=False):
     def s8(o):
         return torch.full((o,), 0.02 * 3 ** 0.5 / 127, device="cuda", dtype=torch.float32)
 
+    def sb(o, i):   # block-32 scales |N(0,1)| * 0.01 in bf16
+        return torch.randn((o, i // 32), generator=g, device="cuda").abs_().mul_(0.01).to(torch.bfloat16)
+
     blocks = []
     dims = {"w_qkv": (3 * D, D), "w_out": (D, D), "w_up": (2 * F, D), "w_down": (D, F)}
     for _ in range(sh.blocks):
@@ -740,11 +749,15 @@ def bench_images(torch, L, synth, images, w8a8=False):
             t = {}
             for n, (o, i) in dims.items():
                 t["q8_" + n], t["s8_" + n] = q8(o, i), s8(o)
+        elif int8:
+            t = {}
+            for n, (o, i) in dims.items():
+                t["q_" + n], t["s_" + n] = q8(o, i), sb(o, i)
         else:
             t = {n: w(o, i) for n, (o, i) in dims.items()}
         t.update({"w_mod": w(6 * D, D), "q_norm": torch.ones(128, device="cuda"),
                   "k_norm": torch.ones(128, device="cuda")})
-        blocks.append(L.BlockWeights(t))
+        blocks.append(L.BlockWeights(t, int8=int8))
     top = {"w_t1": w(D, sh.time_dim), "w_t2": w(D, D), "w_in": w(D, lat), "w_txt": w(D, sh.text_dim),
            "w_fmod": w(2 * D, D), "w_final": w(lat, D)}
     model = L.ModelWeights(top, blocks)
@@ -793,7 +806,7 @@ def bench_images(torch, L, synth, images, w8a8=False):
     blk = sum(stage_flops(S, D, H, F).values())
     img_flops = 4 * (sh.blocks * blk + 2 * sh.N * lat * D + 2 * sh.N * D * lat + 2 * D * 256
                      + 2 * D * D + 2 * 2 * D * D) + 2 * sh.L * sh.text_dim * D
-    log(f"image{' (W8A8)' if w8a8 else ''}: {ms:.1f} ms  {1000 / ms:.3f} img/s  {img_flops / ms / 1e9:.1f} TFLOP/s  "
+    log(f"image{'' if kind == 'bf16' else ' (' + kind + ')'}: {ms:.1f} ms  {1000 / ms:.3f} img/s  {img_flops / ms / 1e9:.1f} TFLOP/s  "
         f"finite={finite}")
     ctx.close()
     del model, blocks, top
@@ -802,7 +815,7 @@ def bench_images(torch, L, synth, images, w8a8=False):
             "prologue_ms": pro, "steps_ms": round(ms - pro["p50"], 2), "euler_ms": euler_ms,
             "image_tflops": round(img_flops / ms / 1e9, 2), "image_flops": img_flops,
             "image_workload": "32-block DiT, 4 Euler steps (sigmas 1, .75, .5, .25, 0), L=512 + N=4096, "
-                              f"latent 64, text features 4096-d, batch 1, random-init {'W8A8' if w8a8 else 'bf16'} "
+                              f"latent 64, text features 4096-d, batch 1, random-init {kind} "
                               "block weights",
             "image_finite": finite}
 
