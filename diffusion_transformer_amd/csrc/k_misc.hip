@@ -5,6 +5,8 @@
 // Sources: "Host contract -- RGBA-Image-2.1-Turbo" s.4 (positions, rotary
 // tables), s.6 (Euler update, fp32); "gizai:dit" reference: sinusoids,
 // Modulation, normedInto; s.1 of the host contract for the int8 format.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -467,6 +469,45 @@ __device__ __forceinline__ float block_max(float v, float *red) {
     return t;
 }
 
+// The value lane ^ m holds (m = 1 .. 32), without the LDS: DPP row
+// permutations for m < 16 (quad_perm for 1, 2 and 3, half-row mirror = 7,
+// row mirror = 15; 4 = 7 then 3, 8 = 15 then 7), the gfx950 row swaps for
+// 16 and 32 (swapping a value with itself leaves each lane its own value in
+// one result and its partner's in the other).
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+    const int u = __float_as_int(v);
+    auto dpp = [](int x, auto ctrl) { return __builtin_amdgcn_mov_dpp(x, decltype(ctrl)::value, 0xf, 0xf, false); };
+    using Q1 = std::integral_constant<int, 0xb1>;    // quad_perm(1, 0, 3, 2)
+    using Q2 = std::integral_constant<int, 0x4e>;    // quad_perm(2, 3, 0, 1)
+    using Q3 = std::integral_constant<int, 0x1b>;    // quad_perm(3, 2, 1, 0)
+    using HM = std::integral_constant<int, 0x141>;   // row_half_mirror: lane ^ 7 within 8
+    using RM = std::integral_constant<int, 0x140>;   // row_mirror: lane ^ 15 within 16
+    if constexpr (M == 1) return __int_as_float(dpp(u, Q1{}));
+    if constexpr (M == 2) return __int_as_float(dpp(u, Q2{}));
+    if constexpr (M == 4) return __int_as_float(dpp(dpp(u, HM{}), Q3{}));
+    if constexpr (M == 8) return __int_as_float(dpp(dpp(u, RM{}), HM{}));
+    const int lane = threadIdx.x & 63;
+    if constexpr (M == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(u), static_cast<unsigned>(u), false, false);
+        return __uint_as_float((lane & 16) ? p[0] : p[1]);
+    }
+    if constexpr (M == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(u), static_cast<unsigned>(u), false, false);
+        return __uint_as_float((lane & 32) ? p[0] : p[1]);
+    }
+    return v;
+}
+
+// One cross-lane butterfly stage: lanes with bit m clear keep a + b, the
+// others b - a (a their own value, b their partner's).
+template <int M, int NPL>
+__device__ __forceinline__ void butterfly_lanes(float (&v)[NPL]) {
+    const float sgn = (threadIdx.x & M) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) v[k] = __builtin_fmaf(sgn, v[k], xor_lane<M>(v[k]));
+}
+
 // ConvRot's rotation ("gizai:dit" reference: linearInto and
 // Block.dequantized: each 256 inputs x go to y = R x, R the regular
 // Hadamard of 256): the fast transform over the 8 index bits, butterflies
@@ -485,14 +526,12 @@ __device__ __forceinline__ void convrot256(float (&v)[NPL]) {
                 v[k] = a + b;
                 v[k + h] = a - b;
             }
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int m = 1; m < 256 / NPL; m <<= 1)
-#pragma unroll
-        for (int k = 0; k < NPL; ++k) {
-            const float p = __shfl_xor(v[k], m, kWave);
-            v[k] = (lane & m) ? p - v[k] : v[k] + p;
-        }
+    butterfly_lanes<1>(v);
+    butterfly_lanes<2>(v);
+    butterfly_lanes<4>(v);
+    butterfly_lanes<8>(v);
+    butterfly_lanes<16>(v);
+    if constexpr (256 / NPL > 32) butterfly_lanes<32>(v);
 #pragma unroll
     for (int k = 0; k < NPL; ++k) v[k] *= 0.0625f;
 }
