@@ -284,9 +284,13 @@ dit_status dit_set_qk_prep(dit_ctx *ctx, int fused);
  * dit_linear) turn codes into bf16 weights ([HC] s.1: dequantised inside
  * the graph, products in bf16): in_product = 0 (the default) runs a
  * dequantisation pass per weight into a scratch buffer the context
- * allocates on first use (2 * max(3*hidden, 2*ffn) * hidden bf16 values,
- * kept until dit_ctx_destroy; DIT_ENOMEM if that fails), then the bf16
- * product; in_product = 1 converts each k-tile's codes inside the product
+ * allocates on first use (two sets of one slot per block weight,
+ * 2 * (4*hidden + 3*ffn) * hidden bf16 values, kept until dit_ctx_destroy;
+ * DIT_ENOMEM if that fails), then the bf16 product (the sequential forms
+ * convert their OUT, UP and DOWN weights on a second stream of the context,
+ * ordered by events against the context's stream; dit_linear weights that
+ * fit no slot, and codes not 16-byte aligned, are converted inside the
+ * product); in_product = 1 converts each k-tile's codes inside the product
  * (no scratch; the conversion's vector instructions then share the SIMDs
  * with the matrix instructions).  Both give the same bf16 weights, bit for
  * bit.  DIT_EINVAL for other values. */
