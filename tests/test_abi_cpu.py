@@ -40,6 +40,8 @@ def test_version_and_null_context():
     assert "NULL" in L.last_error(None)
     assert lib.dit_euler_step(None, None, None, 0, 1.0, 0.0) == L.EINVAL
     assert lib.dit_block_forward(None, None, None, None, None, None, 0, 1) == L.EINVAL
+    assert lib.dit_set_qk_prep(None, 1) == L.EINVAL
+    assert lib.dit_set_int8_products(None, 0) == L.EINVAL
     lib.dit_ctx_destroy(None)      # no-op
 
 

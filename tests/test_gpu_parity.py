@@ -304,6 +304,13 @@ def test_block_full_parity(name, norm, norm_std):
     ctx.close()
 
 
+def test_arm_switches_reject_other_values(ctx_tiny):
+    for fn in ("dit_set_qk_prep", "dit_set_int8_products"):
+        for v in (-1, 2):
+            assert getattr(L.raw(), fn)(ctx_tiny.handle, v) == L.EINVAL
+    assert L.raw().dit_set_int8_products(ctx_tiny.handle, 0) == L.OK
+
+
 @pytest.mark.parametrize("name", ["tiny", "s1088"])
 @pytest.mark.parametrize("in_product", [False, True])
 def test_block_int8_full_parity(name, in_product):
