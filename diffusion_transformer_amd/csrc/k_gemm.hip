@@ -23,12 +23,15 @@
 // (gate, up) pairs meet in one lane without shuffles.  Blocks are remapped
 // so that each XCD works on a compact group of tiles (its own L2), in groups
 // of 8 row-tiles.  Two kernels:
-//  - k_gemm_p3, bf16 weights, 256x256 tiles: a two-group ping-pong schedule
-//    with direct global -> LDS loads (below);
-//  - k_gemm, int8 weights and small or ragged shapes: 256x256 or 128x128
-//    tiles, LDS double buffer with register staging of the next k-tile;
-//    int8 weights are dequantised (code * scale, rounded to bf16) on the way
-//    into LDS, once per block.
+//  - k_gemm_p3, 256x256 tiles: a two-group ping-pong schedule with direct
+//    global -> LDS loads (below), for bf16 weights (int8 block-32 weights
+//    arrive here dequantised by a pass of their own by default), with forms
+//    for INT8 rows on the INT8 matrix cores and for int8 block-32 codes
+//    converted in LDS;
+//  - k_gemm, small or ragged shapes: 256x256 or 128x128 tiles, LDS double
+//    buffer with register staging of the next k-tile; int8 block-32 weights
+//    are dequantised (code * scale, rounded to bf16) on the way into LDS,
+//    once per block.
 #include "common.h"
 #include <type_traits>
 
@@ -637,7 +640,7 @@ __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 //   phase 2t+1 : group 0 converts half 1 of k-tile t+1 (read by group 1 in 2t+2)
 // so a single bf16 W buffer suffices (the half being written was last read
 // the phase before).  The product code * scale is exact: with the code's
-// sign bit flipped, u = code + 128 in 1..255 converts exactly, and
+// sign bit flipped, u = code + 128 in 0..255 converts exactly, and
 // u * s - 128 * s is (code) * s, at most 15 significant bits.  LDS: three A
 // buffers (96 KB), one W buffer (32 KB), codes (16 KB) and scales (2 KB).
 template <int EPI, bool KS, bool I8 = false, bool B32 = false>
