@@ -613,9 +613,9 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
         return launch_gemm(a + int64_t(r0) * K, wa.w, wa.scale, wa.w8, M, N, K, ep, st, true);
     };
     // int8 block-32 weights dequantised by the pass: OUT, UP and DOWN on
-    // the side stream, started with the block, where they can take compute
-    // units the QKV product and the attention leave idle (their last rounds
-    // of tiles); each of those products waits for its own weight
+    // the second stream, started once the QKV product is done, where they
+    // can take compute units the attention's second round of tiles leaves
+    // idle; each of those products waits for its own weight
     bool async_dq = b->wtype == DIT_W_INT8_B32 && !c->int8_in_product;
     for (int i = 0; i < 4; ++i) async_dq = async_dq && codes_aligned(b->w[i]);
     auto fork_dequant = [&]() -> dit_status {
