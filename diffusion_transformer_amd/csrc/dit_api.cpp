@@ -195,6 +195,7 @@ dit_status check_ctx(dit_ctx *c) {
 
 // `sequential`: whether the form is a sequential one, which alone takes a
 // sandwich block's post norms and W8A8 weights; the others reject them.
+bool aligned_to(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bool sequential = false) {
     if (!b) return fail(c, DIT_EINVAL, "block is NULL");
     if (b->wtype != DIT_W_BF16 && b->wtype != DIT_W_INT8_B32 && b->wtype != DIT_W_INT8_ROW &&
@@ -207,13 +208,21 @@ dit_status check_block(dit_ctx *c, const dit_block *b, bool parallel = false, bo
     // at most 16384 wide; refused here, before the attention half updates x
     if (w8a8 && c->arch.ffn > 16384)
         return fail(c, DIT_EUNSUPPORTED, "W8A8 blocks take ffn up to 16384 (arch ffn %d)", c->arch.ffn);
+    // the products and the GEMV read weights in 16-byte pieces, scales in
+    // 4-byte ones
     for (int i = 0; i < 4; ++i) {
         if (!b->w[i]) return fail(c, DIT_EINVAL, "block weight w[%d] is NULL", i);
         if (b->wtype != DIT_W_BF16 && !b->scale[i]) return fail(c, DIT_EINVAL, "int8 weight %d has no scales", i);
         if (b->wtype == DIT_W_BF16 && b->scale[i]) return fail(c, DIT_EINVAL, "bf16 weight %d given scales", i);
+        if (!aligned_to(b->w[i], 16) || !aligned_to(b->scale[i], 4))
+            return fail(c, DIT_EINVAL, "weight %d: w must be 16-byte and scale 4-byte aligned", i);
     }
     if (!b->w_mod) return fail(c, DIT_EINVAL, "block w_mod is NULL");
+    if (!aligned_to(b->w_mod, 16)) return fail(c, DIT_EINVAL, "block w_mod must be 16-byte aligned");
     if (!b->norm_w[2] || !b->norm_w[3]) return fail(c, DIT_EINVAL, "head-norm weights are NULL");
+    for (int i = 0; i < 4; ++i)
+        if (!aligned_to(b->norm_w[i], 16) || (i < 2 && !aligned_to(b->post_w[i], 16)))
+            return fail(c, DIT_EINVAL, "norm and post-norm weights must be 16-byte aligned");
     if (c->arch.norm == DIT_NORM_RMS && (!b->norm_w[0] || (!parallel && !b->norm_w[1])))
         return fail(c, DIT_EINVAL, parallel ? "RMSNorm needs norm weight NORM1" : "RMSNorm needs norm weights NORM1 and NORM2");
     if (!b->post_w[0] != !b->post_w[1])
@@ -252,7 +261,6 @@ dit_status ensure_wdq(dit_ctx *c) {
     c->wdq = static_cast<uint16_t *>(p);
     return DIT_OK;
 }
-bool codes_aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 dit_status ensure_side(dit_ctx *c) {
     if (c->side) return DIT_OK;
     hipStream_t s = nullptr;
@@ -263,14 +271,14 @@ dit_status ensure_side(dit_ctx *c) {
     c->side = s;
     return ok ? DIT_OK : fail(c, DIT_EDEVICE, "creating the dequantisation events failed");
 }
-// Dequantises int8 codes wp (N x K, block-32 scales) into dst of cap
-// values on stream hs when the context takes that path and it applies
-// (16-byte aligned codes that fit); otherwise the codes themselves.
+// Dequantises int8 codes wp (N x K, block-32 scales, 16-byte aligned) into
+// dst of cap values on stream hs when the context takes that path and they
+// fit; otherwise the codes themselves.
 dit_status weight_arg_of(dit_ctx *c, const void *wp, const uint16_t *scale, bool int8, int N, int K, uint16_t *dst,
                          size_t cap, hipStream_t hs, WeightArg *out) {
     *out = WeightArg{wp, nullptr, false};
     if (!int8) return DIT_OK;
-    if (c->int8_in_product || !codes_aligned(wp) || static_cast<size_t>(N) * K > cap) {
+    if (c->int8_in_product || static_cast<size_t>(N) * K > cap) {
         *out = WeightArg{wp, scale, true};
         return DIT_OK;
     }
@@ -347,9 +355,8 @@ dit_status parallel_block_forward(dit_ctx *c, const dit_block *b, float *x, cons
     gk.w2 = static_cast<const uint16_t *>(b->w[3]);
     gk.k_split = D;
     // the fused pair of products takes bf16 weights: bf16 blocks, and int8
-    // block-32 blocks dequantised by a pass first (16-byte aligned codes)
-    bool dq = !c->int8_in_product;
-    for (int i = 0; i < 4; ++i) dq = dq && (reinterpret_cast<uintptr_t>(b->w[i]) & 15) == 0;
+    // block-32 blocks dequantised by a pass first
+    const bool dq = !c->int8_in_product;
     const bool fused = (!w8 || dq) && gemm_pingpong_ok(S, 3 * D + 2 * F, D, false, fin, true) &&
                        gemm_pingpong_ok(S, D, D + F, false, gk, true);
     WeightArg wa{}, wb{};
@@ -616,8 +623,7 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
     // the second stream, started once the QKV product is done, where they
     // can take compute units the attention's second round of tiles leaves
     // idle; each of those products waits for its own weight
-    bool async_dq = b->wtype == DIT_W_INT8_B32 && !c->int8_in_product;
-    for (int i = 0; i < 4; ++i) async_dq = async_dq && codes_aligned(b->w[i]);
+    const bool async_dq = b->wtype == DIT_W_INT8_B32 && !c->int8_in_product;
     auto fork_dequant = [&]() -> dit_status {
         if (!async_dq) return DIT_OK;
         DIT_TRY(ensure_wdq(c));
@@ -1004,6 +1010,8 @@ dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint
     if (M < 1 || M > ctx->max_rows) return fail(ctx, DIT_ERANGE, "M %d outside 1..%d", M, ctx->max_rows);
     if (N < 64 || N % 64 || N > 65536) return fail(ctx, DIT_EINVAL, "N %d: must be a multiple of 64 in 64..65536", N);
     if (K < 64 || K % 64 || K > 65536) return fail(ctx, DIT_EINVAL, "K %d: must be a multiple of 64 in 64..65536", K);
+    if (!aligned_to(a, 16) || !aligned_to(w, 16) || !aligned_to(scale, 4) || !aligned_to(out, 16))
+        return fail(ctx, DIT_EINVAL, "a, w and out must be 16-byte and scale 4-byte aligned");
     DIT_TRY(check_ctx(ctx));
     GemmEpi e{};
     e.kind = EPI_F32;
@@ -1144,6 +1152,7 @@ dit_status dit_block_forward(dit_ctx *ctx, const dit_block *b, float *x, const f
                              const float *sin_t, int L, int N) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
+    if (!aligned_to(x, 16)) return fail(ctx, DIT_EINVAL, "x must be 16-byte aligned");
     DIT_TRY(check_block(ctx, b, false, true));
     DIT_TRY(check_rows(ctx, L, N));
     DIT_TRY(check_ctx(ctx));
@@ -1154,6 +1163,7 @@ dit_status dit_parallel_block_forward(dit_ctx *ctx, const dit_block *b, float *x
                                       const float *cos_t, const float *sin_t, int L, int N) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
+    if (!aligned_to(x, 16)) return fail(ctx, DIT_EINVAL, "x must be 16-byte aligned");
     DIT_TRY(check_block(ctx, b, true));
     DIT_TRY(check_rows(ctx, L, N));
     DIT_TRY(check_ctx(ctx));
@@ -1165,6 +1175,7 @@ dit_status dit_block_forward_runs(dit_ctx *ctx, const dit_block *b, float *x, co
                                   int N) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (!x || !vecs || !runs || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vecs, runs, cos or sin is NULL");
+    if (!aligned_to(x, 16)) return fail(ctx, DIT_EINVAL, "x must be 16-byte aligned");
     DIT_TRY(check_block(ctx, b, false, true));
     DIT_TRY(check_rows(ctx, L, N));
     if (R < 1 || R > kMaxModRows) return fail(ctx, DIT_ERANGE, "R = %d outside 1..%d", R, kMaxModRows);
@@ -1185,6 +1196,7 @@ dit_status dit_block_forward_cached(dit_ctx *ctx, const dit_block *b, float *x, 
                                    const float *sin_t, int L, int N, int first, uint16_t *slot, int record) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
+    if (!aligned_to(x, 16)) return fail(ctx, DIT_EINVAL, "x must be 16-byte aligned");
     DIT_TRY(check_block(ctx, b, false, true));
     DIT_TRY(check_rows(ctx, L, N));
     const int S = L + N;
@@ -1204,6 +1216,7 @@ dit_status dit_double_block_forward(dit_ctx *ctx, const dit_block *txt, const di
                                     const float *vec, const float *cos_t, const float *sin_t, int L, int N) {
     if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
     if (!x || !vec || !cos_t || !sin_t) return fail(ctx, DIT_EINVAL, "x, vec, cos or sin is NULL");
+    if (!aligned_to(x, 16)) return fail(ctx, DIT_EINVAL, "x must be 16-byte aligned");
     DIT_TRY(check_block(ctx, txt));
     DIT_TRY(check_block(ctx, img));
     DIT_TRY(check_rows(ctx, L, N));

@@ -97,7 +97,7 @@ typedef struct {
  *   to INT8 with one scale a row (s = max|row| / 127, codes rint(v * 127 /
  *   max|row|)), fused into the modulated norm for QKV and UP; the int32
  *   sums times both scales.  Only the sequential forms take it (ffn up to
- *   16384); x, cos and sin must then be 16-byte aligned (the INT8 products
+ *   16384); cos and sin must then be 16-byte aligned (the INT8 products
  *   have no unaligned fallback: DIT_EDEVICE).
  * wtype DIT_W_INT8_ROT ([GZ] linearInto, quantizedOf, Block.quantized:
  *   ConvRot): as DIT_W_INT8_ROW with the INT8 rows stored in the rotated
@@ -114,7 +114,11 @@ typedef struct {
  *   product output row is normed (the arch's norm kind and eps, times the
  *   weight) before its gate.  Both NULL: the gated outputs are added as
  *   they are.  Only the sequential forms (dit_block_forward,
- *   dit_block_forward_runs, the blocks of dit_denoise_step) take them. */
+ *   dit_block_forward_runs, the blocks of dit_denoise_step) take them.
+ * Alignment: w[i], w_mod, norm_w[i] and post_w[i] 16-byte aligned,
+ *   scale[i] 4-byte aligned, and the block forms' x 16-byte aligned
+ *   (DIT_EINVAL otherwise; the kernels read them in 16- and 4-byte
+ *   pieces). */
 typedef struct {
     int32_t wtype;
     const void *w[4];
@@ -216,7 +220,8 @@ dit_status dit_modulated_norm(dit_ctx *ctx, const float *x, int rows, const floa
 /* Plain product out = a * W^T ([GZ] linearInto): a bf16 [M, K]; W bf16
  * [N, K] (wtype DIT_W_BF16, scale NULL) or int8 [N, K] with bf16 scales
  * [N, K/32] (DIT_W_INT8_B32); out fp32 [M, N].  K a multiple of 64,
- * N a multiple of 64, 1 <= M <= max_rows. */
+ * N a multiple of 64, 1 <= M <= max_rows; a, W and out 16-byte aligned,
+ * the scales 4-byte aligned (DIT_EINVAL otherwise). */
 dit_status dit_linear(dit_ctx *ctx, const uint16_t *a, const void *w, const uint16_t *scale,
                       int wtype, int M, int N, int K, float *out);
 
@@ -289,8 +294,8 @@ dit_status dit_set_qk_prep(dit_ctx *ctx, int fused);
  * DIT_ENOMEM if that fails), then the bf16 product (the sequential forms
  * convert their OUT, UP and DOWN weights on a second stream of the context,
  * ordered by events against the context's stream; dit_linear weights that
- * fit no slot, and codes not 16-byte aligned, are converted inside the
- * product); in_product = 1 converts each k-tile's codes inside the product
+ * fit no slot are converted inside the product); in_product = 1 converts
+ * each k-tile's codes inside the product
  * (no scratch; the conversion's vector instructions then share the SIMDs
  * with the matrix instructions).  Both give the same bf16 weights, bit for
  * bit.  DIT_EINVAL for other values. */

@@ -440,6 +440,56 @@ def test_block_rejects_bad_rows(ctx_tiny):
         assert e.value.status == L.ERANGE
 
 
+def _shifted(t, elems):
+    """A contiguous view of t's storage starting `elems` elements later (so
+    misaligned by elems * itemsize bytes), same shape: the allocation gets
+    one extra row to hold it."""
+    flat = torch.empty(t.numel() + 64, dtype=t.dtype, device=t.device)
+    flat[elems:elems + t.numel()].copy_(t.reshape(-1))
+    return flat[elems:elems + t.numel()].view(t.shape)
+
+
+@pytest.mark.parametrize("what", ["w_qkv", "q_w_down", "s_w_up", "w_mod", "k_norm", "x"])
+def test_block_rejects_misaligned_pointers(ctx_tiny, what):
+    """Weights and x the kernels read in 16-byte pieces (block-32 scales in
+    4-byte ones) are refused with DIT_EINVAL before any launch."""
+    case = synth.block_case("tiny")
+    sh = case["shape"]
+    seq = GpuSeq(ctx_tiny, sh, case["t"], case["w_t1"], case["w_t2"])
+    blk = case["block"]
+    if what in ("q_w_down", "s_w_up"):
+        blk = synth.block_weights(np.random.default_rng(7), sh, int8=True)
+    bw = L.BlockWeights.from_host(blk)
+    x = L.dev_f32(case["x"])
+    if what == "x":
+        x = _shifted(x, 2)
+    else:
+        t = dict(bw.t)
+        t[what] = _shifted(t[what], 1)
+        bw = L.BlockWeights(t, int8=bw.int8)
+    x0 = x.clone()
+    with pytest.raises(L.DitError) as e:
+        ctx_tiny.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+    assert e.value.status == L.EINVAL
+    assert "aligned" in str(e.value)
+    torch.cuda.synchronize()
+    assert torch.equal(x, x0)
+
+
+def test_linear_rejects_misaligned_weights(ctx_tiny):
+    rng = np.random.default_rng(3)
+    a = L.dev_bf16(rng.standard_normal((64, 128)).astype(np.float32))
+    w = L.dev_bf16(rng.standard_normal((64, 128)).astype(np.float32))
+    out = torch.empty(64, 64, dtype=torch.float32, device="cuda")
+    ctx_tiny.linear(a, w, None, 64, 64, 128, out)          # aligned: accepted
+    for bad in (dict(a=_shifted(a, 4)), dict(w=_shifted(w, 2)), dict(out=_shifted(out, 1))):
+        args = dict(a=a, w=w, out=out)
+        args.update(bad)
+        with pytest.raises(L.DitError) as e:
+            ctx_tiny.linear(args["a"], args["w"], None, 64, 64, 128, args["out"])
+        assert e.value.status == L.EINVAL
+
+
 # --------------------------------------------------------------- unfused q/k/v prep (B arm)
 
 @pytest.mark.parametrize("name", ["tiny", "s1088", "s4608"])
