@@ -34,6 +34,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// The 32-bit value of another lane of the same 16-lane row, by a DPP row
+// permutation (CTRL: a quad_perm or row mirror code); all lanes active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of a row (lane bits 0..3), without the LDS: lane ^ 1
+// and lane ^ 2 by quad permutations, then the half-row and row mirrors, which
+// pair each lane with one of the other quad and half row -- whose values equal
+// those of lane ^ 4 and lane ^ 8 by then, so the sums are those of the xor
+// butterfly, bit for bit.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_row<0xb1>(v);    // quad_perm(1, 0, 3, 2)
+    v += dpp_row<0x4e>(v);    // quad_perm(2, 3, 0, 1)
+    v += dpp_row<0x141>(v);   // row_half_mirror
+    v += dpp_row<0x140>(v);   // row_mirror
+    return v;
+}
+
 // silu(x) = x * sigmoid(x); hardware reciprocal (1 ulp) of 1 + e^-x.
 __device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 

@@ -201,10 +201,7 @@ __device__ __forceinline__ void gemm_epilogue(f32x4 (&acc)[TMW][TN], int m0, int
                         ss += e * e + o * o;
                     }
                     // sum over the 16 lanes that share this row (lane bits 0..3)
-                    ss += __shfl_xor(ss, 1, 64);
-                    ss += __shfl_xor(ss, 2, 64);
-                    ss += __shfl_xor(ss, 4, 64);
-                    ss += __shfl_xor(ss, 8, 64);
+                    ss = row16_sum(ss);
                     const float rstd = rsqrtf(ss * (1.0f / 128.0f) + ep.qk_eps);
                     const int row = rbase + tm * 16 + r;
                     const int rr = min(row, M - 1);
@@ -494,10 +491,7 @@ __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, in
                         const float e = acc[tm][tp][r], o = acc[tm][tp + TN / 2][r];
                         ss += e * e + o * o;
                     }
-                    ss += __shfl_xor(ss, 1, 64);
-                    ss += __shfl_xor(ss, 2, 64);
-                    ss += __shfl_xor(ss, 4, 64);
-                    ss += __shfl_xor(ss, 8, 64);
+                    ss = row16_sum(ss);
                     rs[tm][r] = rsqrtf(ss * (1.0f / 128.0f) + ep.qk_eps);
                 }
         }

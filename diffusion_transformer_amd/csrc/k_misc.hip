@@ -397,10 +397,7 @@ k_qk_prep(const uint16_t *__restrict__ qkv, int S, int H, int Sh, const float *_
             float ss = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
-            ss += __shfl_xor(ss, 1, kWave);
-            ss += __shfl_xor(ss, 2, kWave);
-            ss += __shfl_xor(ss, 4, kWave);
-            ss += __shfl_xor(ss, 8, kWave);
+            ss = row16_sum(ss);
             const float rstd = rsqrtf(ss * (1.0f / 128.0f) + eps);
             const f32x4 c = *reinterpret_cast<const f32x4 *>(cs + static_cast<int64_t>(rr) * 64 + 4 * l16);
             const f32x4 sv = *reinterpret_cast<const f32x4 *>(sn + static_cast<int64_t>(rr) * 64 + 4 * l16);
