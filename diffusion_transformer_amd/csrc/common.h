@@ -34,6 +34,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// The adjacent-pair rotation (a, b) -> (a cos - b sin, a sin + b cos) in fp32
+// with one fixed rounding order (the second product rounded, then one fused
+// multiply-add each), packed to bf16: every kernel that rotates q and k gives
+// the same bits for the same inputs, whatever the compiler would contract.
+__device__ __forceinline__ uint32_t rotate_pack(float a, float b, float c, float s) {
+    return pack_bf16x2(__builtin_fmaf(a, c, -(b * s)), __builtin_fmaf(a, s, b * c));
+}
+
 // The 32-bit value of another lane of the same 16-lane row, by a DPP row
 // permutation (CTRL: a quad_perm or row mirror code); all lanes active.
 template <int CTRL>

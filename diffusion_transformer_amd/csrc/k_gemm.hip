@@ -216,7 +216,7 @@ __device__ __forceinline__ void gemm_epilogue(f32x4 (&acc)[TMW][TN], int m0, int
                             *reinterpret_cast<uint32_t *>(
                                 dst + (static_cast<int64_t>(head) * (ep.rows_total ? ep.rows_total : M) +
                                        ep.row_base + row) * 128 + 2 * p) =
-                                pack_bf16x2(a * c - b * s, a * s + b * c);
+                                rotate_pack(a, b, c, s);
                     }
                 }
         } else {
@@ -427,7 +427,7 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 //    0-127 are written by waves wm = 0, 1, rows 128-255 by wm = 2, 3.
 //  - QKV values (v): written straight from the accumulators (four
 //    consecutive rows of one feature are 8 contiguous bytes of vt).
-template <int EPI>
+template <int EPI, bool PRE = true>
 __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, int m0, int n0, int wm, int wn,
                                             int lane, int tid, int M, int N, const GemmEpi &ep) {
     const int pl = lane & 15, g = lane >> 4;
@@ -504,6 +504,19 @@ __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, in
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             if (hf) pp_barrier();                    // half 0 has been read
+            // QKV: this thread's rows' cos and sin (read back below), fetched
+            // before the staging so that their latency passes meanwhile
+            // (PRE; otherwise where they are used: fewer live registers)
+            f32x4 csr[4], snr[4];
+            auto fetch_cs = [&](int i) {
+                const int64_t gr = min(m0 + hf * 128 + (tid >> 4) + 32 * i, M - 1);
+                csr[i] = *reinterpret_cast<const f32x4 *>(ep.cos + gr * 64 + 4 * (tid & 15));
+                snr[i] = *reinterpret_cast<const f32x4 *>(ep.sin + gr * 64 + 4 * (tid & 15));
+            };
+            if constexpr (EPI == EPI_QKV && PRE) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fetch_cs(i);
+            }
             if ((wm >> 1) == hf) {
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
@@ -527,25 +540,27 @@ __device__ __forceinline__ void pp_epilogue(f32x4 (&acc)[TM][TN], u32x4 *lds, in
             pp_barrier();
             if constexpr (EPI == EPI_QKV) {
                 // thread -> 8 consecutive columns (4 rotation pairs) of one row
-                const int cg = tid & 31;
-                const int head = (n0 / 128) % ep.heads + (cg >> 4);
+                // in each of the tile's two heads: one cos and sin fetch serves both
+                const int c16 = tid & 15, p0 = 4 * c16;
+                const int head0 = (n0 / 128) % ep.heads;
                 uint16_t *dst = region == 0 ? ep.q : ep.k;
+                const int64_t hstride = static_cast<int64_t>(ep.rows_total ? ep.rows_total : M) * 128;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int row = (tid >> 5) + 16 * i, grow = m0 + hf * 128 + row;
+                for (int i = 0; i < 4; ++i) {
+                    const int row = (tid >> 4) + 32 * i, grow = m0 + hf * 128 + row;
                     if (grow >= M) continue;
                     const int sw = ((row >> 2) & 1) << 3;
-                    const f32x4 v0 = *reinterpret_cast<const f32x4 *>(L + row * 1024 + (((2 * cg) ^ sw) << 4));
-                    const f32x4 v1 = *reinterpret_cast<const f32x4 *>(L + row * 1024 + (((2 * cg + 1) ^ sw) << 4));
-                    const int p0 = 4 * (cg & 15);
-                    const f32x4 cs = *reinterpret_cast<const f32x4 *>(ep.cos + static_cast<int64_t>(grow) * 64 + p0);
-                    const f32x4 sn = *reinterpret_cast<const f32x4 *>(ep.sin + static_cast<int64_t>(grow) * 64 + p0);
-                    const u32x4 o = {pack_bf16x2(v0[0] * cs[0] - v0[1] * sn[0], v0[0] * sn[0] + v0[1] * cs[0]),
-                                     pack_bf16x2(v0[2] * cs[1] - v0[3] * sn[1], v0[2] * sn[1] + v0[3] * cs[1]),
-                                     pack_bf16x2(v1[0] * cs[2] - v1[1] * sn[2], v1[0] * sn[2] + v1[1] * cs[2]),
-                                     pack_bf16x2(v1[2] * cs[3] - v1[3] * sn[3], v1[2] * sn[3] + v1[3] * cs[3])};
-                    *reinterpret_cast<u32x4 *>(dst + (static_cast<int64_t>(head) * (ep.rows_total ? ep.rows_total : M) +
-                                                      ep.row_base + grow) * 128 + 2 * p0) = o;
+                    if constexpr (!PRE) fetch_cs(i);
+                    const f32x4 cs = csr[i], sn = snr[i];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int cg = c16 + 16 * h2;
+                        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(L + row * 1024 + (((2 * cg) ^ sw) << 4));
+                        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(L + row * 1024 + (((2 * cg + 1) ^ sw) << 4));
+                        const u32x4 o = {rotate_pack(v0[0], v0[1], cs[0], sn[0]), rotate_pack(v0[2], v0[3], cs[1], sn[1]),
+                                         rotate_pack(v1[0], v1[1], cs[2], sn[2]), rotate_pack(v1[2], v1[3], cs[3], sn[3])};
+                        *reinterpret_cast<u32x4 *>(dst + (head0 + h2) * hstride + (ep.row_base + grow) * 128 + 2 * p0) = o;
+                    }
                 }
             } else {
                 // thread -> 4 consecutive columns, rows tid/64 + 8i: one gate chunk
@@ -990,9 +1005,9 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
         pp_epilogue<EPI>(accf, lds, m0, n0, wm, wn, lane, tid, M, N, ep);
     } else if constexpr (EPI == EPI_QKV_SWIGLU) {
         if (swi) pp_epilogue<EPI_SWIGLU>(acc, lds, m0, n0 - ep.n_split, wm, wn, lane, tid, M, N - ep.n_split, ep);
-        else pp_epilogue<EPI_QKV>(acc, lds, m0, n0, wm, wn, lane, tid, M, ep.n_split, ep);
+        else pp_epilogue<EPI_QKV, !B32>(acc, lds, m0, n0, wm, wn, lane, tid, M, ep.n_split, ep);
     } else {
-        pp_epilogue<EPI>(acc, lds, m0, n0, wm, wn, lane, tid, M, N, ep);
+        pp_epilogue<EPI, !B32>(acc, lds, m0, n0, wm, wn, lane, tid, M, N, ep);
     }
 }
 

@@ -405,7 +405,7 @@ k_qk_prep(const uint16_t *__restrict__ qkv, int S, int H, int Sh, const float *_
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const float a = v[2 * p] * rstd * w[2 * p], b = v[2 * p + 1] * rstd * w[2 * p + 1];
-                o[p] = pack_bf16x2(a * c[p] - b * sv[p], a * sv[p] + b * c[p]);
+                o[p] = rotate_pack(a, b, c[p], sv[p]);
             }
             if (r < S)
                 *reinterpret_cast<u32x4 *>(dst + (static_cast<int64_t>(head) * Sh + r) * 128 + 8 * l16) =
