@@ -19,7 +19,10 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   calibration   secondary denominators measured on this machine: a chained large
              bf16 GEMM rate (20 chained 8192^3 products, the vendor library)
              and a 1 GiB device copy's bandwidth;
-  cpu_baseline  the CPU oracle timed on this host on a bounded sample.
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample;
+  power      the socket power and graphics clocks amd-smi reports while the
+             block runs in a loop for --power-seconds (read-only queries from
+             a child process; null if amd-smi is absent).
 """
 
 from __future__ import annotations
@@ -58,6 +61,8 @@ def parse():
     p.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 block timing")
     p.add_argument("--no-unfused", action="store_true", help="skip the unfused q/k/v prep arm's timing")
     p.add_argument("--no-calibration", action="store_true", help="skip the GEMM and copy calibration")
+    p.add_argument("--power-seconds", type=float, default=5.0,
+                   help="seconds of block loop under amd-smi power and clock sampling (0: skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device-to-device copy (a kernel of known traffic, the "
                         "scale reference for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -327,6 +332,54 @@ def summarize_counters(fetch_csv, write_csv, out_json, mfma_csv=None):
     print(json.dumps(res, indent=1, sort_keys=True))
 
 
+def sample_power(torch, run, seconds):
+    """Runs `run` (a batch of block forwards) back to back for `seconds` while
+    a thread queries amd-smi (socket power, graphics clock of each XCD) about
+    twice a second from a child process.  Returns the means and extremes of
+    the samples taken after the first second, or an error note."""
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return {"error": "amd-smi not found"}
+    samples, errors = [], []
+    stop = threading.Event()
+    t_start = time.time()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=10)
+                d = json.loads(r.stdout)["gpu_data"][0]
+                clk = [v["clk"]["value"] for k, v in d["clock"].items()
+                       if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+                if time.time() - t_start > 1.0 and clk:
+                    samples.append((float(d["power"]["socket_power"]["value"]), sum(clk) / len(clk),
+                                    min(clk), max(clk)))
+            except Exception as e:   # noqa: BLE001 -- a missing field or a failed query
+                errors.append(str(e)[:120])
+            stop.wait(0.4)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    n, t0 = 0, time.time()
+    while time.time() - t0 < seconds:
+        n += run()
+        torch.cuda.synchronize()
+    dt = time.time() - t0
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return {"error": "no amd-smi samples" + (f": {errors[0]}" if errors else "")}
+    w = [a[0] for a in samples]
+    return {"samples": len(samples), "seconds": round(dt, 2), "ms_per_block": round(1e3 * dt / n, 4),
+            "socket_w_mean": round(sum(w) / len(w), 1), "socket_w_max": max(w),
+            "gfx_mhz_mean": round(sum(a[1] for a in samples) / len(samples), 1),
+            "gfx_mhz_min": min(a[2] for a in samples), "gfx_mhz_max": max(a[3] for a in samples),
+            "tool": "amd-smi metric -p -c --json"}
+
+
 def time_blocks(L, torch, ctx, bw, x, seq, sh, steps, warmup, parallel=False):
     fwd = ctx.parallel_block_forward if parallel else ctx.block_forward
     for _ in range(warmup):
@@ -434,6 +487,16 @@ def main():
     per_step = percentiles(time_each(torch, lambda: ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N),
                                      max(20, args.steps)))
     log(f"single block forwards: p50 {per_step['p50']:.3f} ms, min {per_step['min']:.3f} ms")
+    power = None
+    if args.power_seconds > 0:
+        log(f"block loop for {args.power_seconds:.0f} s under amd-smi power and clock sampling")
+
+        def batch():
+            for _ in range(50):
+                ctx.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+            return 50
+        power = sample_power(torch, batch, args.power_seconds)
+        log(f"power: {power}")
     sb_bytes = stage_bytes(S, D, H, F)
     block_bytes = sum(v for k, v in sb_bytes.items() if k != "qk_prep")
     hbm = hbm_rows(stages, {k: sb_bytes[k] for k in ("mod", "norm1", "norm2")})
@@ -683,6 +746,7 @@ def main():
         "block_bytes": block_bytes,
         "frac_hbm": round(block_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "per_step_ms": per_step,
+        "power": power,
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
         "hbm_kernels": hbm,
