@@ -428,6 +428,26 @@ def test_block_rotary_special_tables_bit_exact(name):
     ctx.close()
 
 
+@pytest.mark.parametrize("name", ["s4608", "s4608_int8"])
+def test_block_forward_repeats_bit_identical(ctx_big, name):
+    """The same block on the same rows, three times in a row: every kernel
+    (the attention's per-wave pipeline, the products' tile schedules, the
+    int8 dequantisation on the second stream) gives the same bits."""
+    case = synth.block_case(name)
+    sh = case["shape"]
+    seq = GpuSeq(ctx_big, sh, case["t"], case["w_t1"], case["w_t2"])
+    bw = L.BlockWeights.from_host(case["block"])
+    say("block repeats", name)
+    outs = []
+    for _ in range(3):
+        x = L.dev_f32(case["x"])
+        ctx_big.block_forward(bw, x, seq.vec, seq.cos, seq.sin, sh.L, sh.N)
+        outs.append(x)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
 def test_block_rejects_bad_rows(ctx_tiny):
     case = synth.block_case("tiny")
     sh = case["shape"]
