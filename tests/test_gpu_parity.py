@@ -214,6 +214,22 @@ def test_attention(ctx_big, H, S, peak):
     compare("attention", got[rows], ref, bf16_stored=True)
 
 
+@pytest.mark.parametrize("S", [63, 65, 127, 128, 129, 191, 192, 193, 255, 257, 321])
+def test_attention_tile_boundaries(ctx_big, S):
+    """Key counts on and around the 64-key tiles: one to six tiles, full or
+    with a ragged last tile, so that every form of the per-wave pipeline
+    runs (the first tile's scores in the prologue, the inner tiles, the
+    masked tile before the last, the last tile's products) and the padding
+    of the last value tile (NaN here) is never read."""
+    H = 3
+    say("attention tile boundaries", H, S)
+    q, k, v = _attn_inputs(H, S, 7000 + S, 2.0)
+    got = _run_attention(ctx_big, q, k, v)
+    ref = O.attention(q, k, v).transpose(1, 0, 2).reshape(S, H * 128)
+    assert np.isfinite(got).all()
+    compare(f"attention-S{S}", got, ref, bf16_stored=True)
+
+
 def test_attention_degenerate_keys(ctx_big):
     # all keys equal -> every output row is the mean of the values
     H, S = 2, 150
