@@ -84,6 +84,7 @@ class Shape:
 SHAPES = {
     "tiny": Shape("tiny", 256, 2, 128, 1024, 8, 8, 8, seed=0),
     "s1088": Shape("s1088", 3072, 24, 128, 12288, 64, 32, 32, seed=2),
+    "r1077": Shape("r1077", 3072, 24, 128, 12288, 77, 25, 40, seed=11),
     "s4608": Shape("s4608", 3072, 24, 128, 12288, 512, 64, 64, seed=3),
     "s4608_int8": Shape("s4608_int8", 3072, 24, 128, 12288, 512, 64, 64, seed=4, int8=True),
     "s4608_w8a8": Shape("s4608_w8a8", 3072, 24, 128, 12288, 512, 64, 64, seed=6, w8a8=True),

@@ -300,8 +300,10 @@ def _intermediates(ctx, sh, S):
 
 
 @pytest.mark.parametrize("name,norm,norm_std", [("tiny", "layer", 0.0), ("tiny", "rms", 0.1),
-                                                 ("s1088", "layer", 0.0)])
+                                                 ("s1088", "layer", 0.0), ("r1077", "rms", 0.1)])
 def test_block_full_parity(name, norm, norm_std):
+    # r1077: 77 text + 25 x 40 image rows, ragged against the 64-key
+    # attention tiles and the 256-row product tiles at the full width
     case = synth.block_case(name, norm_std=norm_std, rms=(norm == "rms"))
     sh = case["shape"]
     la, oa = arch_pair(sh, norm)
