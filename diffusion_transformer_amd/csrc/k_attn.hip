@@ -20,7 +20,8 @@
 //    each wave keeps the matrix core fed with its own softmax work in
 //    between; sched_barrier fences hold the slots (and the slots hold no
 //    branches, past which the compiler would sink the exponentials).  A
-//    workgroup barrier ends every tile.
+//    workgroup barrier ends every tile; wave priorities stepped down through
+//    each tile keep the two waves of a SIMD level with each other.
 //  - the wave computes the TRANSPOSED scores S^T = K Q^T for a 64-key tile:
 //    K (from LDS) is the A operand, the wave's queries (registers, loaded
 //    once) the B operand.  A lane then holds one query column and 16 of its
@@ -314,6 +315,13 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
     auto step = [&](auto last_tag, int j) {
         const u32x4 *LK = Kb + ((j + 1) % NKB) * K_U4;
         const u32x4 *LV = Vb + (j % NVB) * V_U4;
+        // wave priority steps down through the tile (3, 2 after a quarter of
+        // the score products, 1 at the output products, 0 after two thirds
+        // of them): the SIMD's issue arbitration otherwise favours the older
+        // of its two waves, which then finishes each tile far ahead and
+        // leaves the younger one to run alone; this way the wave behind in
+        // the tile wins and both stay busy
+        __builtin_amdgcn_s_setprio(3);
         read_k(LK, 0);
         read_k(LK, 1);
 #pragma unroll
@@ -328,6 +336,7 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
             if (i == 6) issue_k(j + 3, i0 + 1);
             if (i == 10) issue_v(j + 2, i0);
             if (i == 13) issue_v(j + 2, i0 + 1);
+            if (i == 4) __builtin_amdgcn_s_setprio(2);
             qk_m(sb, i, 0);
             qk_m(sb, i, 1);
             if (i < 12) exp_pair(sa, i + 4);
@@ -335,6 +344,7 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            if (i == 0) __builtin_amdgcn_s_setprio(1);
             read_v(LV, i + 2);
             pv_m(i, 0);
             pv_m(i, 1);
@@ -346,6 +356,7 @@ k_attention(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kg,
 #pragma unroll
         for (int i = 8; i < 18; ++i) {
             if (i + 2 < 18) read_v(LV, i + 2);
+            if (i == 12) __builtin_amdgcn_s_setprio(0);
             pv_m(i, 0);
             pv_m(i, 1);
             if (i < 16) lane_max_piece(sa, i - 8);
