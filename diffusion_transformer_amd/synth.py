@@ -83,6 +83,11 @@ class Shape:
 
 SHAPES = {
     "tiny": Shape("tiny", 256, 2, 128, 1024, 8, 8, 8, seed=0),
+    # the smallest sequences the block takes: image rows only, one row, and
+    # fewer rows than one 16-row matrix block
+    "t_img": Shape("t_img", 256, 2, 128, 1024, 0, 8, 8, seed=21),
+    "t_one": Shape("t_one", 256, 2, 128, 1024, 0, 1, 1, seed=22),
+    "t_few": Shape("t_few", 256, 2, 128, 1024, 3, 1, 2, seed=23),
     "s1088": Shape("s1088", 3072, 24, 128, 12288, 64, 32, 32, seed=2),
     "r1077": Shape("r1077", 3072, 24, 128, 12288, 77, 25, 40, seed=11),
     "s4608": Shape("s4608", 3072, 24, 128, 12288, 512, 64, 64, seed=3),

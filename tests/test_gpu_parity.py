@@ -214,13 +214,14 @@ def test_attention(ctx_big, H, S, peak):
     compare("attention", got[rows], ref, bf16_stored=True)
 
 
-@pytest.mark.parametrize("S", [63, 65, 127, 128, 129, 191, 192, 193, 255, 257, 321])
+@pytest.mark.parametrize("S", [1, 5, 16, 17, 63, 65, 127, 128, 129, 191, 192, 193, 255, 257, 321])
 def test_attention_tile_boundaries(ctx_big, S):
     """Key counts on and around the 64-key tiles: one to six tiles, full or
     with a ragged last tile, so that every form of the per-wave pipeline
     runs (the first tile's scores in the prologue, the inner tiles, the
     masked tile before the last, the last tile's products) and the padding
-    of the last value tile (NaN here) is never read."""
+    of the last value tile (NaN here) is never read; down to one key and
+    query, fewer than one 16-row matrix block."""
     H = 3
     say("attention tile boundaries", H, S)
     q, k, v = _attn_inputs(H, S, 7000 + S, 2.0)
@@ -300,10 +301,13 @@ def _intermediates(ctx, sh, S):
 
 
 @pytest.mark.parametrize("name,norm,norm_std", [("tiny", "layer", 0.0), ("tiny", "rms", 0.1),
+                                                 ("t_img", "layer", 0.0), ("t_one", "rms", 0.1),
+                                                 ("t_few", "layer", 0.0),
                                                  ("s1088", "layer", 0.0), ("r1077", "rms", 0.1)])
 def test_block_full_parity(name, norm, norm_std):
     # r1077: 77 text + 25 x 40 image rows, ragged against the 64-key
-    # attention tiles and the 256-row product tiles at the full width
+    # attention tiles and the 256-row product tiles at the full width;
+    # t_img, t_one, t_few: no text rows, a single row, five rows
     case = synth.block_case(name, norm_std=norm_std, rms=(norm == "rms"))
     sh = case["shape"]
     la, oa = arch_pair(sh, norm)
