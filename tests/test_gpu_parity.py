@@ -333,7 +333,7 @@ def test_arm_switches_reject_other_values(ctx_tiny):
     assert L.raw().dit_set_int8_products(ctx_tiny.handle, 0) == L.OK
 
 
-@pytest.mark.parametrize("name", ["tiny", "s1088", "r1077"])
+@pytest.mark.parametrize("name", ["tiny", "t_one", "t_few", "s1088", "r1077"])
 @pytest.mark.parametrize("in_product", [False, True])
 def test_block_int8_full_parity(name, in_product):
     """int8 block-32 weights in the sequential block, every row and
@@ -642,6 +642,7 @@ def _parallel_gpu(ctx, case):
 
 
 @pytest.mark.parametrize("name,norm,norm_std", [("tiny", "layer", 0.0), ("tiny", "rms", 0.1),
+                                                 ("t_one", "layer", 0.0), ("t_few", "rms", 0.1),
                                                  ("s1088", "layer", 0.0), ("r1077", "layer", 0.0)])
 def test_parallel_block_full_parity(name, norm, norm_std):
     # below the ping-pong sizes: the four-product form
@@ -723,7 +724,8 @@ def _double_gpu(ctx, case):
     return x
 
 
-@pytest.mark.parametrize("name,in_product", [("tiny", False), ("s1088", False), ("r1077", False), ("s4608", False),
+@pytest.mark.parametrize("name,in_product", [("tiny", False), ("t_img", False), ("t_few", False), ("s1088", False),
+                                             ("r1077", False), ("s4608", False),
                                              ("s4608_int8", False), ("s4608_int8", True)])
 def test_double_block_full_parity(ctx_big, name, in_product):
     case = _double_case(name)
@@ -881,7 +883,7 @@ def test_block_runs_rejects_bad_runs(ctx_tiny):
 
 @pytest.mark.parametrize("name,norm,norm_std", [("tiny", "layer", 0.0), ("tiny", "rms", 0.1),
                                                  ("s1088", "layer", 0.0), ("s1088", "rms", 0.1),
-                                                 ("r1077", "rms", 0.1)])
+                                                 ("t_few", "layer", 0.0), ("r1077", "rms", 0.1)])
 def test_sandwich_block_full_parity(name, norm, norm_std):
     case = synth.block_case(name, norm_std=norm_std, rms=(norm == "rms"), sandwich=True)
     sh = case["shape"]
@@ -1087,6 +1089,8 @@ def _w8a8_gpu(ctx, case, runs=None, rotated=False):
                                                               ("s1088", "layer", 0.0, False, False),
                                                               ("tiny", "layer", 0.0, False, True),
                                                               ("tiny", "rms", 0.1, True, True),
+                                                              ("t_one", "layer", 0.0, False, False),
+                                                              ("t_few", "rms", 0.1, True, True),
                                                               ("s1088", "layer", 0.0, False, True),
                                                               ("r1077", "rms", 0.1, False, True)])
 def test_w8a8_block_full_parity(name, norm, norm_std, sandwich, rot):
