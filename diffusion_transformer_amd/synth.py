@@ -210,9 +210,11 @@ def model_case(name: str = "dit32", blocks=None, seed=None, hidden=None, heads=N
     ctx [L, text_dim] ~ N(0,1), and all weights (time MLP, in/out linears,
     final modulation, `blocks` blocks).  Overrides make reduced-size twins."""
     sh = SHAPES[name]
-    kw = dict(hidden=hidden or sh.hidden, heads=heads or sh.heads, ffn=ffn or sh.ffn,
-              L=L or sh.L, h=h or sh.h, w=w or sh.w, blocks=blocks or sh.blocks,
-              text_dim=text_dim or sh.text_dim)
+    def pick(v, d):
+        return d if v is None else v
+    kw = dict(hidden=pick(hidden, sh.hidden), heads=pick(heads, sh.heads), ffn=pick(ffn, sh.ffn),
+              L=pick(L, sh.L), h=pick(h, sh.h), w=pick(w, sh.w), blocks=pick(blocks, sh.blocks),
+              text_dim=pick(text_dim, sh.text_dim))
     sh = Shape(sh.name, kw["hidden"], kw["heads"], sh.head_dim, kw["ffn"], kw["L"], kw["h"],
                kw["w"], seed=sh.seed if seed is None else seed, blocks=kw["blocks"],
                latent=sh.latent, text_dim=kw["text_dim"], time_dim=sh.time_dim, axes=sh.axes)

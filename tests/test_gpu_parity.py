@@ -1425,16 +1425,18 @@ def test_sigma_schedule_bit_exact(shift):
 
 # --------------------------------------------------------------- denoise
 
-@pytest.mark.parametrize("w8a8", [False, True])
-def test_denoise_twin(ctx_tiny, w8a8):
+@pytest.mark.parametrize("w8a8,Lh", [(False, (8, 8, 8)), (True, (8, 8, 8)), (False, (0, 4, 4))])
+def test_denoise_twin(ctx_tiny, w8a8, Lh):
     """A reduced-width DiT (hidden 256, 2 heads, 3 blocks, 8 text + 8x8 image
     rows, text features 256-d) through the full 4-step loop; bf16 or W8A8
-    block weights."""
-    m = synth.model_case("dit32", blocks=3, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8, text_dim=256, w8a8=w8a8)
+    block weights; and one with no text rows (4x4 image rows only, no
+    prologue: the step takes no text)."""
+    Ln, h, w = Lh
+    m = synth.model_case("dit32", blocks=3, hidden=256, heads=2, ffn=1024, L=Ln, h=h, w=w, text_dim=256, w8a8=w8a8)
     sh = m["shape"]
     la, oa = arch_pair(sh)
     ctx = L.Context(la, max_rows=sh.S)
-    say("denoise twin S =", sh.S)
+    say("denoise twin S =", sh.S, "L =", sh.L)
     mw = L.ModelWeights.from_host(m["top"], m["blocks"])
     pos = torch.empty((sh.S, 3), dtype=torch.int32, device="cuda")
     ctx.positions(sh.L, sh.h, sh.w, pos)
@@ -1442,7 +1444,8 @@ def test_denoise_twin(ctx_tiny, w8a8):
     sn = torch.empty_like(cs)
     ctx.rope_tables(pos, sh.S, cs, sn)
     txt = torch.empty((sh.L, sh.hidden), dtype=torch.float32, device="cuda")
-    ctx.prologue(mw, L.dev_f32(m["ctx"]), sh.L, txt)
+    if sh.L > 0:
+        ctx.prologue(mw, L.dev_f32(m["ctx"]), sh.L, txt)
     x = L.dev_f32(m["x_lat"])
     sig = O.sigma_grid(4)
     vels = []
@@ -1454,7 +1457,8 @@ def test_denoise_twin(ctx_tiny, w8a8):
     ow = O.ModelWeights(**m["top"], blocks=[oracle_block(b) for b in m["blocks"]])
     opos = O.positions(sh.L, sh.h, sh.w)
     ocs, osn = O.rope_tables(opos, sh.axes)
-    compare("txt", np_of(txt), O.text_rows(m["ctx"], ow))
+    if sh.L > 0:
+        compare("txt", np_of(txt), O.text_rows(m["ctx"], ow))
     xr, vr = O.denoise(m["x_lat"], m["ctx"], ow, ocs, osn, sig, oa, keep_velocities=True)
     compare("vel0", np_of(vels[0]), vr[0])
     for i in range(1, 4):
