@@ -9,8 +9,11 @@ Prints ONE JSON line on stdout (progress goes to stderr):
              attention, the modulation GEMV) over the measured time of K
              consecutive dit_block_forward calls (inputs resident in HBM);
   images_per_s  the whole path for one image: positions and rotary tables,
-             the text-row prologue and 4 Euler steps of a 32-block DiT
-             (random-init bf16 weights), timed over I images;
+             the text-row prologue, the schedule's modulation planned
+             (dit_plan_schedule: each modulation weight read once for the
+             4 steps) and 4 Euler steps of a 32-block DiT (random-init bf16
+             weights), timed over I images; `unplanned` the same without
+             the plan (each step computes its own modulation);
   roofline   the dominant kernel's algorithmic TFLOP/s from HIP events around
              its launches, against the bf16 dense MFMA peak;
   per_step_ms   p50 / min / max of single block forwards (HIP events per call);
@@ -773,9 +776,9 @@ def main():
         img["image_frac_hbm"] = round(img_bytes / (img["ms_per_image"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         out.update(img)
     if img8:
-        out["w8a8_image"] = {k: img8[k] for k in ("images_per_s", "ms_per_image", "image_finite", "image_workload")}
+        out["w8a8_image"] = {k: img8[k] for k in ("images_per_s", "ms_per_image", "unplanned", "image_finite", "image_workload")}
     if imgi8:
-        out["int8_image"] = {k: imgi8[k] for k in ("images_per_s", "ms_per_image", "image_finite", "image_workload")}
+        out["int8_image"] = {k: imgi8[k] for k in ("images_per_s", "ms_per_image", "unplanned", "image_finite", "image_workload")}
     out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
@@ -833,25 +836,30 @@ def bench_images(torch, L, synth, images, w8a8=False, int8=False):
     txt = torch.empty((sh.L, D), dtype=torch.float32, device="cuda")
     sig = np.linspace(1.0, 0.0, 5).astype(np.float32)
 
-    def one_image(x):
+    def one_image(x, planned=True):
         ctx.positions(sh.L, sh.h, sh.w, pos)
         ctx.rope_tables(pos, S, cs, sn)
         ctx.prologue(model, ctx_feats, sh.L, txt)
+        ctx.plan_schedule(model, sig[:4] if planned else [])
         for i in range(4):
             ctx.denoise_step(model, x, txt, cs, sn, sh.L, sh.N, float(sig[i]), float(sig[i + 1]))
 
     x = x0.clone()
-    one_image(x)                       # warm-up image
-    torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(images):
-        x.copy_(x0)
-        one_image(x)
-    e1.record(st)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / images
+
+    def timed(planned):
+        one_image(x, planned)              # warm-up image
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(images):
+            x.copy_(x0)
+            one_image(x, planned)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / images
+    ms_un = timed(False)
+    ms = timed(True)
     finite = bool(torch.isfinite(x).all().item())
 
     # the per-image prologue on its own (positions, tables, text rows), and
@@ -871,13 +879,14 @@ def bench_images(torch, L, synth, images, w8a8=False, int8=False):
     img_flops = 4 * (sh.blocks * blk + 2 * sh.N * lat * D + 2 * sh.N * D * lat + 2 * D * 256
                      + 2 * D * D + 2 * 2 * D * D) + 2 * sh.L * sh.text_dim * D
     log(f"image{'' if kind == 'bf16' else ' (' + kind + ')'}: {ms:.1f} ms  {1000 / ms:.3f} img/s  {img_flops / ms / 1e9:.1f} TFLOP/s  "
-        f"finite={finite}")
+        f"finite={finite}  (unplanned {ms_un:.1f} ms)")
     ctx.close()
     del model, blocks, top
     torch.cuda.empty_cache()
     return {"images_per_s": round(1000.0 / ms, 4), "ms_per_image": round(ms, 2),
             "prologue_ms": pro, "steps_ms": round(ms - pro["p50"], 2), "euler_ms": euler_ms,
             "image_tflops": round(img_flops / ms / 1e9, 2), "image_flops": img_flops,
+            "unplanned": {"images_per_s": round(1000.0 / ms_un, 4), "ms_per_image": round(ms_un, 2)},
             "image_workload": "32-block DiT, 4 Euler steps (sigmas 1, .75, .5, .25, 0), L=512 + N=4096, "
                               f"latent 64, text features 4096-d, batch 1, random-init {kind} "
                               "block weights",

@@ -60,6 +60,15 @@ struct dit_ctx {
     // products run; the events order it against the context's stream
     hipStream_t side = nullptr;
     hipEvent_t ev_fork = nullptr, ev_ready[4] = {};
+    // a planned schedule (dit_plan_schedule): the time vectors [n][D], every
+    // block's modulation rows [n][blocks][6D] and the final layer's [n][2D]
+    // for the sigmas plan_sig, computed from the weights named in plan_keys
+    // (time MLP, final modulation, each block's modulation weight)
+    float *plan_mem = nullptr, *plan_vec = nullptr, *plan_mod = nullptr, *plan_fmod = nullptr;
+    size_t plan_bytes = 0;
+    int plan_n = 0;
+    std::vector<float> plan_sig;
+    std::vector<const void *> plan_keys;
     std::string err;
     // stage timing
     bool timing = false;
@@ -574,17 +583,19 @@ dit_status ref_copy(dit_ctx *c, uint16_t *slot_mut, const uint16_t *slot, int fi
 // the attention's queries are rows [0, S) against all Sk keys.
 dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const float *vecs, int R, const int32_t *runs,
                               int n_runs, const float *cs, const float *sn, int S, int Sk = 0,
-                              const uint16_t *slot = nullptr) {
+                              const uint16_t *slot = nullptr, const float *pre_mod = nullptr) {
     const dit_arch &A = c->arch;
     const int D = A.hidden, F = A.ffn, H = A.heads;
     if (Sk < S) Sk = S;
     const int Sp = round_up(Sk, 64);
     const bool rms = A.norm == DIT_NORM_RMS;
     hipStream_t st = c->stream;
-    float *mod = c->mod;
-    for (int r = 0; r < R; ++r) {
+    // the modulation rows: computed here, or given (one vector's six rows,
+    // from a planned schedule)
+    const float *mod = pre_mod ? pre_mod : c->mod;
+    for (int r = 0; r < R && !pre_mod; ++r) {
         Stage t(c, DIT_ST_MOD);
-        DIT_LAUNCH(c, launch_gemv(b->w_mod, vecs + int64_t(r) * D, 6 * D, D, true, mod + int64_t(r) * 6 * D, st),
+        DIT_LAUNCH(c, launch_gemv(b->w_mod, vecs + int64_t(r) * D, 6 * D, D, true, c->mod + int64_t(r) * 6 * D, st),
                    "modulation");
     }
     // W8A8 (DIT_W_INT8_ROW, DIT_W_INT8_ROT): every product takes its A rows
@@ -772,9 +783,9 @@ dit_status block_forward_runs(dit_ctx *c, const dit_block *b, float *x, const fl
 // The block forward ([GZ] Block.forward; validated arguments): one run of
 // all rows on the one modulation row.
 dit_status block_forward(dit_ctx *c, const dit_block *b, float *x, const float *vec, const float *cs,
-                         const float *sn, int S) {
+                         const float *sn, int S, const float *pre_mod = nullptr) {
     const int32_t one[3] = {0, S, 0};
-    return block_forward_runs(c, b, x, vec, 1, one, 1, cs, sn, S);
+    return block_forward_runs(c, b, x, vec, 1, one, 1, cs, sn, S, 0, nullptr, pre_mod);
 }
 
 dit_status time_vector(dit_ctx *c, const uint16_t *w1, const uint16_t *w2, float t, float *vec) {
@@ -806,6 +817,24 @@ dit_status check_model(dit_ctx *c, const dit_model *m) {
         return fail(c, DIT_EINVAL, "a model weight pointer is NULL");
     for (int i = 0; i < m->n_blocks; ++i) DIT_TRY(check_block(c, &m->blocks[i], false, true));
     return DIT_OK;
+}
+
+// the steps a schedule may plan
+constexpr int kMaxPlanSteps = 64;
+
+// the weights a plan's rows are computed from, in a fixed order
+std::vector<const void *> plan_keys_of(const dit_model *m) {
+    std::vector<const void *> k = {m->w_t1, m->w_t2, m->w_fmod};
+    for (int i = 0; i < m->n_blocks; ++i) k.push_back(m->blocks[i].w_mod);
+    return k;
+}
+
+// the planned step of sigma (the same bits) for this model's weights, or -1
+int plan_step(const dit_ctx *c, const dit_model *m, float sigma) {
+    if (c->plan_n == 0 || c->plan_keys != plan_keys_of(m)) return -1;
+    for (int i = 0; i < c->plan_n; ++i)
+        if (std::memcmp(&c->plan_sig[i], &sigma, sizeof(float)) == 0) return i;
+    return -1;
 }
 
 }  // namespace
@@ -903,6 +932,7 @@ void dit_ctx_destroy(dit_ctx *ctx) {
         for (hipEvent_t e : ctx->spare) hipEventDestroy(e);
         hipFree(ctx->pool);
         if (ctx->wdq) hipFree(ctx->wdq);
+        if (ctx->plan_mem) hipFree(ctx->plan_mem);
         if (ctx->ev_fork) hipEventDestroy(ctx->ev_fork);
         for (hipEvent_t e : ctx->ev_ready)
             if (e) hipEventDestroy(e);
@@ -1252,7 +1282,9 @@ dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, cons
     const int D = A.hidden, S = L + N, lat = A.latent;
     hipStream_t st = ctx->stream;
 
-    DIT_TRY(time_vector(ctx, m->w_t1, m->w_t2, dit_time_input(sigma), ctx->vec));
+    // a planned step takes its modulation rows from the plan
+    const int pi = plan_step(ctx, m, sigma);
+    if (pi < 0) DIT_TRY(time_vector(ctx, m->w_t1, m->w_t2, dit_time_input(sigma), ctx->vec));
     {
         Stage tm(ctx, DIT_ST_IMG_IN);
         if (L > 0 &&
@@ -1265,11 +1297,14 @@ dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, cons
         e.ldo = D;
         DIT_LAUNCH(ctx, launch_gemm(ctx->latb, m->w_in, nullptr, false, N, D, lat, e, st, true), "img_in");
     }
-    for (int i = 0; i < m->n_blocks; ++i) DIT_TRY(block_forward(ctx, &m->blocks[i], ctx->seq, ctx->vec, cos_t, sin_t, S));
+    for (int i = 0; i < m->n_blocks; ++i)
+        DIT_TRY(block_forward(ctx, &m->blocks[i], ctx->seq, ctx->vec, cos_t, sin_t, S,
+                              pi < 0 ? nullptr : ctx->plan_mod + (int64_t(pi) * m->n_blocks + i) * 6 * D));
     {
         Stage tm(ctx, DIT_ST_FINAL);
-        DIT_LAUNCH(ctx, launch_gemv(m->w_fmod, ctx->vec, 2 * D, D, true, ctx->fmod, st), "final modulation");
-        DIT_LAUNCH(ctx, launch_modnorm(ctx->seq + static_cast<size_t>(L) * D, N, D, ctx->fmod, ctx->fmod + D, nullptr,
+        const float *fm = pi < 0 ? ctx->fmod : ctx->plan_fmod + int64_t(pi) * 2 * D;
+        if (pi < 0) DIT_LAUNCH(ctx, launch_gemv(m->w_fmod, ctx->vec, 2 * D, D, true, ctx->fmod, st), "final modulation");
+        DIT_LAUNCH(ctx, launch_modnorm(ctx->seq + static_cast<size_t>(L) * D, N, D, fm, fm + D, nullptr,
                                        false, A.final_eps, ctx->h, st),
                    "final norm");
         GemmEpi f{};
@@ -1286,6 +1321,60 @@ dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, cons
                                       st) != hipSuccess)
             return fail(ctx, DIT_EDEVICE, "copy of the velocity failed");
     }
+    return DIT_OK;
+}
+
+dit_status dit_plan_schedule(dit_ctx *ctx, const dit_model *m, const float *sigmas, int n) {
+    if (!ctx) return fail(nullptr, DIT_EINVAL, "context is NULL");
+    if (n < 0 || n > kMaxPlanSteps) return fail(ctx, DIT_ERANGE, "n = %d outside 0..%d", n, kMaxPlanSteps);
+    if (n > 0 && !sigmas) return fail(ctx, DIT_EINVAL, "sigmas is NULL");
+    DIT_TRY(check_ctx(ctx));
+    // whatever happens below, the old plan is gone
+    ctx->plan_n = 0;
+    ctx->plan_sig.clear();
+    ctx->plan_keys.clear();
+    if (n == 0) return DIT_OK;
+    DIT_TRY(check_model(ctx, m));
+    for (int i = 0; i < n; ++i)
+        if (!std::isfinite(sigmas[i])) return fail(ctx, DIT_ERANGE, "sigmas[%d] is not finite", i);
+    const int D = ctx->arch.hidden, nb = m->n_blocks;
+    hipStream_t st = ctx->stream;
+    const size_t need = (size_t(n) * D + size_t(n) * nb * 6 * D + size_t(n) * 2 * D) * sizeof(float);
+    if (need > ctx->plan_bytes) {
+        // earlier steps may still read the old rows
+        if (hipStreamSynchronize(st) != hipSuccess) return fail(ctx, DIT_EDEVICE, "stream synchronize failed");
+        if (ctx->plan_mem) hipFree(ctx->plan_mem);
+        ctx->plan_mem = nullptr;
+        ctx->plan_bytes = 0;
+        void *p = nullptr;
+        if (hipMalloc(&p, need) != hipSuccess) return fail(ctx, DIT_ENOMEM, "plan of %zu bytes failed", need);
+        ctx->plan_mem = static_cast<float *>(p);
+        ctx->plan_bytes = need;
+    }
+    ctx->plan_vec = ctx->plan_mem;
+    ctx->plan_mod = ctx->plan_vec + size_t(n) * D;
+    ctx->plan_fmod = ctx->plan_mod + size_t(n) * nb * 6 * D;
+    for (int i = 0; i < n; ++i)
+        DIT_TRY(time_vector(ctx, m->w_t1, m->w_t2, dit_time_input(sigmas[i]), ctx->plan_vec + int64_t(i) * D));
+    // each weight read once for up to four steps
+    for (int i0 = 0; i0 < n; i0 += 4) {
+        const int nv = std::min(4, n - i0);
+        const float *vec = ctx->plan_vec + int64_t(i0) * D;
+        {
+            Stage tm(ctx, DIT_ST_MOD);
+            for (int b = 0; b < nb; ++b)
+                DIT_LAUNCH(ctx, launch_gemv_multi(m->blocks[b].w_mod, vec, D, nv, 6 * D, D, true,
+                                                  ctx->plan_mod + (int64_t(i0) * nb + b) * 6 * D, int64_t(nb) * 6 * D, st),
+                           "planned modulation");
+        }
+        Stage tm(ctx, DIT_ST_FINAL);
+        DIT_LAUNCH(ctx, launch_gemv_multi(m->w_fmod, vec, D, nv, 2 * D, D, true, ctx->plan_fmod + int64_t(i0) * 2 * D,
+                                          2 * D, st),
+                   "planned final modulation");
+    }
+    ctx->plan_sig.assign(sigmas, sigmas + n);
+    ctx->plan_keys = plan_keys_of(m);
+    ctx->plan_n = n;
     return DIT_OK;
 }
 

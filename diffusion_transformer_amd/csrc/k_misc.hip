@@ -7,6 +7,8 @@
 // Modulation, normedInto; s.1 of the host contract for the int8 format.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -172,59 +174,124 @@ hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *y, hipStream_t st
 }
 
 // ---------------------------------------------------------------------- GEMV
-// One wave per output row, 16-byte loads of W (8 bf16 per lane per step),
-// the input vector staged once per block in LDS (with silu applied).  The
-// weight is read exactly once: the kernel is HBM-bound, so a lane issues all
-// its loads of a row (at most 8) before the first multiply, keeping several
-// in flight per wave; the sum runs in the same order as a one-load loop.
+// One wave per output row, 16-byte loads of W (8 bf16 per lane per step).
+// A lane always takes the same columns (chunks lane + 64j of 8), so it holds
+// its columns of the input vectors in registers, loaded once (with silu
+// applied) before its first row.  The weight is read exactly once: the
+// kernel is HBM-bound, so a lane issues all its loads of a row before the
+// first multiply, keeping several in flight per wave; the sum runs in the
+// same order as a one-load loop.  NV vectors share each row's loads (the
+// planned schedule's steps); every vector's sum is formed by the same
+// expressions in the same order whatever NV is, so a row's result does not
+// depend on how many vectors share the launch.  JM chunks per lane at most
+// (I <= 512 * JM).
 constexpr int kGemvThreads = 256;
 constexpr int kGemvMaxI = 4096;
+constexpr int kGemvMaxV = 4;
 
+template <int NV, int JM>
 __global__ void __launch_bounds__(kGemvThreads)
-k_gemv(const uint16_t *__restrict__ W, const float *__restrict__ x, int O, int I, int silu_in,
-       float *__restrict__ y) {
-    __shared__ float xs[kGemvMaxI];
-    for (int i = threadIdx.x; i < I; i += kGemvThreads) {
-        float v = x[i];
-        xs[i] = silu_in ? silu_f(v) : v;
-    }
-    __syncthreads();
+k_gemv(const uint16_t *__restrict__ W, const float *__restrict__ x, int64_t ldx, int O, int I, int silu_in,
+       float *__restrict__ y, int64_t ldy) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int nchunk = I / 8;
+    float4 xr[NV][JM][2];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int c = lane + 64 * j;
+            float4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+            if (c < nchunk) {
+                a = *reinterpret_cast<const float4 *>(x + v * ldx + c * 8);
+                b = *reinterpret_cast<const float4 *>(x + v * ldx + c * 8 + 4);
+                if (silu_in) {
+                    a = float4{silu_f(a.x), silu_f(a.y), silu_f(a.z), silu_f(a.w)};
+                    b = float4{silu_f(b.x), silu_f(b.y), silu_f(b.z), silu_f(b.w)};
+                }
+            }
+            xr[v][j][0] = a;
+            xr[v][j][1] = b;
+        }
     for (int o = blockIdx.x * 4 + wv; o < O; o += gridDim.x * 4) {
         const u32x4 *row = reinterpret_cast<const u32x4 *>(W + static_cast<int64_t>(o) * I);
-        constexpr int J = kGemvMaxI / 8 / 64;
-        u32x4 wr[J];
+        u32x4 wr[JM];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
+        for (int j = 0; j < JM; ++j) {
             const int c = lane + 64 * j;
             wr[j] = c < nchunk ? __builtin_nontemporal_load(row + c) : u32x4{0u, 0u, 0u, 0u};
         }
-        float acc = 0.f;
+        float acc[NV];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
+        for (int v = 0; v < NV; ++v) acc[v] = 0.f;
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
             const int c = lane + 64 * j;
             if (c >= nchunk) break;
             const u32x4 w = wr[j];
-            const float *xp = xs + c * 8;
-            acc += bf16lo_to_f32(w.x) * xp[0] + bf16hi_to_f32(w.x) * xp[1];
-            acc += bf16lo_to_f32(w.y) * xp[2] + bf16hi_to_f32(w.y) * xp[3];
-            acc += bf16lo_to_f32(w.z) * xp[4] + bf16hi_to_f32(w.z) * xp[5];
-            acc += bf16lo_to_f32(w.w) * xp[6] + bf16hi_to_f32(w.w) * xp[7];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const float4 a = xr[v][j][0], b = xr[v][j][1];
+                acc[v] += bf16lo_to_f32(w.x) * a.x + bf16hi_to_f32(w.x) * a.y;
+                acc[v] += bf16lo_to_f32(w.y) * a.z + bf16hi_to_f32(w.y) * a.w;
+                acc[v] += bf16lo_to_f32(w.z) * b.x + bf16hi_to_f32(w.z) * b.y;
+                acc[v] += bf16lo_to_f32(w.w) * b.z + bf16hi_to_f32(w.w) * b.w;
+            }
         }
-        acc = wave_sum(acc);
-        if (lane == 0) y[o] = acc;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const float t = wave_sum(acc[v]);
+            if (lane == 0) y[v * ldy + o] = t;
+        }
+    }
+}
+
+// One launch of k_gemv<NV, JM>: as many blocks as the device holds at once
+// (each wave loads its vector columns once, then walks its rows), at most
+// one row per wave.
+template <int NV, int JM>
+hipError_t launch_gemv_nv(const uint16_t *W, const float *x, int64_t ldx, int O, int I, int si, float *y,
+                          int64_t ldy, hipStream_t st) {
+    static int resident[64] = {};   // blocks the device holds at once, per device id
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (resident[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<NV, JM>, kGemvThreads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidValue;
+        resident[dev] = std::max(1, per_cu) * std::max(1, cus);
+    }
+    const int blocks = std::min((O + 3) / 4, resident[dev]);
+    k_gemv<NV, JM><<<blocks, kGemvThreads, 0, st>>>(W, x, ldx, O, I, si, y, ldy);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_multi(const uint16_t *W, const float *x, int64_t ldx, int nv, int O, int I, bool silu_in,
+                             float *y, int64_t ldy, hipStream_t st) {
+    if (O <= 0 || nv == 0) return hipSuccess;
+    if (I <= 0 || I > kGemvMaxI || I % 8 || nv < 0 || nv > kGemvMaxV) return hipErrorInvalidValue;
+    const int si = silu_in ? 1 : 0;
+    // the vectors' columns a lane holds: 8 * JM of each (JM 6 covers I <= 3072)
+    if (I <= 3072) {
+        switch (nv) {
+            case 1: return launch_gemv_nv<1, 6>(W, x, ldx, O, I, si, y, ldy, st);
+            case 2: return launch_gemv_nv<2, 6>(W, x, ldx, O, I, si, y, ldy, st);
+            case 3: return launch_gemv_nv<3, 6>(W, x, ldx, O, I, si, y, ldy, st);
+            default: return launch_gemv_nv<4, 6>(W, x, ldx, O, I, si, y, ldy, st);
+        }
+    }
+    switch (nv) {
+        case 1: return launch_gemv_nv<1, 8>(W, x, ldx, O, I, si, y, ldy, st);
+        case 2: return launch_gemv_nv<2, 8>(W, x, ldx, O, I, si, y, ldy, st);
+        case 3: return launch_gemv_nv<3, 8>(W, x, ldx, O, I, si, y, ldy, st);
+        default: return launch_gemv_nv<4, 8>(W, x, ldx, O, I, si, y, ldy, st);
     }
 }
 
 hipError_t launch_gemv(const uint16_t *W, const float *x, int O, int I, bool silu_in, float *y,
                        hipStream_t st) {
-    if (O <= 0) return hipSuccess;
-    if (I <= 0 || I > kGemvMaxI || I % 8) return hipErrorInvalidValue;
-    int blocks = (O + 3) / 4;
-    if (blocks > 2048) blocks = 2048;
-    k_gemv<<<blocks, kGemvThreads, 0, st>>>(W, x, O, I, silu_in ? 1 : 0, y);
-    return hipGetLastError();
+    return launch_gemv_multi(W, x, I, 1, O, I, silu_in, y, O, st);
 }
 
 // ------------------------------------------------------------ modulated norm

@@ -22,9 +22,13 @@ hipError_t launch_dequant(const int8_t *q, const uint16_t *s, int out, int in, f
 hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *y, hipStream_t st);
 
 // y[o] = sum_i W[o, i] * f(x[i]); f = silu when silu_in, else identity.
-// W bf16 [O, I]; x, y fp32.  I a multiple of 8.
+// W bf16 [O, I]; x, y fp32.  I a multiple of 8, at most 4096.
 hipError_t launch_gemv(const uint16_t *W, const float *x, int O, int I, bool silu_in, float *y,
                        hipStream_t st);
+// The same for nv <= 4 vectors at once, W read once: vector v is x + v*ldx,
+// its result y + v*ldy; each result equals launch_gemv's bit for bit.
+hipError_t launch_gemv_multi(const uint16_t *W, const float *x, int64_t ldx, int nv, int O, int I, bool silu_in,
+                             float *y, int64_t ldy, hipStream_t st);
 
 // out[r] = bf16(norm(x[r]) * (1 + scale) + shift), r < rows; D <= 4096,
 // D a multiple of 4.  rms: RMSNorm times norm_w; else LayerNorm.

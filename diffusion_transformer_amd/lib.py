@@ -95,6 +95,7 @@ _SIGS = {
     "dit_denoise_step": (C.c_int, [_P, C.POINTER(Model), _P, _P, _P, _P, C.c_int, C.c_int,
                                    C.c_float, C.c_float, _P]),
     "dit_euler_step": (C.c_int, [_P, _P, _P, C.c_int64, C.c_float, C.c_float]),
+    "dit_plan_schedule": (C.c_int, [_P, C.POINTER(Model), _P, C.c_int]),
     "dit_dequant_int8_b32": (C.c_int, [_P, _P, _P, C.c_int, C.c_int, _P]),
     "dit_debug_copy": (C.c_int, [_P, C.c_int, _P, C.c_int64]),
     "dit_timing_enable": (C.c_int, [_P, C.c_int]),
@@ -318,6 +319,14 @@ class Context:
                    _ptr(txt, torch.float32, "txt"), _ptr(cos, torch.float32, "cos"),
                    _ptr(sin, torch.float32, "sin"), L, N, float(sigma), float(sigma_next),
                    _ptr(vel_out, torch.float32, "vel_out"))
+
+    def plan_schedule(self, model: "ModelWeights", sigmas):
+        """dit_plan_schedule: the modulation of the steps at the host values
+        `sigmas` (float32, compared bit for bit by later steps); an empty
+        sequence drops the plan."""
+        sg = np.ascontiguousarray(np.asarray(sigmas, dtype=np.float32))
+        self._call("dit_plan_schedule", C.byref(model.struct),
+                   sg.ctypes.data_as(C.c_void_p) if len(sg) else None, len(sg))
 
     def euler_step(self, x, v, n, sigma, sigma_next):
         self._call("dit_euler_step", _ptr(x, torch.float32, "x"), _ptr(v, torch.float32, "v"),

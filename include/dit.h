@@ -400,6 +400,26 @@ dit_status dit_denoise_step(dit_ctx *ctx, const dit_model *m, float *x_lat, cons
                             const float *cos, const float *sin, int L, int N, float sigma,
                             float sigma_next, float *vel_out);
 
+/* Plans a schedule's modulation on the context.  The modulation of every
+ * block and of the final layer depends on the step only through sigma
+ * ([HC] s.6: the time input of each step), so, like the text rows and the
+ * rotary tables that [K4] Appendix B D2 hoists out of the Euler loop, it
+ * can be computed before the loop: for each of the n host values sigmas[i]
+ * the time vector, every block's six modulation rows (w_mod * silu(vec))
+ * and the final layer's two, reading each modulation weight once for up to
+ * four steps.  A later dit_denoise_step on this context whose sigma has the
+ * same bits as a planned sigma, with a model naming the same time-MLP,
+ * final-modulation and block modulation weights (pointers), takes the
+ * planned rows instead of computing them: the same values, bit for bit.
+ * Any other step computes its own, as without a plan.  The plan holds the
+ * rows as computed here: plan again after changing those weights in place.
+ * n = 0 drops the plan.  The context allocates the plan's memory
+ * (n * (3 + 6 * blocks) * D floats) on first use and keeps the largest
+ * until dit_ctx_destroy; a call replaces the previous plan, on failure
+ * leaving none.  Errors: DIT_ERANGE (n outside 0..64, a sigma not finite),
+ * DIT_EINVAL (NULL sigmas with n > 0, a bad model), DIT_ENOMEM. */
+dit_status dit_plan_schedule(dit_ctx *ctx, const dit_model *m, const float *sigmas, int n);
+
 /* [HC] s.6 Euler update, fp32, unfused: x[i] = x[i] + (float)(sigma_next -
  * sigma) * v[i] (difference, product and sum each rounded to fp32).
  * x, v fp32 [n]; n >= 0 (0 is a no-op). */

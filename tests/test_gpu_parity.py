@@ -9,6 +9,7 @@ grid axis, ragged tails and the full 1024-px block.
 """
 
 import contextlib
+import ctypes as C
 
 import numpy as np
 import pytest
@@ -1424,6 +1425,94 @@ def test_sigma_schedule_bit_exact(shift):
         L.sigma_schedule(grid, 0.0)
 
 # --------------------------------------------------------------- denoise
+
+def _twin_setup(m):
+    sh = m["shape"]
+    la, _ = arch_pair(sh)
+    ctx = L.Context(la, max_rows=sh.S)
+    mw = L.ModelWeights.from_host(m["top"], m["blocks"])
+    pos = torch.empty((sh.S, 3), dtype=torch.int32, device="cuda")
+    ctx.positions(sh.L, sh.h, sh.w, pos)
+    cs = torch.empty((sh.S, 64), dtype=torch.float32, device="cuda")
+    sn = torch.empty_like(cs)
+    ctx.rope_tables(pos, sh.S, cs, sn)
+    txt = torch.empty((sh.L, sh.hidden), dtype=torch.float32, device="cuda")
+    if sh.L > 0:
+        ctx.prologue(mw, L.dev_f32(m["ctx"]), sh.L, txt)
+    return ctx, mw, cs, sn, txt
+
+
+def _run_steps(ctx, mw, m, cs, sn, txt, sig, steps):
+    sh = m["shape"]
+    x = L.dev_f32(m["x_lat"])
+    vels = []
+    for i in steps:
+        v = torch.empty((sh.N, sh.latent), dtype=torch.float32, device="cuda")
+        ctx.denoise_step(mw, x, txt, cs, sn, sh.L, sh.N, float(sig[i]), float(sig[i + 1]), v)
+        vels.append(v)
+    torch.cuda.synchronize()
+    return x, vels
+
+
+@pytest.mark.parametrize("name,kw", [("twin", dict(blocks=3, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8,
+                                                   text_dim=256)),
+                                     ("twin_w8a8", dict(blocks=2, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8,
+                                                        text_dim=256, w8a8=True)),
+                                     ("full", dict(blocks=2))])
+def test_planned_schedule_is_the_loop_bit_exact(name, kw):
+    """Steps whose modulation rows come from dit_plan_schedule (each
+    modulation weight read once for all four steps) equal the unplanned
+    steps bit for bit: the whole 4-step loop on a small model, and at the
+    1024-px DiT's sizes (two blocks); a plan of the first two sigmas only
+    (the other steps compute their own); a plan made for another model's
+    weights is not used."""
+    m = synth.model_case("dit32", **kw)
+    sh = m["shape"]
+    ctx, mw, cs, sn, txt = _twin_setup(m)
+    say("planned schedule", name, "S =", sh.S)
+    sig = O.sigma_grid(4)
+    steps = range(4) if name != "full" else range(2)
+    x0, v0 = _run_steps(ctx, mw, m, cs, sn, txt, sig, steps)
+    ctx.plan_schedule(mw, sig[:4])
+    x1, v1 = _run_steps(ctx, mw, m, cs, sn, txt, sig, steps)
+    for a, b in zip(v0, v1):
+        assert torch.equal(a, b)
+    assert torch.equal(x0, x1)
+    ctx.plan_schedule(mw, sig[:2])
+    x2, v2 = _run_steps(ctx, mw, m, cs, sn, txt, sig, steps)
+    for a, b in zip(v0, v2):
+        assert torch.equal(a, b)
+    assert torch.equal(x0, x2)
+    if name == "twin":
+        # another model's weights: its steps ignore this plan
+        m2 = synth.model_case("dit32", seed=77, **kw)
+        mw2 = L.ModelWeights.from_host(m2["top"], m2["blocks"])
+        txt2 = torch.empty_like(txt)
+        ctx.prologue(mw2, L.dev_f32(m2["ctx"]), sh.L, txt2)
+        ctx.plan_schedule(mw2, [])
+        xa, va = _run_steps(ctx, mw2, m2, cs, sn, txt2, sig, steps)
+        ctx.plan_schedule(mw, sig[:4])
+        xb, vb = _run_steps(ctx, mw2, m2, cs, sn, txt2, sig, steps)
+        for a, b in zip(va, vb):
+            assert torch.equal(a, b)
+        assert torch.equal(xa, xb)
+        assert not torch.equal(xa, x0)
+    ctx.close()
+
+
+def test_planned_schedule_rejects_bad_arguments(ctx_tiny):
+    m = synth.model_case("dit32", blocks=1, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8, text_dim=256)
+    mw = L.ModelWeights.from_host(m["top"], m["blocks"])
+    with pytest.raises(L.DitError) as e:
+        ctx_tiny.plan_schedule(mw, np.linspace(1, 0, 65))
+    assert e.value.status == L.ERANGE
+    with pytest.raises(L.DitError) as e:
+        ctx_tiny.plan_schedule(mw, [1.0, float("nan")])
+    assert e.value.status == L.ERANGE
+    assert L.raw().dit_plan_schedule(ctx_tiny.handle, C.byref(mw.struct), None, 2) == L.EINVAL
+    assert L.raw().dit_plan_schedule(None, C.byref(mw.struct), None, 0) == L.EINVAL
+    ctx_tiny.plan_schedule(mw, [])
+
 
 @pytest.mark.parametrize("w8a8,Lh", [(False, (8, 8, 8)), (True, (8, 8, 8)), (False, (0, 4, 4))])
 def test_denoise_twin(ctx_tiny, w8a8, Lh):
