@@ -8,6 +8,7 @@
 #include <type_traits>
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "kernels.h"
@@ -252,17 +253,21 @@ k_gemv(const uint16_t *__restrict__ W, const float *__restrict__ x, int64_t ldx,
 template <int NV, int JM>
 hipError_t launch_gemv_nv(const uint16_t *W, const float *x, int64_t ldx, int O, int I, int si, float *y,
                           int64_t ldy, hipStream_t st) {
-    static int resident[64] = {};   // blocks the device holds at once, per device id
+    // blocks the device holds at once, per device id (computed once; calls
+    // from several threads may both compute it, with the same result)
+    static std::atomic<int> resident[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (resident[dev] == 0) {
+    int res = resident[dev].load(std::memory_order_relaxed);
+    if (res == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<NV, JM>, kGemvThreads, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipErrorInvalidValue;
-        resident[dev] = std::max(1, per_cu) * std::max(1, cus);
+        res = std::max(1, per_cu) * std::max(1, cus);
+        resident[dev].store(res, std::memory_order_relaxed);
     }
-    const int blocks = std::min((O + 3) / 4, resident[dev]);
+    const int blocks = std::min((O + 3) / 4, res);
     k_gemv<NV, JM><<<blocks, kGemvThreads, 0, st>>>(W, x, ldx, O, I, si, y, ldy);
     return hipGetLastError();
 }
