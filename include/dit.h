@@ -156,7 +156,10 @@ dit_status dit_ctx_create(dit_ctx **out, int device, void *stream, const dit_arc
  * synchronise the stream first if calls are still in flight. */
 void dit_ctx_destroy(dit_ctx *ctx);
 
-/* Change the stream later calls enqueue on. */
+/* Change the stream later calls enqueue on.  Work already enqueued on the
+ * previous stream (which uses the context's workspace, and a planned
+ * schedule's rows) is not waited for: the caller orders the two streams,
+ * e.g. by synchronising the old one, before calls on the new one. */
 dit_status dit_ctx_set_stream(dit_ctx *ctx, void *stream);
 
 /* Text of the last non-OK status on this context (or of the last failed
