@@ -89,6 +89,8 @@ SHAPES = {
     "t_one": Shape("t_one", 256, 2, 128, 1024, 0, 1, 1, seed=22),
     "t_few": Shape("t_few", 256, 2, 128, 1024, 3, 1, 2, seed=23),
     "s1088": Shape("s1088", 3072, 24, 128, 12288, 64, 32, 32, seed=2),
+    # another width: 12 heads, ffn 6144, 40 text + 20x30 image rows
+    "m640": Shape("m640", 1536, 12, 128, 6144, 40, 20, 30, seed=24),
     "r1077": Shape("r1077", 3072, 24, 128, 12288, 77, 25, 40, seed=11),
     "s4608": Shape("s4608", 3072, 24, 128, 12288, 512, 64, 64, seed=3),
     "s4608_int8": Shape("s4608_int8", 3072, 24, 128, 12288, 512, 64, 64, seed=4, int8=True),
