@@ -42,6 +42,8 @@ def test_version_and_null_context():
     assert lib.dit_block_forward(None, None, None, None, None, None, 0, 1) == L.EINVAL
     assert lib.dit_set_qk_prep(None, 1) == L.EINVAL
     assert lib.dit_set_int8_products(None, 0) == L.EINVAL
+    assert lib.dit_plan_schedule(None, None, None, 0) == L.EINVAL
+    assert lib.dit_ctx_set_stream(None, None) == L.EINVAL
     lib.dit_ctx_destroy(None)      # no-op
 
 
