@@ -91,6 +91,8 @@ SHAPES = {
     "s1088": Shape("s1088", 3072, 24, 128, 12288, 64, 32, 32, seed=2),
     # another width: 12 heads, ffn 6144, 40 text + 20x30 image rows
     "m640": Shape("m640", 1536, 12, 128, 6144, 40, 20, 30, seed=24),
+    # wider than 3072: 32 heads, ffn 16384, tiny's rows
+    "w4096": Shape("w4096", 4096, 32, 128, 16384, 8, 8, 8, seed=25),
     "r1077": Shape("r1077", 3072, 24, 128, 12288, 77, 25, 40, seed=11),
     "s4608": Shape("s4608", 3072, 24, 128, 12288, 512, 64, 64, seed=3),
     "s4608_int8": Shape("s4608_int8", 3072, 24, 128, 12288, 512, 64, 64, seed=4, int8=True),

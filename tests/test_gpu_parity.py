@@ -77,11 +77,12 @@ def test_positions_and_rope_tables_bit_exact(ctx_big, Lh):
 
 # --------------------------------------------------------------- small steps
 
-@pytest.mark.parametrize("name", ["tiny", "s4608"])
+@pytest.mark.parametrize("name", ["tiny", "w4096", "s4608"])
 def test_time_vector_and_modulation(ctx_tiny, ctx_big, name):
+    # w4096: inputs wider than 3072 (the GEMV's other register layout)
     case = synth.block_case(name)
     sh = case["shape"]
-    ctx = ctx_tiny if name == "tiny" else ctx_big
+    ctx = {"tiny": ctx_tiny, "s4608": ctx_big}.get(name) or L.Context(arch_pair(sh)[0], max_rows=sh.S)
     say("time_vector/modulation", name)
     seq = GpuSeq(ctx, sh, case["t"], case["w_t1"], case["w_t2"])
     vref = O.time_vector(float(case["t"]), case["w_t1"], case["w_t2"], sh.time_dim)
@@ -96,7 +97,7 @@ def test_time_vector_and_modulation(ctx_tiny, ctx_big, name):
 
 
 @pytest.mark.parametrize("norm", ["layer", "rms"])
-@pytest.mark.parametrize("rows,D", [(72, 256), (4608, 3072), (5, 3072)])
+@pytest.mark.parametrize("rows,D", [(72, 256), (4608, 3072), (5, 3072), (72, 4096)])
 def test_modulated_norm(norm, rows, D):
     sh = synth.Shape("n", D, D // 128, 128, 1024, 0, 1, rows, seed=0)
     la, oa = arch_pair(sh, norm)
@@ -304,6 +305,7 @@ def _intermediates(ctx, sh, S):
 @pytest.mark.parametrize("name,norm,norm_std", [("tiny", "layer", 0.0), ("tiny", "rms", 0.1),
                                                  ("t_img", "layer", 0.0), ("t_one", "rms", 0.1),
                                                  ("t_few", "layer", 0.0), ("m640", "rms", 0.1),
+                                                 ("w4096", "layer", 0.0),
                                                  ("s1088", "layer", 0.0), ("r1077", "rms", 0.1)])
 def test_block_full_parity(name, norm, norm_std):
     # r1077: 77 text + 25 x 40 image rows, ragged against the 64-key
@@ -1461,6 +1463,8 @@ def _run_steps(ctx, mw, m, cs, sn, txt, sig, steps):
                                                    text_dim=256)),
                                      ("twin_w8a8", dict(blocks=2, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8,
                                                         text_dim=256, w8a8=True)),
+                                     ("wide", dict(blocks=2, hidden=4096, heads=32, ffn=16384, L=8, h=8, w=8,
+                                                   text_dim=256)),
                                      ("full", dict(blocks=2))])
 def test_planned_schedule_is_the_loop_bit_exact(name, kw):
     """Steps whose modulation rows come from dit_plan_schedule (each
