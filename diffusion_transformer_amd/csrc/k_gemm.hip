@@ -22,7 +22,7 @@
 // 2p and 2p+1 in two accumulators: the rotary pairs and the SwiGLU
 // (gate, up) pairs meet in one lane without shuffles.  Blocks are remapped
 // so that each XCD works on a compact group of tiles (its own L2), in groups
-// of 4 row-tiles.  Two kernels:
+// of 6 row-tiles.  Two kernels:
 //  - k_gemm_p3, 256x256 tiles: a two-group ping-pong schedule with direct
 //    global -> LDS loads (below), for bf16 weights (int8 block-32 weights
 //    arrive here dequantised by a pass of their own by default), with forms
@@ -255,7 +255,7 @@ k_gemm(const uint16_t *__restrict__ A, const void *__restrict__ Wv,
         const int per = total / 8, rem = total % 8, xcd = bid % 8, loc = bid / 8;
         bid = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
     }
-    constexpr int GM = 4;
+    constexpr int GM = 6;
     const int group = bid / (GM * ntn), first = group * GM;
     const int gsz = min(ntm - first, GM);
     const int tile_m = first + (bid % (GM * ntn)) % gsz;
@@ -691,7 +691,7 @@ k_gemm_p3(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int M,
         ep = ep2;
     }
     const int ntm = (M + BM - 1) / BM;
-    constexpr int GM = 4;
+    constexpr int GM = 6;
     const int group = bid / (GM * ntn), first = group * GM;
     const int gsz = min(ntm - first, GM);
     const int tile_m = first + (bid % (GM * ntn)) % gsz;
