@@ -473,20 +473,21 @@ def test_block_forward_repeats_bit_identical(ctx_big, name):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-@pytest.mark.parametrize("int8", [False, True])
-def test_block_independent_of_earlier_calls(ctx_big, int8):
+@pytest.mark.parametrize("kind", ["bf16", "int8", "w8a8"])
+def test_block_independent_of_earlier_calls(ctx_big, kind):
     """One context runs blocks of different lengths in turn (the full
     1024-px sequence, ragged ones, a single row); every result equals the
     same call on a fresh context bit for bit, so nothing a call leaves in
     the workspace (padding of the transposed values, rows past S, the
-    dequantised weights) reaches a later one."""
-    case = synth.block_case("s4608_int8" if int8 else "s1088")
+    dequantised weights, the INT8 rows of W8A8 products) reaches a later
+    one."""
+    case = synth.block_case({"bf16": "s1088", "int8": "s4608_int8", "w8a8": "s4608_w8a8"}[kind])
     base = case["shape"]
     bw = L.BlockWeights.from_host(case["block"])
     shapes = [(512, 64, 64), (77, 25, 40), (0, 1, 1), (3, 1, 2), (64, 32, 32), (5, 9, 13)]
     for k, (Ln, h, w) in enumerate(shapes):
         sh = synth.Shape("seq", base.hidden, base.heads, 128, base.ffn, Ln, h, w, seed=100 + k)
-        say("independent of earlier calls", int8, sh.L, sh.N)
+        say("independent of earlier calls", kind, sh.L, sh.N)
         x0 = synth.normal((sh.S, sh.hidden), seed=100 + k)
         outs = []
         for fresh in (False, True):
