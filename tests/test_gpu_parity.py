@@ -336,7 +336,7 @@ def test_arm_switches_reject_other_values(ctx_tiny):
     assert L.raw().dit_set_int8_products(ctx_tiny.handle, 0) == L.OK
 
 
-@pytest.mark.parametrize("name", ["tiny", "t_one", "t_few", "m640", "s1088", "r1077"])
+@pytest.mark.parametrize("name", ["tiny", "t_one", "t_few", "m640", "w4096", "s1088", "r1077"])
 @pytest.mark.parametrize("in_product", [False, True])
 def test_block_int8_full_parity(name, in_product):
     """int8 block-32 weights in the sequential block, every row and
@@ -675,7 +675,7 @@ def _parallel_gpu(ctx, case):
 
 @pytest.mark.parametrize("name,norm,norm_std", [("tiny", "layer", 0.0), ("tiny", "rms", 0.1),
                                                  ("t_one", "layer", 0.0), ("t_few", "rms", 0.1),
-                                                 ("m640", "layer", 0.0),
+                                                 ("m640", "layer", 0.0), ("w4096", "rms", 0.1),
                                                  ("s1088", "layer", 0.0), ("r1077", "layer", 0.0)])
 def test_parallel_block_full_parity(name, norm, norm_std):
     # below the ping-pong sizes: the four-product form
@@ -758,6 +758,7 @@ def _double_gpu(ctx, case):
 
 
 @pytest.mark.parametrize("name,in_product", [("tiny", False), ("t_img", False), ("t_few", False), ("m640", False),
+                                             ("w4096", False),
                                              ("s1088", False),
                                              ("r1077", False), ("s4608", False),
                                              ("s4608_int8", False), ("s4608_int8", True)])
@@ -1126,6 +1127,7 @@ def _w8a8_gpu(ctx, case, runs=None, rotated=False):
                                                               ("t_one", "layer", 0.0, False, False),
                                                               ("t_few", "rms", 0.1, True, True),
                                                               ("m640", "layer", 0.0, False, True),
+                                                              ("w4096", "rms", 0.1, True, True),
                                                               ("s1088", "layer", 0.0, False, True),
                                                               ("r1077", "rms", 0.1, False, True)])
 def test_w8a8_block_full_parity(name, norm, norm_std, sandwich, rot):
