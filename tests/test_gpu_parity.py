@@ -1538,6 +1538,23 @@ def test_planned_schedule_is_the_loop_bit_exact(name, kw):
     ctx.close()
 
 
+@pytest.mark.parametrize("steps", [5, 8])
+def test_planned_schedule_longer_than_four_steps(steps):
+    """Plans of more than four steps (the four-vector GEMV in chunks: 4 + 1,
+    4 + 4) give every step the unplanned rows bit for bit."""
+    m = synth.model_case("dit32", blocks=2, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8, text_dim=256)
+    ctx, mw, cs, sn, txt = _twin_setup(m)
+    say("planned schedule of", steps, "steps")
+    sig = O.sigma_grid(steps)
+    x0, v0 = _run_steps(ctx, mw, m, cs, sn, txt, sig, range(steps))
+    ctx.plan_schedule(mw, sig[:steps])
+    x1, v1 = _run_steps(ctx, mw, m, cs, sn, txt, sig, range(steps))
+    for a, b in zip(v0, v1):
+        assert torch.equal(a, b)
+    assert torch.equal(x0, x1)
+    ctx.close()
+
+
 def test_planned_schedule_rejects_bad_arguments(ctx_tiny):
     m = synth.model_case("dit32", blocks=1, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8, text_dim=256)
     mw = L.ModelWeights.from_host(m["top"], m["blocks"])
