@@ -1538,10 +1538,11 @@ def test_planned_schedule_is_the_loop_bit_exact(name, kw):
     ctx.close()
 
 
-@pytest.mark.parametrize("steps", [5, 8])
+@pytest.mark.parametrize("steps", [3, 5, 8])
 def test_planned_schedule_longer_than_four_steps(steps):
-    """Plans of more than four steps (the four-vector GEMV in chunks: 4 + 1,
-    4 + 4) give every step the unplanned rows bit for bit."""
+    """Plans of three steps (the three-vector GEMV) and of more than four
+    (the four-vector GEMV in chunks: 4 + 1, 4 + 4) give every step the
+    unplanned rows bit for bit."""
     m = synth.model_case("dit32", blocks=2, hidden=256, heads=2, ffn=1024, L=8, h=8, w=8, text_dim=256)
     ctx, mw, cs, sn, txt = _twin_setup(m)
     say("planned schedule of", steps, "steps")
