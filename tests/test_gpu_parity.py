@@ -1539,7 +1539,7 @@ def test_planned_schedule_is_the_loop_bit_exact(name, kw):
 
 
 @pytest.mark.parametrize("steps", [3, 5, 8])
-def test_planned_schedule_longer_than_four_steps(steps):
+def test_planned_schedule_of_other_lengths(steps):
     """Plans of three steps (the three-vector GEMV) and of more than four
     (the four-vector GEMV in chunks: 4 + 1, 4 + 4) give every step the
     unplanned rows bit for bit."""
